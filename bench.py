@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of the Engram n-gram memory hot path on one MI355X.
+
+A step is one pass of the whole path over one batch with every input resident
+in HBM: engram_compress_hash -> engram_gather_dequant -> engram_project ->
+engram_gate_add (the two halves of engram_gated_residual, called separately so
+that each kernel is bracketed by its own HIP events on the launch stream).
+
+Default workload ("full"): 8 x 8,192 Zipf(1.1) tokens against three
+5,040,000-row e4m3fn tables (row dim 6,500 + an fp32 scale per row, 91.6 GiB),
+one hash head per order, projection 19,500 -> 4,096 into 4 residual streams.
+
+Prints one JSON line: tokens/s, the roofline of the gather kernel (HBM bytes
+the method must move / measured average launch time, against 8 TB/s), the
+per-kernel breakdown, and the oracle's single-core throughput on a bounded
+token sample.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+[--config full|full_bf16|long|prefill|decode|tiny] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Engram tokens/s at 1 GPU + achieved HBM GB/s as % of MI355X peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+WORKLOAD_TEXT = {
+    "full": "full scale: 8 x 8,192 Zipf(1.1) tokens; 3 tables x 5,040,000 rows (15.12M) of 6,500 "
+            "e4m3fn + fp32 row scale (91.6 GiB); 1 head per order; wkv 19,500->4,096 bf16; hc 4",
+    "full_bf16": "full scale, BF16 tables: 8 x 8,192 Zipf(1.1) tokens; 3 x 5,040,000 rows of 6,500 "
+                 "bf16 (183.1 GiB); 1 head per order; wkv 19,500->4,096; hc 4",
+    "long": "long prefill: 65,536 Zipf(1.1) tokens in Geometric(mean 2,048) documents; "
+            "3 x 4,194,304 rows of 1,024 e4m3fn; 1 head per order; wkv 3,072->4,096; hc 4",
+    "prefill": "prefill: 4 x 4,096 Zipf(1.1) tokens; 3 x 1,048,576 rows of 512 e4m3fn; "
+               "2 heads per order; wkv 3,072->4,096; hc 4",
+    "decode": "decode step: 256 slots x 1 token, rolling store; prefill's tables and wkv",
+    "tiny": "tiny: 512 uniform tokens; 3 x 4,096 rows of 128 e4m3fn; 2 heads; wkv 768->256; hc 4",
+}
+
+
+def algorithmic_per_token(cfg):
+    """Bytes (or flops) each kernel must move per token, counting rows touched."""
+    H, D, hidden = cfg.heads, cfg.row_dim, cfg.hidden
+    K = 3 * H * D
+    scale = 4 if cfg.table_dtype == "fp8" else 0
+    return {
+        # token id, tid2eid entry, compressed id out, 3H row ids out
+        "hash_bytes": 4 + 4 + 4 + 4 * 3 * H,
+        # 3H rows of D elements + their scale in; K bf16 out
+        "gather_bytes": 3 * H * (D * cfg.elt_bytes + scale) + 2 * K,
+        "project_flops": 2 * K * hidden,
+        # 4 bf16 streams read and written, v (fp32) read
+        "gate_bytes": cfg.hc_mult * hidden * 2 * 2 + 4 * hidden,
+    }
+
+
+def cpu_baseline(cfg, batch, tables, weight, streams_host_bits, budget_s: float):
+    """The oracle as it stands, single-threaded on a host core, on a bounded token
+    sample of the same workload (rows read from the device tables by torch)."""
+    import numpy as np
+    import torch
+
+    import engram_inputs as ei
+    import oracle
+
+    tid2eid = ei.make_tid2eid(cfg.vocab, cfg.vc)
+    L = oracle.fit_layout([cfg.rows] * 3, cfg.heads)
+    store = ei.make_store_init(cfg) if batch.slots is not None else None
+    t0 = time.perf_counter()
+    _, rows = oracle.compress_hash(L, vocab=cfg.vocab, vc=cfg.vc, pad_token_id=cfg.pad_token_id,
+                                   tid2eid=tid2eid, tokens=batch.tokens, cu_seqlens=batch.cu_seqlens,
+                                   seq_start=batch.seq_start, slots=batch.slots, store=store)
+    t_hash_all = time.perf_counter() - t0
+    W = weight.view(torch.int16).cpu().numpy().view(np.uint16)
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(batch.T)
+    H, D = cfg.heads, cfg.row_dim
+    done, t_rest = 0, 0.0
+    chunk = 4
+    while done < batch.T and t_rest + t_hash_all * done / batch.T < budget_s:
+        idx = np.sort(order[done:done + chunk])
+        raw = np.zeros((len(idx), 3 * H, D), np.uint16 if cfg.table_dtype == "bf16" else np.uint8)
+        sc = None if cfg.table_dtype == "bf16" else np.zeros((len(idx), 3 * H), np.float32)
+        for o in range(3):
+            view = tables.row_view(o)
+            for h in range(H):
+                ii = torch.from_numpy(rows[idx, o, h].astype(np.int64)).to(view.device)
+                r = view.index_select(0, ii)
+                raw[:, o * H + h] = (r.view(torch.int16).cpu().numpy().view(np.uint16)
+                                     if cfg.table_dtype == "bf16" else r.cpu().numpy())
+                if sc is not None:
+                    sc[:, o * H + h] = tables.scale[o].index_select(0, ii).cpu().numpy()
+        x = streams_host_bits[idx]
+        t1 = time.perf_counter()
+        _, e16 = oracle.dequant_rows(raw.reshape(-1, D), None if sc is None else sc.reshape(-1),
+                                     bf16_table=cfg.table_dtype == "bf16")
+        v = oracle.project(e16.reshape(len(idx), -1), W)
+        oracle.gate_add(x, v)
+        t_rest += time.perf_counter() - t1
+        done += len(idx)
+    total = t_rest + t_hash_all * done / batch.T
+    return {
+        "value": done / total,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} of {batch.T} tokens of the same batch (seeded), full path per token: "
+                   f"compress+hash (whole batch {t_hash_all:.3f}s, charged pro rata), dequant, "
+                   f"fp64 projection, gate; {total:.1f}s of single-thread C on "
+                   f"{platform.processor() or platform.machine()}, {os.cpu_count()} host threads visible"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="full", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import engram_inputs as ei
+    import hashed_gram_memory_tid2eid_amd as eng
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = ei.get_config(args.config)
+    t_setup = time.perf_counter()
+    tid2eid = torch.from_numpy(ei.make_tid2eid(cfg.vocab, cfg.vc)).to(dev)
+    if cfg.decode_steps:
+        batches = ei.make_decode_steps(cfg, 1)
+        batch = batches[0]
+    else:
+        batch = ei.make_batch(cfg)
+    T = batch.T
+    tables = ei.make_tables(cfg, dev)
+    weight = ei.make_weight(cfg, dev)
+    site = eng.Engram(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+                      heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+                      table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes,
+                      tid2eid=tid2eid, tables=tables.data, scales=tables.scale, weight=weight,
+                      hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=T)
+    streams = ei.make_streams(cfg, T, dev)
+    streams_host = None
+    if not args.no_cpu_baseline:
+        streams_host = streams.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+
+    def d(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    tok, cu, ss, sl = d(batch.tokens), d(batch.cu_seqlens), d(batch.seq_start), d(batch.slots)
+    store = d(ei.make_store_init(cfg)) if cfg.decode_steps else None
+    L = site.layout
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print(f"# setup {setup_s:.1f}s: {cfg.name}, T={T}, k_pad={site.info.k_pad}", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        eng.engram_compress_hash(L, tid2eid, tok, cu, site.eids, site.row_ids, seq_start=ss,
+                                 slots=sl, store=store)
+        if ev:
+            ev[1].record()
+        eng.engram_gather_dequant(L, site.tables, site.scales, site.row_ids, site.rows, T=T)
+        if ev:
+            ev[2].record()
+        eng.engram_project(L, site.rows, site.weight, site.v, T=T)
+        if ev:
+            ev[3].record()
+        eng.engram_gate_add(L, site.v, streams, T=T)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    eng.check_device_error("warmup")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    eng.check_device_error("timed steps")
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    names = ["compress_hash", "gather_dequant", "project", "gate_add"]
+    kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+
+    per = algorithmic_per_token(cfg)
+    def gbs(b, ms):
+        return b / (ms * 1e-3) / 1e9
+    gather_bytes = per["gather_bytes"] * T
+    gather_gbs = gbs(gather_bytes, kern_ms["gather_dequant"])
+    proj_tflops = per["project_flops"] * T / (kern_ms["project"] * 1e-3) / 1e12
+    gate_gbs = gbs(per["gate_bytes"] * T, kern_ms["gate_add"])
+    hash_gbs = gbs(per["hash_bytes"] * T, kern_ms["compress_hash"])
+
+    result = {
+        "metric": METRIC,
+        "value": T * args.steps / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; see engram_inputs)",
+        "config": {"workload": WORKLOAD_TEXT[cfg.name], "name": cfg.name, "tokens_per_step": T,
+                   "table_dtype": cfg.table_dtype, "rows_per_table": cfg.rows, "row_dim": cfg.row_dim,
+                   "heads_per_order": cfg.heads, "hidden": cfg.hidden, "hc_mult": cfg.hc_mult,
+                   "k_pad": site.info.k_pad},
+        "roofline": {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": gather_bytes,
+                     "avg_launch_ms": kern_ms["gather_dequant"]},
+        "kernels": {
+            "compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs},
+            "gather_dequant": {"ms": kern_ms["gather_dequant"], "bound": "hbm", "GB/s": gather_gbs,
+                               "frac": gather_gbs / HBM_PEAK_GBS},
+            "project": {"ms": kern_ms["project"], "bound": "mfma", "TFLOP/s": proj_tflops,
+                        "frac": proj_tflops / BF16_PEAK_TFLOPS},
+            "gate_add": {"ms": kern_ms["gate_add"], "bound": "hbm", "GB/s": gate_gbs,
+                         "frac": gate_gbs / HBM_PEAK_GBS},
+        },
+        "wall_s_timed": wall,
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, batch, tables, weight, streams_host, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,340 @@
+"""MI355X (gfx950) Engram n-gram memory hot path: Python binding of libengram.so.
+
+The functions below carry the names of the C ABI in ``include/engram.h`` and do
+argument marshalling only: torch tensors provide device memory and the HIP
+stream; every step of the path runs in the library's kernels.  Importing this
+package fails loudly if the library has not been built (there is no fallback).
+Build it with ``python -m hashed_gram_memory_tid2eid_amd._build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "engram.h")
+
+ENGRAM_DTYPE_FP8_E4M3FN = 1
+ENGRAM_DTYPE_BF16 = 2
+ENGRAM_DTYPE_F32 = 3
+ENGRAM_MAX_HEADS = 8
+
+
+def _status_codes():
+    codes = {}
+    with open(HEADER_PATH) as f:
+        for m in re.finditer(r"#define\s+(ENGRAM_(?:OK|E_\w+))\s+\(?(-?\d+)\)?", f.read()):
+            codes[m.group(1)] = int(m.group(2))
+    return codes
+
+
+STATUS = _status_codes()
+globals().update(STATUS)
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {engram_strerror(status)} (status {status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m hashed_gram_memory_tid2eid_amd._build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_i32, _i64 = ctypes.c_int32, ctypes.c_int64
+
+
+class engram_layout_desc(ctypes.Structure):
+    _fields_ = [
+        ("vocab_size", _i64), ("compressed_vocab", _i64), ("pad_token_id", _i64),
+        ("max_ngram", _i32), ("heads_per_order", _i32), ("rows", _i64 * 3), ("hash_floor", _i64),
+        ("row_dim", _i32), ("table_dtype", _i32), ("row_pitch_bytes", _i64),
+    ]
+
+
+class engram_layout_info(ctypes.Structure):
+    _fields_ = [
+        ("hash_floor", _i64), ("heads_per_order", _i32), ("row_dim", _i32), ("rows", _i64 * 3),
+        ("primes", _i64 * (3 * ENGRAM_MAX_HEADS)), ("offsets", _i64 * (3 * ENGRAM_MAX_HEADS)),
+        ("prime_sum", _i64 * 3), ("seg_pitch", _i64), ("k_pad", _i64),
+    ]
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_sig("engram_layout_create", [ctypes.POINTER(engram_layout_desc), ctypes.POINTER(_P)])
+_sig("engram_layout_destroy", [_P], None)
+_sig("engram_layout_query", [_P, ctypes.POINTER(engram_layout_info)])
+_sig("engram_tid2eid_check", [_P, _P, ctypes.POINTER(_i32), _P])
+_sig("engram_store_reset", [_P, _P, _i32, _P, _i32, _i32, _P])
+_sig("engram_store_write", [_P, _P, _i32, _P, _i32, _P, _P])
+_sig("engram_store_read", [_P, _P, _i32, _P, _i32, _P, _P])
+_sig("engram_compress_hash", [_P, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _P, _P, _P, _P])
+_sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _P])
+_sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
+_sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
+_sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
+_sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
+_sig("engram_get_error", [_P])
+
+
+def engram_strerror(status: int) -> str:
+    return _lib.engram_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise EngramError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _need(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def _dev(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous CUDA tensor (or None)."""
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# layout
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LayoutInfo:
+    hash_floor: int
+    heads: int
+    row_dim: int
+    rows: tuple
+    primes: list      # [3][H]
+    offsets: list     # [3][H]
+    prime_sum: tuple
+    seg_pitch: int
+    k_pad: int
+
+
+class Layout:
+    """Owner of an ``engram_layout*`` handle."""
+
+    def __init__(self, handle: int, desc: engram_layout_desc):
+        self.handle = handle
+        self.desc = desc
+        self.info = engram_layout_query(self)
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            _lib.engram_layout_destroy(h)
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+
+def engram_layout_create(*, vocab_size: int, compressed_vocab: int, pad_token_id: int,
+                         heads_per_order: int, rows: Sequence[int], row_dim: int,
+                         table_dtype: int, row_pitch_bytes: int, hash_floor: int = 0,
+                         max_ngram: int = 4) -> Layout:
+    d = engram_layout_desc()
+    d.vocab_size, d.compressed_vocab, d.pad_token_id = vocab_size, compressed_vocab, pad_token_id
+    d.max_ngram, d.heads_per_order = max_ngram, heads_per_order
+    for i in range(3):
+        d.rows[i] = int(rows[i])
+    d.hash_floor, d.row_dim, d.table_dtype, d.row_pitch_bytes = hash_floor, row_dim, table_dtype, row_pitch_bytes
+    h = _P()
+    _check(_lib.engram_layout_create(ctypes.byref(d), ctypes.byref(h)), "engram_layout_create")
+    return Layout(h.value, d)
+
+
+def engram_layout_query(layout: Layout) -> LayoutInfo:
+    info = engram_layout_info()
+    _check(_lib.engram_layout_query(layout.handle, ctypes.byref(info)), "engram_layout_query")
+    H = info.heads_per_order
+    return LayoutInfo(
+        hash_floor=info.hash_floor, heads=H, row_dim=info.row_dim, rows=tuple(info.rows),
+        primes=[[info.primes[n * H + h] for h in range(H)] for n in range(3)],
+        offsets=[[info.offsets[n * H + h] for h in range(H)] for n in range(3)],
+        prime_sum=tuple(info.prime_sum), seg_pitch=info.seg_pitch, k_pad=info.k_pad)
+
+
+def engram_tid2eid_check(layout: Layout, tid2eid, stream=None) -> int:
+    import torch
+    pad = _i32()
+    _need(tid2eid.numel() == layout.desc.vocab_size, "tid2eid must hold vocab_size entries")
+    _check(_lib.engram_tid2eid_check(layout.handle, _dev(tid2eid, torch.int32, "tid2eid"),
+                                     ctypes.byref(pad), _stream(stream)), "engram_tid2eid_check")
+    return pad.value
+
+
+# ---------------------------------------------------------------------------
+# store
+# ---------------------------------------------------------------------------
+
+def engram_store_reset(layout: Layout, store, pad_eid: int, slots=None, stream=None):
+    import torch
+    n = 0 if slots is None else slots.numel()
+    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
+    _check(_lib.engram_store_reset(layout.handle, _dev(store, torch.int32, "store"), store.shape[0],
+                                   _dev(slots, torch.int32, "slots"), n, pad_eid, _stream(stream)),
+           "engram_store_reset")
+
+
+def engram_store_write(layout: Layout, store, slots, ids, stream=None):
+    import torch
+    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
+    _need(ids.numel() >= 3 * slots.numel(), "ids must be [n][3]")
+    _check(_lib.engram_store_write(layout.handle, _dev(store, torch.int32, "store"), store.shape[0],
+                                   _dev(slots, torch.int32, "slots"), slots.numel(),
+                                   _dev(ids, torch.int32, "ids"), _stream(stream)),
+           "engram_store_write")
+
+
+def engram_store_read(layout: Layout, store, slots, ids, stream=None):
+    import torch
+    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
+    _need(ids.numel() >= 3 * slots.numel(), "ids must be [n][3]")
+    _check(_lib.engram_store_read(layout.handle, _dev(store, torch.int32, "store"), store.shape[0],
+                                  _dev(slots, torch.int32, "slots"), slots.numel(),
+                                  _dev(ids, torch.int32, "ids"), _stream(stream)),
+           "engram_store_read")
+
+
+# ---------------------------------------------------------------------------
+# the three hot calls
+# ---------------------------------------------------------------------------
+
+def engram_compress_hash(layout: Layout, tid2eid, tokens, cu_seqlens, eids, row_ids, *,
+                         seq_start=None, slots=None, store=None, dead=None, stream=None):
+    import torch
+    T = tokens.numel()
+    S = cu_seqlens.numel() - 1
+    H = layout.info.heads
+    _need(eids.numel() >= T and row_ids.numel() >= T * 3 * H, "eids / row_ids too small")
+    _need(tid2eid.numel() == layout.desc.vocab_size, "tid2eid must hold vocab_size entries")
+    _need(seq_start is None or seq_start.numel() >= S, "seq_start too small")
+    _need(slots is None or slots.numel() >= S, "slots too small")
+    _need(dead is None or dead.numel() >= T, "dead too small")
+    _need(store is None or (store.dim() == 2 and store.shape[1] == 3), "store must be [num_slots][3]")
+    _check(_lib.engram_compress_hash(
+        layout.handle, _dev(tid2eid, torch.int32, "tid2eid"), _dev(tokens, torch.int32, "tokens"), T,
+        _dev(cu_seqlens, torch.int32, "cu_seqlens"), S, _dev(seq_start, torch.uint8, "seq_start"),
+        _dev(slots, torch.int32, "slots"), _dev(store, torch.int32, "store"),
+        0 if store is None else store.shape[0], _dev(dead, torch.uint8, "dead"),
+        _dev(eids, torch.int32, "eids"), _dev(row_ids, torch.int32, "row_ids"), _stream(stream)),
+        "engram_compress_hash")
+
+
+def engram_gather_dequant(layout: Layout, tables: Sequence, scales: Optional[Sequence], row_ids,
+                          out, *, T: Optional[int] = None, stream=None):
+    import torch
+    if T is None:
+        T = row_ids.shape[0]
+    info = layout.info
+    _need(row_ids.numel() >= T * 3 * info.heads, "row_ids too small")
+    _need(out.dim() == 2 and out.shape[0] >= T and out.shape[1] >= info.k_pad, "out too small")
+    pitch = layout.desc.row_pitch_bytes
+    for n, t in enumerate(tables):
+        _need(t.numel() >= info.rows[n] * pitch, f"table {n} smaller than rows x pitch")
+    if scales is not None:
+        for n, sc in enumerate(scales):
+            _need(sc.numel() >= info.rows[n], f"scale {n} smaller than rows")
+    tp = (_P * 3)(*[_dev(t, torch.uint8, "table") for t in tables])
+    sp = None
+    if scales is not None:
+        sp = (_P * 3)(*[_dev(s, torch.float32, "scale") for s in scales])
+    if out.dtype == torch.bfloat16:
+        odt = ENGRAM_DTYPE_BF16
+    elif out.dtype == torch.float32:
+        odt = ENGRAM_DTYPE_F32
+    else:
+        raise TypeError("out must be bfloat16 or float32")
+    _check(_lib.engram_gather_dequant(layout.handle, tp, sp, _dev(row_ids, torch.int32, "row_ids"), T,
+                                      odt, _dev(out, None, "out"), out.shape[1], _stream(stream)),
+           "engram_gather_dequant")
+
+
+def engram_project(layout: Layout, rows, w, v, *, T: Optional[int] = None, stream=None):
+    import torch
+    if T is None:
+        T = rows.shape[0]
+    _need(rows.dim() == 2 and rows.shape[0] >= T, "rows too small")
+    _need(w.dim() == 2 and v.dim() == 2 and v.shape[0] >= T and v.shape[1] == w.shape[0],
+          "v must be [T][hidden]")
+    _check(_lib.engram_project(layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
+                               _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
+                               _dev(v, torch.float32, "v"), T, _stream(stream)), "engram_project")
+
+
+def engram_gate_add(layout: Layout, v, streams, *, keep=None, T: Optional[int] = None, stream=None):
+    import torch
+    if T is None:
+        T = streams.shape[0]
+    _need(streams.dim() == 3 and streams.shape[0] >= T, "streams must be [T][hc][hidden]")
+    _need(v.dim() == 2 and v.shape[0] >= T and v.shape[1] == streams.shape[2], "v must be [T][hidden]")
+    _need(keep is None or keep.numel() >= T, "keep too small")
+    _check(_lib.engram_gate_add(layout.handle, _dev(v, torch.float32, "v"), streams.shape[2],
+                                streams.shape[1], _dev(keep, torch.uint8, "keep"),
+                                _dev(streams, torch.bfloat16, "streams"), T, _stream(stream)),
+           "engram_gate_add")
+
+
+def engram_gated_residual(layout: Layout, rows, w, streams, v, *, keep=None,
+                          T: Optional[int] = None, stream=None):
+    import torch
+    if T is None:
+        T = streams.shape[0]
+    _need(streams.dim() == 3 and streams.shape[0] >= T, "streams must be [T][hc][hidden]")
+    _need(rows.dim() == 2 and rows.shape[0] >= T, "rows too small")
+    _need(v.dim() == 2 and v.shape[0] >= T and v.shape[1] == streams.shape[2] == w.shape[0],
+          "v must be [T][hidden]")
+    _need(keep is None or keep.numel() >= T, "keep too small")
+    _check(_lib.engram_gated_residual(
+        layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
+        _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0], streams.shape[1],
+        _dev(keep, torch.uint8, "keep"), _dev(streams, torch.bfloat16, "streams"),
+        _dev(v, torch.float32, "v"), T, _stream(stream)), "engram_gated_residual")
+
+
+def engram_get_error(stream=None) -> int:
+    return int(_lib.engram_get_error(_stream(stream)))
+
+
+def check_device_error(where: str = "device", stream=None):
+    _check(engram_get_error(stream), where)
+
+
+from .runtime import Engram, pad_weight  # noqa: E402  (needs the functions above)

@@ -1,0 +1,232 @@
+// abi.cpp -- the extern "C" entry points of include/engram.h: argument checks
+// that the host can make without touching device memory, then kernel launches
+// on the caller's stream.  Hot calls allocate nothing and never synchronise.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_E_HIP; }
+
+}  // namespace
+
+extern "C" int engram_tid2eid_check(const engram_layout* L, const int32_t* d_tid2eid,
+                                    int32_t* pad_eid, hipStream_t stream) {
+  if (!L || !d_tid2eid || !pad_eid) return ENGRAM_E_ARG;
+  int32_t* d_res = nullptr;
+  if (hipMalloc(&d_res, 3 * sizeof(int32_t)) != hipSuccess) return ENGRAM_E_HIP;
+  int32_t h_res[3] = {0, 0, 0};
+  hipError_t e = hipMemcpyAsync(d_res, h_res, sizeof h_res, hipMemcpyHostToDevice, stream);
+  engram::MapCheckArgs a;
+  a.tid2eid = d_tid2eid;
+  a.vocab = (int32_t)L->desc.vocab_size;
+  a.vc = (int32_t)L->desc.compressed_vocab;
+  a.pad_token_id = (int32_t)L->desc.pad_token_id;
+  a.result = d_res;
+  if (e == hipSuccess) e = engram::launch_map_check(a, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h_res, d_res, sizeof h_res, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  hipFree(d_res);
+  if (e != hipSuccess) return ENGRAM_E_HIP;
+  if (h_res[0] != 0 || h_res[1] != a.vc - 1) return ENGRAM_E_MAP_RANGE;
+  *pad_eid = h_res[2];
+  return ENGRAM_OK;
+}
+
+// ---- store ------------------------------------------------------------------
+
+static int store_op(const engram_layout* L, int32_t* d_store, int32_t num_slots,
+                    const int32_t* d_slots, int32_t n, int32_t* d_ids, int32_t pad, int op,
+                    hipStream_t stream) {
+  if (!L || !d_store || num_slots < 1) return ENGRAM_E_ARG;
+  if (op != engram::STORE_RESET && (!d_slots || (n > 0 && !d_ids))) return ENGRAM_E_ARG;
+  if (d_slots && n < 0) return ENGRAM_E_ARG;
+  engram::StoreArgs a;
+  a.store = d_store;
+  a.num_slots = num_slots;
+  a.slots = d_slots;
+  a.n = d_slots ? n : num_slots;
+  a.ids = d_ids;
+  a.pad_eid = pad;
+  a.op = op;
+  return hip_status(engram::launch_store_op(a, stream));
+}
+
+extern "C" int engram_store_reset(const engram_layout* L, int32_t* d_store, int32_t num_slots,
+                                  const int32_t* d_slots, int32_t n, int32_t pad_eid,
+                                  hipStream_t stream) {
+  if (L && (pad_eid < 0 || pad_eid >= L->desc.compressed_vocab)) return ENGRAM_E_ARG;
+  return store_op(L, d_store, num_slots, d_slots, n, nullptr, pad_eid, engram::STORE_RESET,
+                  stream);
+}
+
+extern "C" int engram_store_write(const engram_layout* L, int32_t* d_store, int32_t num_slots,
+                                  const int32_t* d_slots, int32_t n, const int32_t* d_ids,
+                                  hipStream_t stream) {
+  return store_op(L, d_store, num_slots, d_slots, n, const_cast<int32_t*>(d_ids), 0,
+                  engram::STORE_WRITE, stream);
+}
+
+extern "C" int engram_store_read(const engram_layout* L, const int32_t* d_store,
+                                 int32_t num_slots, const int32_t* d_slots, int32_t n,
+                                 int32_t* d_ids, hipStream_t stream) {
+  return store_op(L, const_cast<int32_t*>(d_store), num_slots, d_slots, n, d_ids, 0,
+                  engram::STORE_READ, stream);
+}
+
+// ---- 1. compress + hash -------------------------------------------------------
+
+extern "C" int engram_compress_hash(const engram_layout* L, const int32_t* d_tid2eid,
+                                    const int32_t* d_tokens, int32_t T,
+                                    const int32_t* d_cu_seqlens, int32_t S,
+                                    const uint8_t* d_seq_start, const int32_t* d_slots,
+                                    int32_t* d_store, int32_t num_slots, const uint8_t* d_dead,
+                                    int32_t* d_eids, int32_t* d_row_ids, hipStream_t stream) {
+  if (!L || T < 0 || S < 0 || !d_tid2eid) return ENGRAM_E_ARG;
+  if (T > 0 && (S < 1 || !d_tokens || !d_eids || !d_row_ids)) return ENGRAM_E_ARG;
+  if (S > 0 && !d_cu_seqlens) return ENGRAM_E_ARG;
+  if (d_store && num_slots < 1) return ENGRAM_E_ARG;
+  if (!d_store) num_slots = 0;
+  if (T == 0 && S == 0) return ENGRAM_OK;
+  engram::HashArgs a;
+  a.tid2eid = d_tid2eid;
+  a.tokens = d_tokens;
+  a.cu_seqlens = d_cu_seqlens;
+  a.seq_start = d_seq_start;
+  a.slots = d_slots;
+  a.store = d_store;
+  a.dead = d_dead;
+  a.eids = d_eids;
+  a.row_ids = d_row_ids;
+  a.T = T;
+  a.S = S;
+  a.num_slots = num_slots;
+  a.heads = L->heads;
+  a.vocab = (int32_t)L->desc.vocab_size;
+  a.pad_token_id = (int32_t)L->desc.pad_token_id;
+  a.vc1 = L->vc_pow[1];
+  a.vc2 = L->vc_pow[2];
+  a.vc3 = L->vc_pow[3];
+  memcpy(a.prime, L->prime, sizeof a.prime);
+  memcpy(a.offset, L->offset, sizeof a.offset);
+  memcpy(a.barrett, L->barrett, sizeof a.barrett);
+  return hip_status(engram::launch_compress_hash(a, stream));
+}
+
+// ---- 2. gather + dequant -------------------------------------------------------
+
+extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* d_tables,
+                                     const float* const* d_scales, const int32_t* d_row_ids,
+                                     int32_t T, int32_t out_dtype, void* d_out, int64_t out_ld,
+                                     hipStream_t stream) {
+  if (!L || T < 0 || !d_tables) return ENGRAM_E_ARG;
+  if (out_dtype != ENGRAM_DTYPE_BF16 && out_dtype != ENGRAM_DTYPE_F32) return ENGRAM_E_ARG;
+  const bool bf16_table = L->desc.table_dtype == ENGRAM_DTYPE_BF16;
+  if (!bf16_table && !d_scales) return ENGRAM_E_ARG;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_row_ids || !d_out) return ENGRAM_E_ARG;
+  if (out_ld < L->k_pad || out_ld % 8 != 0) return ENGRAM_E_ALIGN;
+  if (!aligned(d_out, 16)) return ENGRAM_E_ALIGN;
+  engram::GatherArgs g;
+  for (int n = 0; n < 3; ++n) {
+    if (!d_tables[n]) return ENGRAM_E_ARG;
+    if (!aligned(d_tables[n], 16)) return ENGRAM_E_ALIGN;
+    g.table[n] = static_cast<const uint8_t*>(d_tables[n]);
+    g.scale[n] = nullptr;
+    if (!bf16_table) {
+      if (!d_scales[n]) return ENGRAM_E_ARG;
+      if (!aligned(d_scales[n], 4)) return ENGRAM_E_ALIGN;
+      g.scale[n] = d_scales[n];
+    }
+    g.rows[n] = L->desc.rows[n];
+  }
+  g.pitch = L->desc.row_pitch_bytes;
+  g.heads = L->heads;
+  g.cols = L->cols;
+  g.row_dim = L->desc.row_dim;
+  g.seg_pitch = (int32_t)L->seg_pitch;
+  g.bf16_table = bf16_table ? 1 : 0;
+  g.f32_out = out_dtype == ENGRAM_DTYPE_F32 ? 1 : 0;
+  const size_t out_elt = out_dtype == ENGRAM_DTYPE_F32 ? 4 : 2;
+  g.out_ld = out_ld;
+  // one launch covers fewer than 2^31 output chunks; split bigger calls by tokens
+  const int64_t chunks_per_token = (int64_t)L->cols * (L->seg_pitch / 16);
+  const int64_t max_tokens = ((int64_t)1 << 31) / chunks_per_token - 1;
+  for (int64_t t0 = 0; t0 < T; t0 += max_tokens) {
+    const int64_t tn = (T - t0 < max_tokens) ? T - t0 : max_tokens;
+    g.row_ids = d_row_ids + t0 * L->cols;
+    g.out = static_cast<char*>(d_out) + (size_t)t0 * out_ld * out_elt;
+    g.T = (int32_t)tn;
+    hipError_t e = engram::launch_gather_dequant(g, stream);
+    if (e != hipSuccess) return ENGRAM_E_HIP;
+  }
+  return ENGRAM_OK;
+}
+
+// ---- 3. projection + gated residual ---------------------------------------------
+
+extern "C" int engram_project(const engram_layout* L, const void* d_rows, int64_t rows_ld,
+                              const void* d_w, int64_t w_ld, int32_t hidden, float* d_v,
+                              int32_t T, hipStream_t stream) {
+  if (!L || T < 0 || hidden < 1) return ENGRAM_E_ARG;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_rows || !d_w || !d_v) return ENGRAM_E_ARG;
+  if (rows_ld < L->k_pad || w_ld < L->k_pad || rows_ld % 8 || w_ld % 8) return ENGRAM_E_ALIGN;
+  if (!aligned(d_rows, 16) || !aligned(d_w, 16) || !aligned(d_v, 4)) return ENGRAM_E_ALIGN;
+  engram::GemmArgs g;
+  g.A = d_rows;
+  g.B = d_w;
+  g.C = d_v;
+  g.lda = rows_ld;
+  g.ldb = w_ld;
+  g.ldc = hidden;
+  g.M = T;
+  g.N = hidden;
+  g.K = (int32_t)L->k_pad;
+  return hip_status(engram::launch_gemm_bf16_nt(g, stream));
+}
+
+extern "C" int engram_gate_add(const engram_layout* L, const float* d_v, int32_t hidden,
+                               int32_t hc_mult, const uint8_t* d_keep, void* d_streams,
+                               int32_t T, hipStream_t stream) {
+  if (!L || T < 0) return ENGRAM_E_ARG;
+  if (hc_mult != 4) return ENGRAM_E_UNSUPPORTED;
+  if (hidden < 8 || hidden % 8 != 0) return ENGRAM_E_ALIGN;
+  if (hidden > 8192) return ENGRAM_E_UNSUPPORTED;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_v || !d_streams) return ENGRAM_E_ARG;
+  if (!aligned(d_v, 16) || !aligned(d_streams, 16)) return ENGRAM_E_ALIGN;
+  engram::GateArgs a;
+  a.v = d_v;
+  a.keep = d_keep;
+  a.streams = d_streams;
+  a.T = T;
+  a.hidden = hidden;
+  a.hc = hc_mult;
+  a.inv_sqrt_hidden = (float)(1.0 / sqrt((double)hidden));
+  return hip_status(engram::launch_gate_add(a, stream));
+}
+
+extern "C" int engram_gated_residual(const engram_layout* L, const void* d_rows,
+                                     int64_t rows_ld, const void* d_w, int64_t w_ld,
+                                     int32_t hidden, int32_t hc_mult, const uint8_t* d_keep,
+                                     void* d_streams, float* d_v, int32_t T, hipStream_t stream) {
+  if (hc_mult != 4) return ENGRAM_E_UNSUPPORTED;
+  if (hidden < 8 || hidden % 8 != 0) return ENGRAM_E_ALIGN;
+  if (hidden > 8192) return ENGRAM_E_UNSUPPORTED;
+  if (d_v && !aligned(d_v, 16)) return ENGRAM_E_ALIGN;
+  int rc = engram_project(L, d_rows, rows_ld, d_w, w_ld, hidden, d_v, T, stream);
+  if (rc != ENGRAM_OK) return rc;
+  return engram_gate_add(L, d_v, hidden, hc_mult, d_keep, d_streams, T, stream);
+}
+
+extern "C" int engram_get_error(hipStream_t stream) {
+  int status = 0;
+  if (engram::read_and_clear_device_error(stream, &status) != hipSuccess) return ENGRAM_E_HIP;
+  return status;
+}

@@ -1,0 +1,100 @@
+// internal.h -- declarations shared by the library's host and device translation
+// units (not part of the public ABI in include/engram.h).
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/engram.h"
+
+#define ENGRAM_MAX_COLS (3 * ENGRAM_MAX_HEADS)
+
+struct engram_layout {
+  engram_layout_desc desc;
+  int64_t floor;
+  int32_t heads;
+  int32_t cols;                          // 3 * heads
+  uint32_t prime[ENGRAM_MAX_COLS];       // [order][head]
+  uint32_t offset[ENGRAM_MAX_COLS];
+  uint64_t barrett[ENGRAM_MAX_COLS];     // floor((2^64 - 1) / prime)
+  int64_t prime_sum[3];
+  int64_t seg_pitch;                     // round_up(D, 64) elements
+  int64_t k_pad;                         // cols * seg_pitch
+  uint64_t vc_pow[4];                    // V_c^0 .. V_c^3
+};
+
+namespace engram {
+
+// Device-side status word (one per device, see engram_get_error).
+hipError_t read_and_clear_device_error(hipStream_t stream, int* status);
+
+struct HashArgs {
+  const int32_t* tid2eid;
+  const int32_t* tokens;
+  const int32_t* cu_seqlens;
+  const uint8_t* seq_start;
+  const int32_t* slots;
+  int32_t* store;
+  const uint8_t* dead;
+  int32_t* eids;
+  int32_t* row_ids;
+  int32_t T, S, num_slots, heads;
+  int32_t vocab, pad_token_id;
+  uint64_t vc1, vc2, vc3;
+  uint32_t prime[ENGRAM_MAX_COLS];
+  uint32_t offset[ENGRAM_MAX_COLS];
+  uint64_t barrett[ENGRAM_MAX_COLS];
+};
+hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream);
+
+struct MapCheckArgs {
+  const int32_t* tid2eid;
+  int32_t vocab, vc, pad_token_id;
+  int32_t* result;  // device int32[3]: {bad count, max id, pad id}
+};
+hipError_t launch_map_check(const MapCheckArgs& a, hipStream_t stream);
+
+enum StoreOp { STORE_RESET = 0, STORE_WRITE = 1, STORE_READ = 2 };
+struct StoreArgs {
+  int32_t* store;
+  int32_t num_slots;
+  const int32_t* slots;  // NULL = all slots (reset only)
+  int32_t n;
+  int32_t* ids;          // [n][3]
+  int32_t pad_eid;
+  int32_t op;
+};
+hipError_t launch_store_op(const StoreArgs& a, hipStream_t stream);
+
+struct GatherArgs {
+  const uint8_t* table[3];
+  const float* scale[3];
+  int64_t rows[3];
+  const int32_t* row_ids;
+  void* out;
+  int64_t out_ld;          // elements
+  int64_t pitch;           // bytes
+  int32_t T, heads, cols, row_dim, seg_pitch;
+  int32_t bf16_table;      // 0: e4m3fn + fp32 scale, 1: bf16
+  int32_t f32_out;         // 0: bf16 out, 1: fp32 out
+};
+hipError_t launch_gather_dequant(const GatherArgs& a, hipStream_t stream);
+
+struct GemmArgs {
+  const void* A;   // bf16 [M][lda]
+  const void* B;   // bf16 [N][ldb]
+  float* C;        // f32 [M][ldc]
+  int64_t lda, ldb, ldc;
+  int32_t M, N, K;
+};
+hipError_t launch_gemm_bf16_nt(const GemmArgs& a, hipStream_t stream);
+
+struct GateArgs {
+  const float* v;         // [T][hidden]
+  const uint8_t* keep;    // [T] or NULL
+  void* streams;          // bf16 [T][hc][hidden]
+  int32_t T, hidden, hc;
+  float inv_sqrt_hidden;
+};
+hipError_t launch_gate_add(const GateArgs& a, hipStream_t stream);
+
+}  // namespace engram

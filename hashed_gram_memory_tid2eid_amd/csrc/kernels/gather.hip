@@ -1,0 +1,220 @@
+// gather.hip -- row gather + row-wise dequant ([VeOmni#1370] "feat: support
+// DeepSeek-V4.1-Flash in SeedOmni", PR summary: native FP8 row-wise
+// dequantization on lookup).  Included into engram_device.hip.
+//
+// The output of one call is T token rows of k_pad elements, each the 3*H
+// segments (order-major, then head) of seg_pitch elements; a segment holds the
+// D dequantised elements of one looked-up table row followed by zeros.  The
+// work is a flat list of 16-element output chunks (T * 3H * seg_pitch/16 of
+// them).  Consecutive lanes take consecutive chunks, so a wave reads 1 KB of
+// consecutive table bytes (fp8) and writes 2 KB of consecutive output (bf16)
+// in 16-byte vector accesses; each lane keeps UNROLL chunks in flight.
+//
+// Dequant of a chunk: 16 e4m3fn bytes -> 16 fp32 (hardware conversion,
+// v_cvt_pk_f32_fp8), times the row's fp32 scale (one v_mul_f32 each: exactly
+// the IEEE product), then round-to-nearest-even to bf16 (v_cvt_pk_bf16_f32)
+// or kept as fp32.  BF16 tables are copied (or widened to fp32).
+
+namespace engram {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 4;
+
+// q = n / d for 0 <= n < 2^31 via a 64-bit multiply: m = ceil(2^s / d) with
+// s = 31 + ceil(log2 d) is exact on that range (round-up multiplier method).
+struct FastDiv {
+  uint64_t m;
+  uint32_t s;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.s);
+}
+
+struct GatherKArgs {
+  const uint8_t* t0;
+  const uint8_t* t1;
+  const uint8_t* t2;
+  const float* s0;
+  const float* s1;
+  const float* s2;
+  int32_t r0, r1, r2;  // rows per table
+  const int32_t* row_ids;
+  void* out;
+  int64_t out_ld;
+  int64_t pitch;
+  uint32_t total;      // chunks
+  uint32_t chunks;     // per segment = seg_pitch / 16
+  uint32_t cols;       // 3 * heads
+  uint32_t heads;
+  uint32_t row_dim;
+  uint32_t seg_pitch;
+  FastDiv div_chunks;
+  FastDiv div_cols;
+};
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  __bf16 b = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(unsigned short, b);
+}
+
+template <bool kBf16Table, bool kF32Out>
+__global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKArgs a) {
+  const uint32_t first = blockIdx.x * (kGatherThreads * kGatherUnroll) + threadIdx.x;
+
+  u32x4 raw[kGatherUnroll][kBf16Table ? 2 : 1];
+  float scale[kGatherUnroll];
+  uint32_t tok[kGatherUnroll], seg[kGatherUnroll], chunk[kGatherUnroll];
+  bool live[kGatherUnroll], any[kGatherUnroll];
+
+  // Issue every load first so that UNROLL row reads are in flight per lane.
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) {
+    const uint32_t g = first + (uint32_t)u * kGatherThreads;
+    live[u] = g < a.total;
+    any[u] = false;
+    scale[u] = 1.0f;
+    raw[u][0] = u32x4{0u, 0u, 0u, 0u};
+    if (kBf16Table) raw[u][kBf16Table ? 1 : 0] = u32x4{0u, 0u, 0u, 0u};
+    tok[u] = seg[u] = chunk[u] = 0;
+    if (!live[u]) continue;
+    const uint32_t rowidx = fdiv(g, a.div_chunks);  // token * cols + seg
+    chunk[u] = g - rowidx * a.chunks;
+    tok[u] = fdiv(rowidx, a.div_cols);
+    seg[u] = rowidx - tok[u] * a.cols;
+    const uint32_t n = (seg[u] >= a.heads) + (seg[u] >= 2 * a.heads);
+    if (chunk[u] * 16 >= a.row_dim) continue;  // pure padding: zeros
+    const int32_t row = a.row_ids[rowidx];
+    const int32_t rows = n == 0 ? a.r0 : (n == 1 ? a.r1 : a.r2);
+    if (row < 0 || row >= rows) {
+      latch_error(ENGRAM_E_ROW_RANGE);
+      continue;
+    }
+    const uint8_t* tb = n == 0 ? a.t0 : (n == 1 ? a.t1 : a.t2);
+    const uint8_t* src = tb + (int64_t)row * a.pitch + (int64_t)chunk[u] * 16 * (kBf16Table ? 2 : 1);
+    raw[u][0] = *reinterpret_cast<const u32x4*>(src);
+    if (kBf16Table) {
+      raw[u][kBf16Table ? 1 : 0] = *reinterpret_cast<const u32x4*>(src + 16);
+    } else {
+      const float* sc = n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2);
+      scale[u] = sc[row];
+    }
+    any[u] = true;
+  }
+
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) {
+    if (!live[u]) continue;
+    const uint32_t e0 = chunk[u] * 16;
+    const uint32_t valid = e0 >= a.row_dim ? 0u : (a.row_dim - e0 >= 16 ? 16u : a.row_dim - e0);
+    const int64_t obase = (int64_t)tok[u] * a.out_ld + (int64_t)seg[u] * a.seg_pitch + e0;
+
+    float f[16];
+    if (kBf16Table) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t word = raw[u][w >> 2][w & 3];
+        f[2 * w] = __uint_as_float(word << 16);
+        f[2 * w + 1] = __uint_as_float(word & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t word = raw[u][0][w];
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+        f[4 * w + 0] = lo[0] * scale[u];
+        f[4 * w + 1] = lo[1] * scale[u];
+        f[4 * w + 2] = hi[0] * scale[u];
+        f[4 * w + 3] = hi[1] * scale[u];
+      }
+    }
+    if (!any[u]) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) f[i] = 0.0f;
+    } else if (valid < 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((uint32_t)i >= valid) f[i] = 0.0f;
+    }
+
+    if (kF32Out) {
+      float* dst = reinterpret_cast<float*>(a.out) + obase;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst) + q);
+      }
+    } else {
+      u32x4 o[2];
+      if (kBf16Table && any[u] && valid == 16) {
+        o[0] = raw[u][0];
+        o[1] = raw[u][kBf16Table ? 1 : 0];
+      } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          o[w >> 2][w & 3] = bf16_bits_rne(f[2 * w]) | (bf16_bits_rne(f[2 * w + 1]) << 16);
+      }
+      unsigned short* dst = reinterpret_cast<unsigned short*>(a.out) + obase;
+      __builtin_nontemporal_store(o[0], reinterpret_cast<u32x4*>(dst));
+      __builtin_nontemporal_store(o[1], reinterpret_cast<u32x4*>(dst) + 1);
+    }
+  }
+}
+
+static FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;  // ceil(log2 d)
+  FastDiv f;
+  f.s = 31 + l;
+  f.m = (uint64_t)(((unsigned __int128)1 << f.s) + d - 1) / d;
+  return f;
+}
+
+hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
+  GatherKArgs a;
+  a.t0 = g.table[0];
+  a.t1 = g.table[1];
+  a.t2 = g.table[2];
+  a.s0 = g.scale[0];
+  a.s1 = g.scale[1];
+  a.s2 = g.scale[2];
+  a.r0 = (int32_t)g.rows[0];
+  a.r1 = (int32_t)g.rows[1];
+  a.r2 = (int32_t)g.rows[2];
+  a.row_ids = g.row_ids;
+  a.out = g.out;
+  a.out_ld = g.out_ld;
+  a.pitch = g.pitch;
+  a.chunks = (uint32_t)(g.seg_pitch / 16);
+  a.cols = (uint32_t)g.cols;
+  a.heads = (uint32_t)g.heads;
+  a.row_dim = (uint32_t)g.row_dim;
+  a.seg_pitch = (uint32_t)g.seg_pitch;
+  const uint64_t total = (uint64_t)g.T * a.cols * a.chunks;
+  if (total == 0) return hipSuccess;
+  if (total >= (1ull << 31)) return hipErrorInvalidValue;  // host splits larger calls
+  a.total = (uint32_t)total;
+  a.div_chunks = make_fastdiv(a.chunks);
+  a.div_cols = make_fastdiv(a.cols);
+  const uint32_t per_block = kGatherThreads * kGatherUnroll;
+  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+  if (g.bf16_table) {
+    if (g.f32_out)
+      hipLaunchKernelGGL((gather_dequant_kernel<true, true>), grid, dim3(kGatherThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gather_dequant_kernel<true, false>), grid, dim3(kGatherThreads), 0, stream, a);
+  } else {
+    if (g.f32_out)
+      hipLaunchKernelGGL((gather_dequant_kernel<false, true>), grid, dim3(kGatherThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gather_dequant_kernel<false, false>), grid, dim3(kGatherThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace engram

@@ -1,0 +1,240 @@
+// hash.hip -- compress + rolling n-gram hash, the slot store, and the tid2eid
+// set-up check.  Included into engram_device.hip (one device translation unit
+// so that every kernel can latch the device status word).
+//
+// One lane per token.  A wave covers 64 consecutive tokens of the flattened
+// batch; the three lookback ids of every lane come from its neighbours through
+// cross-lane shuffles, and lanes 0..2 additionally fetch the three tokens in
+// front of the wave (the halo).  Blocking (sequence starts, dead positions) is
+// decided per lane from the shuffled dead bits and the lane's sequence start,
+// found by a binary search over cu_seqlens.
+//
+// Hash ([VeOmni#1370] "feat: support DeepSeek-V4.1-Flash in SeedOmni", n-gram
+// memory lookup commit: hash multipliers derive from the compressed vocab
+// size): key_n = sum_{j<n} w_j V_c^j, exact in 64 bits since V_c <= 2^16, then
+// key mod p by Barrett reduction with the host-computed m = floor((2^64-1)/p):
+// q' = mulhi(key, m) is q or q-1, so one conditional subtraction finishes it.
+
+namespace engram {
+
+constexpr uint32_t kDeadBit = 1u << 30;
+constexpr uint32_t kIdMask = kDeadBit - 1;
+
+__device__ __forceinline__ uint32_t mod_barrett(uint64_t key, uint32_t p, uint64_t m) {
+  const uint64_t q = __umul64hi(key, m);
+  uint64_t r = key - q * (uint64_t)p;
+  if (r >= p) r -= p;
+  return (uint32_t)r;
+}
+
+// Compressed id of position q packed with its dead bit.  Only the owning lane
+// reports an out-of-range token (`report`), the halo copies stay silent.
+__device__ __forceinline__ uint32_t packed_eid(const HashArgs& a, int q, uint32_t pad,
+                                               bool report) {
+  const bool dead = a.dead != nullptr && a.dead[q] != 0;
+  if (dead) return pad | kDeadBit;
+  const int32_t tok = a.tokens[q];
+  if (tok < 0 || tok >= a.vocab) {
+    if (report) latch_error(ENGRAM_E_TOKEN_RANGE);
+    return pad;
+  }
+  return (uint32_t)a.tid2eid[tok] & kIdMask;
+}
+
+// Largest s in [0, S) with cu[s] <= t (cu[0] = 0 <= t).
+__device__ __forceinline__ int find_sequence(const int32_t* cu, int S, int t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void compress_hash_kernel(HashArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < a.T;
+  const uint32_t pad = (uint32_t)a.tid2eid[a.pad_token_id] & kIdMask;
+
+  // cu_seqlens must be 0 = c0 <= c1 <= ... <= cS = T.
+  if (t < a.S && a.cu_seqlens[t] > a.cu_seqlens[t + 1]) latch_error(ENGRAM_E_SEQLENS);
+  if (t == 0 && (a.cu_seqlens[0] != 0 || a.cu_seqlens[a.S] != a.T)) latch_error(ENGRAM_E_SEQLENS);
+
+  const uint32_t own = valid ? packed_eid(a, t, pad, true) : 0u;
+  uint32_t halo = 0u;
+  if (lane < 3) {
+    const int q = (t - lane) - 3 + lane;  // the three positions before the wave
+    if (q >= 0 && q < a.T) halo = packed_eid(a, q, pad, false);
+  }
+  // prev[j] = packed id of position t - j (all lanes take part in the shuffles)
+  uint32_t prev[4];
+#pragma unroll
+  for (int j = 1; j <= 3; ++j) {
+    const uint32_t from_wave = __shfl_up(own, (unsigned)j, 64);
+    const uint32_t from_halo = __shfl(halo, (lane - j + 3) & 63, 64);
+    prev[j] = lane >= j ? from_wave : from_halo;
+  }
+  if (!valid) return;
+
+  const int s = find_sequence(a.cu_seqlens, a.S, t);
+  int start = a.cu_seqlens[s];
+  if (start > t) {  // only when cu_seqlens[0] > 0, already latched above
+    start = t;
+  }
+  const bool starts = a.seq_start == nullptr || a.seq_start[s] != 0;
+  int slot = a.slots != nullptr ? a.slots[s] : -1;
+  if (slot < -1 || slot >= a.num_slots || (slot >= 0 && a.store == nullptr)) {
+    latch_error(ENGRAM_E_SLOT_RANGE);
+    slot = -1;
+  }
+
+  uint32_t w[4];
+  bool blocked = (own & kDeadBit) != 0;
+  w[0] = own & kIdMask;  // pad when dead
+#pragma unroll
+  for (int j = 1; j <= 3; ++j) {
+    const int q = t - j;
+    uint32_t val = pad;
+    if (!blocked) {
+      if (q >= start) {
+        if (prev[j] & kDeadBit)
+          blocked = true;
+        else
+          val = prev[j] & kIdMask;
+      } else if (starts) {
+        blocked = true;
+      } else if (slot < 0) {
+        latch_error(ENGRAM_E_NEED_STORE);
+        blocked = true;
+      } else {
+        val = (uint32_t)a.store[3 * slot + 3 - (start - q)];
+      }
+    }
+    w[j] = blocked ? pad : val;
+  }
+
+  const uint64_t k2 = (uint64_t)w[0] + (uint64_t)w[1] * a.vc1;
+  const uint64_t k3 = k2 + (uint64_t)w[2] * a.vc2;
+  const uint64_t k4 = k3 + (uint64_t)w[3] * a.vc3;
+  a.eids[t] = (int32_t)w[0];
+  int32_t* out = a.row_ids + (int64_t)t * (3 * a.heads);
+  for (int h = 0; h < a.heads; ++h) {
+    out[h] = (int32_t)(a.offset[h] + mod_barrett(k2, a.prime[h], a.barrett[h]));
+    const int c3 = a.heads + h;
+    out[c3] = (int32_t)(a.offset[c3] + mod_barrett(k3, a.prime[c3], a.barrett[c3]));
+    const int c4 = 2 * a.heads + h;
+    out[c4] = (int32_t)(a.offset[c4] + mod_barrett(k4, a.prime[c4], a.barrett[c4]));
+  }
+}
+
+// One thread per sequence: the slot keeps the last three window ids of its
+// sequence, oldest first.  Runs after compress_hash_kernel on the same stream,
+// so every read of the old slot content has happened.
+__global__ __launch_bounds__(256) void store_update_kernel(HashArgs a) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= a.S) return;
+  const int slot = a.slots[s];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    latch_error(ENGRAM_E_SLOT_RANGE);
+    return;
+  }
+  const int b0 = a.cu_seqlens[s], b1 = a.cu_seqlens[s + 1];
+  if (b0 < 0 || b1 > a.T || b1 < b0) return;  // malformed: latched by the hash kernel
+  const int32_t pad = a.tid2eid[a.pad_token_id];
+  const bool starts = a.seq_start == nullptr || a.seq_start[s] != 0;
+  int32_t* st = a.store + 3 * slot;
+  if (b1 == b0) {
+    if (starts) st[0] = st[1] = st[2] = pad;
+    return;
+  }
+  const int last = b1 - 1;
+  int32_t w[3];
+  bool blocked = a.dead != nullptr && a.dead[last] != 0;
+  w[0] = blocked ? pad : a.eids[last];
+  for (int j = 1; j <= 2; ++j) {
+    const int q = last - j;
+    int32_t val = pad;
+    if (!blocked) {
+      if (q >= b0) {
+        if (a.dead != nullptr && a.dead[q] != 0)
+          blocked = true;
+        else
+          val = a.eids[q];
+      } else if (starts) {
+        blocked = true;
+      } else {
+        val = st[3 - (b0 - q)];
+      }
+    }
+    w[j] = blocked ? pad : val;
+  }
+  st[0] = w[2];
+  st[1] = w[1];
+  st[2] = w[0];
+}
+
+hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream) {
+  const int work = a.T > a.S + 1 ? a.T : a.S + 1;
+  const int blocks = (work + 255) / 256;
+  hipLaunchKernelGGL(compress_hash_kernel, dim3(blocks), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.slots != nullptr && a.store != nullptr && a.S > 0) {
+    hipLaunchKernelGGL(store_update_kernel, dim3((a.S + 255) / 256), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// tid2eid set-up check: count ids outside [0, V_c), find the largest id, and
+// report the pad id.
+__global__ __launch_bounds__(256) void map_check_kernel(MapCheckArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) a.result[2] = a.tid2eid[a.pad_token_id];
+  if (i >= a.vocab) return;
+  const int32_t e = a.tid2eid[i];
+  if (e < 0 || e >= a.vc) atomicAdd(&a.result[0], 1);
+  atomicMax(&a.result[1], e);
+}
+
+hipError_t launch_map_check(const MapCheckArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(map_check_kernel, dim3((a.vocab + 255) / 256), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Store helpers (reset / write / read by slot), one thread per (slot, column).
+__global__ __launch_bounds__(256) void store_op_kernel(StoreArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t count = (a.slots == nullptr ? (int64_t)a.num_slots : (int64_t)a.n) * 3;
+  if (i >= count) return;
+  const int64_t r = i / 3, c = i - r * 3;
+  const int32_t slot = a.slots == nullptr ? (int32_t)r : a.slots[r];
+  if (slot < 0 || slot >= a.num_slots) {
+    latch_error(ENGRAM_E_SLOT_RANGE);
+    return;
+  }
+  int32_t* cell = a.store + 3 * (int64_t)slot + c;
+  if (a.op == STORE_RESET)
+    *cell = a.pad_eid;
+  else if (a.op == STORE_WRITE)
+    *cell = a.ids[i];
+  else
+    a.ids[i] = *cell;
+}
+
+hipError_t launch_store_op(const StoreArgs& a, hipStream_t stream) {
+  const int64_t count = (a.slots == nullptr ? (int64_t)a.num_slots : (int64_t)a.n) * 3;
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(store_op_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace engram

@@ -1,0 +1,207 @@
+// layout.cpp -- host-side bucket layout of one Engram site (no HIP calls).
+//
+// Bucket primes ([VeOmni#1370] "feat: support DeepSeek-V4.1-Flash in SeedOmni",
+// n-gram memory lookup commit and the validate_bucket_layout review thread):
+// for each order 2..4 and each head, the smallest prime at or above the floor
+// that no earlier (order, head) drew.  With one layer this is simply the first
+// 3*H primes at or above the floor, dealt out order-major; that is how it is
+// computed here (Miller-Rabin on a walk upward from the floor).
+//
+// Table split: one table per order (PR summary: 3-table lookup over 2-/3-/4-gram
+// tables), so each order's buckets start at offset 0 of its own table and the
+// row-count guard of the review thread (fewer rows than the prime sum is an
+// error, more is allowed) applies per table.  With no floor given, the floor
+// is the largest one whose primes fit every table; it is found by walking the
+// floor down from min(rows)/H while keeping the window of the first 3*H primes
+// at or above it.
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+uint64_t mulmod(uint64_t a, uint64_t b, uint64_t m) {
+  return (uint64_t)((unsigned __int128)a * b % m);
+}
+
+uint64_t powmod(uint64_t b, uint64_t e, uint64_t m) {
+  uint64_t r = 1 % m;
+  b %= m;
+  while (e) {
+    if (e & 1) r = mulmod(r, b, m);
+    b = mulmod(b, b, m);
+    e >>= 1;
+  }
+  return r;
+}
+
+// Deterministic Miller-Rabin for 64-bit n (the first twelve prime bases suffice).
+bool is_prime(uint64_t n) {
+  static const uint64_t bases[] = {2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37};
+  if (n < 2) return false;
+  for (uint64_t p : bases) {
+    if (n % p == 0) return n == p;
+  }
+  uint64_t d = n - 1;
+  int s = 0;
+  while ((d & 1) == 0) {
+    d >>= 1;
+    ++s;
+  }
+  for (uint64_t a : bases) {
+    uint64_t x = powmod(a, d, n);
+    if (x == 1 || x == n - 1) continue;
+    bool composite = true;
+    for (int r = 1; r < s; ++r) {
+      x = mulmod(x, x, n);
+      if (x == n - 1) {
+        composite = false;
+        break;
+      }
+    }
+    if (composite) return false;
+  }
+  return true;
+}
+
+// The first `count` primes >= floor, in increasing order.
+std::vector<uint64_t> primes_from(uint64_t floor_, int count) {
+  std::vector<uint64_t> out;
+  for (uint64_t x = floor_; (int)out.size() < count; ++x)
+    if (is_prime(x)) out.push_back(x);
+  return out;
+}
+
+bool window_fits(const std::vector<uint64_t>& p, int heads, const int64_t rows[3],
+                 int64_t sums[3]) {
+  bool ok = true;
+  for (int n = 0; n < 3; ++n) {
+    int64_t s = 0;
+    for (int h = 0; h < heads; ++h) s += (int64_t)p[n * heads + h];
+    sums[n] = s;
+    if (s > rows[n]) ok = false;
+  }
+  return ok;
+}
+
+}  // namespace
+
+extern "C" int engram_layout_create(const engram_layout_desc* d, engram_layout** out) {
+  if (!d || !out) return ENGRAM_E_ARG;
+  *out = nullptr;
+  const int H = d->heads_per_order;
+  if (d->max_ngram != 4 || H < 1 || H > ENGRAM_MAX_HEADS) return ENGRAM_E_ARG;
+  if (d->vocab_size < 1 || d->vocab_size > INT32_MAX) return ENGRAM_E_ARG;
+  if (d->compressed_vocab < 1) return ENGRAM_E_ARG;
+  if (d->compressed_vocab > 65536) return ENGRAM_E_VC_RANGE;  // V_c^4 <= 2^64
+  if (d->pad_token_id < 0 || d->pad_token_id >= d->vocab_size) return ENGRAM_E_ARG;
+  if (d->row_dim < 1) return ENGRAM_E_ARG;
+  if (d->hash_floor < 0) return ENGRAM_E_ARG;
+  for (int n = 0; n < 3; ++n)
+    if (d->rows[n] < 1 || d->rows[n] > INT32_MAX) return ENGRAM_E_ARG;
+  int elt;
+  if (d->table_dtype == ENGRAM_DTYPE_FP8_E4M3FN)
+    elt = 1;
+  else if (d->table_dtype == ENGRAM_DTYPE_BF16)
+    elt = 2;
+  else
+    return ENGRAM_E_ARG;
+  const int64_t min_pitch = ((int64_t)(d->row_dim + 15) / 16) * 16 * elt;
+  if (d->row_pitch_bytes % 16 != 0 || d->row_pitch_bytes < min_pitch) return ENGRAM_E_ALIGN;
+
+  const int cols = 3 * H;
+  std::vector<uint64_t> p;
+  int64_t sums[3];
+  uint64_t floor_;
+  if (d->hash_floor > 0) {
+    floor_ = (uint64_t)d->hash_floor;
+    p = primes_from(floor_, cols);
+    if (!window_fits(p, H, d->rows, sums)) return ENGRAM_E_LAYOUT_ROWS;
+  } else {
+    int64_t rmin = d->rows[0];
+    if (d->rows[1] < rmin) rmin = d->rows[1];
+    if (d->rows[2] < rmin) rmin = d->rows[2];
+    floor_ = (uint64_t)(rmin / H);
+    if (floor_ < 2) return ENGRAM_E_NOFIT;
+    p = primes_from(floor_, cols);
+    while (!window_fits(p, H, d->rows, sums)) {
+      if (floor_ <= 2) return ENGRAM_E_NOFIT;
+      --floor_;
+      if (is_prime(floor_)) {  // it joins the window at the front, the largest leaves
+        p.insert(p.begin(), floor_);
+        p.pop_back();
+      }
+    }
+  }
+
+  engram_layout* L = (engram_layout*)calloc(1, sizeof(engram_layout));
+  if (!L) return ENGRAM_E_ARG;
+  L->desc = *d;
+  L->floor = (int64_t)floor_;
+  L->heads = H;
+  L->cols = cols;
+  for (int n = 0; n < 3; ++n) {
+    uint64_t acc = 0;
+    for (int h = 0; h < H; ++h) {
+      const int c = n * H + h;
+      L->prime[c] = (uint32_t)p[c];
+      L->offset[c] = (uint32_t)acc;
+      L->barrett[c] = UINT64_MAX / p[c];
+      acc += p[c];
+    }
+    L->prime_sum[n] = sums[n];
+  }
+  L->seg_pitch = ((int64_t)d->row_dim + 63) / 64 * 64;
+  L->k_pad = (int64_t)cols * L->seg_pitch;
+  const uint64_t vc = (uint64_t)d->compressed_vocab;
+  L->vc_pow[0] = 1;
+  L->vc_pow[1] = vc;
+  L->vc_pow[2] = vc * vc;
+  L->vc_pow[3] = vc * vc * vc;
+  *out = L;
+  return ENGRAM_OK;
+}
+
+extern "C" void engram_layout_destroy(engram_layout* L) { free(L); }
+
+extern "C" int engram_layout_query(const engram_layout* L, engram_layout_info* info) {
+  if (!L || !info) return ENGRAM_E_ARG;
+  memset(info, 0, sizeof *info);
+  info->hash_floor = L->floor;
+  info->heads_per_order = L->heads;
+  info->row_dim = L->desc.row_dim;
+  for (int n = 0; n < 3; ++n) {
+    info->rows[n] = L->desc.rows[n];
+    info->prime_sum[n] = L->prime_sum[n];
+  }
+  for (int c = 0; c < L->cols; ++c) {
+    info->primes[c] = L->prime[c];
+    info->offsets[c] = L->offset[c];
+  }
+  info->seg_pitch = L->seg_pitch;
+  info->k_pad = L->k_pad;
+  return ENGRAM_OK;
+}
+
+extern "C" const char* engram_strerror(int s) {
+  switch (s) {
+    case ENGRAM_OK: return "ok";
+    case ENGRAM_E_ARG: return "malformed argument";
+    case ENGRAM_E_LAYOUT_ROWS: return "a table has fewer rows than its bucket prime sum";
+    case ENGRAM_E_VC_RANGE: return "compressed vocabulary too large for an exact 64-bit key";
+    case ENGRAM_E_NEED_STORE: return "a continuing sequence has no rolling-store slot";
+    case ENGRAM_E_TOKEN_RANGE: return "token id outside the vocabulary";
+    case ENGRAM_E_ROW_RANGE: return "row id outside its table";
+    case ENGRAM_E_SEQLENS: return "cu_seqlens is not a non-decreasing 0..T sequence";
+    case ENGRAM_E_SLOT_RANGE: return "store slot out of range";
+    case ENGRAM_E_MAP_RANGE: return "tid2eid does not map onto [0, compressed_vocab)";
+    case ENGRAM_E_ALIGN: return "misaligned pointer, pitch or leading dimension";
+    case ENGRAM_E_HIP: return "HIP runtime error";
+    case ENGRAM_E_NOFIT: return "no bucket floor fits the table rows";
+    case ENGRAM_E_UNSUPPORTED: return "unsupported shape";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,255 @@
+/*
+ * engram.h -- C ABI of the MI355X (gfx950) Engram n-gram memory hot path.
+ *
+ * The path, in the order the calls run:
+ *   1. engram_compress_hash   token ids -> compressed ids (tid2eid) -> rolling
+ *                             2/3/4-gram windows -> hashed row ids, with a
+ *                             slot-keyed store of the last three ids for decode;
+ *   2. engram_gather_dequant  row ids -> e4m3fn (or bf16) table rows from HBM ->
+ *                             row-wise dequantised bf16 (or fp32) rows;
+ *   3. engram_gated_residual  rows -> wkv down-projection (MFMA) -> per-stream
+ *                             sigmoid gate -> residual add into the hc streams.
+ *                             engram_project + engram_gate_add are its two halves.
+ *
+ * Pages defining the operations (titles; sections named):
+ *  [VeOmni#1370] GitHub PR "feat: support DeepSeek-V4.1-Flash in SeedOmni"
+ *                (ByteDance-Seed/VeOmni #1370).
+ *  [NeMo-V41]    NeMo AutoModel API page
+ *                "nemo_automodel.components.models.deepseek_v41.model".
+ *  [vLLM-V41]    vLLM docs page "vllm/models/deepseek_v41/nvidia/model".
+ *
+ * Conventions for every call:
+ *  - Return value: ENGRAM_OK (0) or a negative ENGRAM_E_* status.  Argument
+ *    errors that the host can see are returned at once and nothing is launched.
+ *  - Device pointers ("d_" prefix) are caller-owned device memory on the
+ *    current HIP device; the library never frees or keeps them.  Host pointers
+ *    have no prefix.  Sizes are element counts unless the name says bytes.
+ *  - Hot calls (compress_hash, gather_dequant, project, gate_add,
+ *    gated_residual, store_*) allocate nothing, never synchronise, and only
+ *    enqueue kernels on `stream`.
+ *  - Faults that only the device can see (a token id outside the vocabulary,
+ *    a row id outside its table, a bad slot, malformed cu_seqlens, a continuing
+ *    sequence without a store) latch the first such status in a per-device
+ *    error word; the affected outputs are unspecified.  engram_get_error()
+ *    synchronises, returns that status and clears it.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define ENGRAM_OK 0
+#define ENGRAM_E_ARG (-1)          /* malformed argument (null, negative size, bad enum)   */
+#define ENGRAM_E_LAYOUT_ROWS (-2)  /* a table has fewer rows than its bucket prime sum      */
+#define ENGRAM_E_VC_RANGE (-3)     /* compressed vocab^4 exceeds 2^64 (key not exact)      */
+#define ENGRAM_E_NEED_STORE (-4)   /* a continuing sequence (seq_start 0) has no store slot */
+#define ENGRAM_E_TOKEN_RANGE (-5)  /* device: a live token id outside [0, vocab_size)       */
+#define ENGRAM_E_ROW_RANGE (-6)    /* device: a row id outside [0, rows of its table)        */
+#define ENGRAM_E_SEQLENS (-7)      /* device: cu_seqlens not 0 = c0 <= c1 <= ... <= cS = T    */
+#define ENGRAM_E_SLOT_RANGE (-8)   /* device: a slot outside [-1, num_slots)                 */
+#define ENGRAM_E_MAP_RANGE (-9)    /* tid2eid has an id outside [0, V_c) or its size != V_c  */
+#define ENGRAM_E_ALIGN (-10)       /* pointer / leading dimension / pitch misaligned        */
+#define ENGRAM_E_HIP (-11)         /* a HIP runtime call failed                             */
+#define ENGRAM_E_NOFIT (-12)       /* no bucket floor fits the requested table rows         */
+#define ENGRAM_E_UNSUPPORTED (-13) /* a valid but unimplemented shape (e.g. hc_mult != 4)   */
+
+/* ---- element types ------------------------------------------------------ */
+typedef enum engram_dtype {
+  ENGRAM_DTYPE_FP8_E4M3FN = 1, /* OCP e4m3fn: bias 7, max 448, 0x7F/0xFF NaN, no inf */
+  ENGRAM_DTYPE_BF16 = 2,
+  ENGRAM_DTYPE_F32 = 3
+} engram_dtype;
+
+#define ENGRAM_MAX_HEADS 8 /* hash heads per n-gram order */
+
+/* ---- layout ------------------------------------------------------------- */
+/* Description of one Engram site: three hashed tables, one per n-gram order
+ * 2, 3, 4 ([VeOmni#1370] PR summary: 3-table hashed n-gram lookup over 2-/3-/
+ * 4-gram tables), each with `heads_per_order` prime-sized hash buckets. */
+typedef struct engram_layout_desc {
+  int64_t vocab_size;       /* tokenizer vocabulary = length of tid2eid ([VeOmni#1370]
+                               vocab_size / engram_vocab_size commit: 129,280)        */
+  int64_t compressed_vocab; /* V_c, size of the compressed id space (<= 65,536)       */
+  int64_t pad_token_id;     /* its compressed id is the pad id of blocked lookbacks    */
+  int32_t max_ngram;        /* must be 4 (orders 2, 3, 4)                              */
+  int32_t heads_per_order;  /* H, 1..ENGRAM_MAX_HEADS                                  */
+  int64_t rows[3];          /* rows of the 2-, 3-, 4-gram tables                        */
+  int64_t hash_floor;       /* primes are drawn at and above this floor (the pages'
+                               hash_vocab_size); 0 = fit the largest floor whose
+                               primes fit every table                                  */
+  int32_t row_dim;          /* D, elements per table row                                */
+  int32_t table_dtype;      /* ENGRAM_DTYPE_FP8_E4M3FN (+ fp32 scale per row) or BF16   */
+  int64_t row_pitch_bytes;  /* bytes between rows: multiple of 16 and at least
+                               round_up(D, 16) * element size                           */
+} engram_layout_desc;
+
+typedef struct engram_layout engram_layout; /* opaque, immutable after creation */
+
+/* Read-back of a created layout. */
+typedef struct engram_layout_info {
+  int64_t hash_floor;                       /* the floor used (given or fitted)          */
+  int32_t heads_per_order;
+  int32_t row_dim;
+  int64_t rows[3];
+  int64_t primes[3 * ENGRAM_MAX_HEADS];     /* [order][head]; first 3*H entries used    */
+  int64_t offsets[3 * ENGRAM_MAX_HEADS];    /* bucket start inside its order's table    */
+  int64_t prime_sum[3];                     /* addressable rows of each table           */
+  int64_t seg_pitch;                        /* elements between the (order, head)
+                                               segments of one gathered token row:
+                                               round_up(D, 64); the tail is zero        */
+  int64_t k_pad;                            /* 3 * H * seg_pitch: width of a gathered
+                                               token row and of the projection's K      */
+} engram_layout_info;
+
+/* Creates the layout: draws the bucket primes (for each order, for each head,
+ * the smallest prime at or above the floor not yet drawn, [VeOmni#1370]
+ * n-gram memory lookup commit and the validate_bucket_layout review thread),
+ * fixes offsets as prefix sums inside each order's table, and checks every
+ * table against its prime sum (fewer rows -> ENGRAM_E_LAYOUT_ROWS, more rows
+ * allowed, as that review thread proposes).  Host only: no HIP call.
+ * Errors: ENGRAM_E_ARG, ENGRAM_E_LAYOUT_ROWS, ENGRAM_E_VC_RANGE, ENGRAM_E_NOFIT,
+ * ENGRAM_E_ALIGN (pitch).  On success *out owns host memory freed by destroy. */
+int engram_layout_create(const engram_layout_desc* desc, engram_layout** out);
+void engram_layout_destroy(engram_layout* layout);
+int engram_layout_query(const engram_layout* layout, engram_layout_info* info);
+
+/* Set-up check of the compression map (not a hot call; synchronises `stream`):
+ * every entry of d_tid2eid[vocab_size] must lie in [0, V_c) and the largest
+ * must be V_c - 1 ([VeOmni#1370] checkpoint-splitter commit: the compressed
+ * vocabulary size the map produces is checked against the config, because a
+ * different map silently rehashes the tables).  Writes the pad id
+ * tid2eid[pad_token_id] to *pad_eid.  Errors: ENGRAM_E_MAP_RANGE, ENGRAM_E_HIP. */
+int engram_tid2eid_check(const engram_layout* layout, const int32_t* d_tid2eid,
+                         int32_t* pad_eid, hipStream_t stream);
+
+/* ---- rolling store ------------------------------------------------------ */
+/* The store is caller-owned device memory int32 [num_slots][3]: per slot the
+ * last three window ids of its sequence, oldest first ([VeOmni#1370] n-gram
+ * incremental decode cache commit: the whole cache is a fixed-width tail of
+ * max_ngram_size - 1 ids; [vLLM-V41] DeepseekV4Model.__init__: a slot-keyed
+ * rolling store of compressed ids for chunked prefill and decode).  A slot
+ * holding pad ids behaves exactly like a sequence start. */
+
+/* d_slots[n] (NULL = all slots, n ignored) <- (pad, pad, pad). */
+int engram_store_reset(const engram_layout* layout, int32_t* d_store, int32_t num_slots,
+                       const int32_t* d_slots, int32_t n, int32_t pad_eid, hipStream_t stream);
+/* store[d_slots[i]] <- d_ids[i][0..2] for i < n. */
+int engram_store_write(const engram_layout* layout, int32_t* d_store, int32_t num_slots,
+                       const int32_t* d_slots, int32_t n, const int32_t* d_ids,
+                       hipStream_t stream);
+/* d_ids[i][0..2] <- store[d_slots[i]] for i < n. */
+int engram_store_read(const engram_layout* layout, const int32_t* d_store, int32_t num_slots,
+                      const int32_t* d_slots, int32_t n, int32_t* d_ids, hipStream_t stream);
+
+/* ---- 1. compress + hash -------------------------------------------------- */
+/* For each token t of each sequence s (tokens cu_seqlens[s] .. cu_seqlens[s+1]-1):
+ *   e_t   = dead_t ? PAD : tid2eid[token_t],  PAD = tid2eid[pad_token_id]
+ *           ([VeOmni#1370] pack_ngram_inputs commit: dead image-span positions
+ *           compress to pad, the id a blocked lookback already reads);
+ *   window (w0..w3) = (e_t, e_{t-1}, e_{t-2}, e_{t-3}) where a lookback stops
+ *           (reads PAD from there on) at a dead position or before a sequence
+ *           that starts here ([VeOmni#1370] n-gram memory lookup commit: an
+ *           n-gram never spans an image span or reaches past position 0); a
+ *           dead token's own window is all PAD; positions before a continuing
+ *           sequence are read from its store slot;
+ *   key_n = sum_{j<n} w_j * V_c^j (exact in 64 bits), n = 2, 3, 4;
+ *   row_ids[t][n-2][h] = offsets[n][h] + key_n mod primes[n][h]
+ *           ([NeMo-V41] DeepseekV41Block.forward: logical memory rows
+ *           [batch, sequence, hash_heads]; [vLLM-V41] forward: one hash pass
+ *           over the flattened batch).
+ * After the call, each sequence with a slot leaves its last three window ids
+ * (oldest first) in the store; an empty sequence that starts here leaves PAD.
+ * Arguments:
+ *   d_tid2eid   int32 [vocab_size]
+ *   d_tokens    int32 [T], T >= 0
+ *   d_cu_seqlens int32 [S+1], S >= 1 if T > 0
+ *   d_seq_start uint8 [S] or NULL (= every sequence starts here)
+ *   d_slots     int32 [S] or NULL; -1 = no slot.  Slots of one call must be
+ *               distinct (two sequences updating one slot race).
+ *   d_store     int32 [num_slots][3] or NULL
+ *   d_dead      uint8 [T] or NULL (= no dead position)
+ *   d_eids      int32 [T] out: e_t
+ *   d_row_ids   int32 [T][3][H] out
+ * Host errors: ENGRAM_E_ARG.  Device errors: ENGRAM_E_TOKEN_RANGE,
+ * ENGRAM_E_SEQLENS, ENGRAM_E_SLOT_RANGE, ENGRAM_E_NEED_STORE. */
+int engram_compress_hash(const engram_layout* layout, const int32_t* d_tid2eid,
+                         const int32_t* d_tokens, int32_t T, const int32_t* d_cu_seqlens,
+                         int32_t S, const uint8_t* d_seq_start, const int32_t* d_slots,
+                         int32_t* d_store, int32_t num_slots, const uint8_t* d_dead,
+                         int32_t* d_eids, int32_t* d_row_ids, hipStream_t stream);
+
+/* ---- 2. gather + dequant -------------------------------------------------- */
+/* For each token t, order n, head h, element d < D:
+ *   out[t][(n*H + h)*seg_pitch + d] = fp32(q * scale_n[row]) rounded to
+ *   out_dtype, q = e4m3fn value of table_n[row][d], row = row_ids[t][n][h]
+ *   ([VeOmni#1370] PR summary: native FP8 row-wise dequantization on lookup).
+ *   BF16 tables carry no scale and are copied (or widened to fp32).
+ *   Elements d in [D, seg_pitch) of every segment are written as zero.
+ * Arguments:
+ *   d_tables   host array of 3 device pointers, table_n uint8 [rows_n][pitch],
+ *              16-byte aligned
+ *   d_scales   host array of 3 device pointers to float [rows_n] (fp8 tables),
+ *              or NULL (bf16 tables)
+ *   d_row_ids  int32 [T][3][H], as written by engram_compress_hash
+ *   out_dtype  ENGRAM_DTYPE_BF16 (hot path) or ENGRAM_DTYPE_F32 (exact check)
+ *   d_out      [T][out_ld] of out_dtype, 16-byte aligned; out_ld >= k_pad and a
+ *              multiple of 8
+ * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN.  Device error: ENGRAM_E_ROW_RANGE
+ * (that segment is written as zero). */
+int engram_gather_dequant(const engram_layout* layout, const void* const* d_tables,
+                          const float* const* d_scales, const int32_t* d_row_ids, int32_t T,
+                          int32_t out_dtype, void* d_out, int64_t out_ld, hipStream_t stream);
+
+/* ---- 3. projection + gated residual ---------------------------------------- */
+/* v[t][o] = sum_{k < k_pad} rows[t][k] * W[o][k], bf16 x bf16 accumulated in
+ * fp32 on the matrix cores: the Engram connection's wkv projection
+ * ([VeOmni#1370] config commit: the Engram connection is wkv plus a gate that
+ * reads the mHC residual stream).
+ *   d_rows bf16 [T][rows_ld], d_w bf16 [hidden][w_ld] (columns k_pad.. ignored;
+ *   columns of W facing segment padding must be zero), d_v float [T][hidden].
+ *   rows_ld, w_ld >= k_pad and multiples of 8; pointers 16-byte aligned;
+ *   hidden a multiple of 8.
+ * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN. */
+int engram_project(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
+                   const void* d_w, int64_t w_ld, int32_t hidden, float* d_v, int32_t T,
+                   hipStream_t stream);
+
+/* For each token t and stream s < hc_mult:
+ *   z = <x[t][s][:], v[t][:]> / sqrt(hidden),  g = keep_t * sigmoid(z),
+ *   x[t][s][:] <- bf16(x[t][s][:] + g * v[t][:])   (in place; keep_t = 0 leaves
+ *   the stream bit for bit)
+ * ([NeMo-V41] forward contract: Engram writes into the hc residual streams
+ * before its layer; [vLLM-V41] forward: image-span tokens have their gate
+ * zeroed).  d_v float [T][hidden]; d_keep uint8 [T] or NULL (= all kept);
+ * d_streams bf16 [T][hc_mult][hidden], 16-byte aligned; hidden a multiple of 8,
+ * at most 8192.  hc_mult must be 4 (ENGRAM_E_UNSUPPORTED otherwise). */
+int engram_gate_add(const engram_layout* layout, const float* d_v, int32_t hidden,
+                    int32_t hc_mult, const uint8_t* d_keep, void* d_streams, int32_t T,
+                    hipStream_t stream);
+
+/* engram_project followed by engram_gate_add on the same stream; d_v is the
+ * caller's fp32 [T][hidden] workspace.  There is no variant without rows: a
+ * site that has Engram and no looked-up rows is a caller error, never a skip
+ * ([VeOmni#1370] decode-stack commit: a missing n-gram embedding raises). */
+int engram_gated_residual(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
+                          const void* d_w, int64_t w_ld, int32_t hidden, int32_t hc_mult,
+                          const uint8_t* d_keep, void* d_streams, float* d_v, int32_t T,
+                          hipStream_t stream);
+
+/* ---- errors ------------------------------------------------------------- */
+const char* engram_strerror(int status);
+/* Synchronises `stream`, returns the first device-detected status latched on
+ * the current device since the last call (ENGRAM_OK if none) and clears it.
+ * Returns ENGRAM_E_HIP if the synchronisation itself fails. */
+int engram_get_error(hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ENGRAM_H */

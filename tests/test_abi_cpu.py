@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and exports
+every symbol include/engram.h declares; the host layout (bucket primes, floor
+fit, row-count guard, segment geometry) matches the oracle; argument errors."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import engram_inputs as ei
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+eng = pytest.importorskip("hashed_gram_memory_tid2eid_amd")
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "engram.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(engram_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 14, names
+    lib = ctypes.CDLL(eng.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", eng.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(engram_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_codes_have_messages():
+    for name, code in eng.STATUS.items():
+        msg = eng.engram_strerror(code)
+        assert msg and msg != "unknown status", name
+    assert eng.engram_strerror(12345) == "unknown status"
+
+
+def _layout(cfg, **kw):
+    args = dict(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+                heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+                table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN if cfg.table_dtype == "fp8" else eng.ENGRAM_DTYPE_BF16,
+                row_pitch_bytes=cfg.row_pitch_bytes)
+    args.update(kw)
+    return eng.engram_layout_create(**args)
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "decode", "long", "full", "full_bf16"])
+def test_layout_matches_oracle(name):
+    cfg = ei.get_config(name)
+    L = _layout(cfg)
+    ref = oracle.fit_layout([cfg.rows] * 3, cfg.heads)
+    info = L.info
+    assert info.hash_floor == ref.floor
+    assert np.array_equal(np.array(info.primes, dtype=np.uint64), ref.primes)
+    assert np.array_equal(np.array(info.offsets, dtype=np.uint64), ref.offsets)
+    assert list(info.prime_sum) == [int(s) for s in ref.primes.sum(axis=1)]
+    assert info.seg_pitch % 64 == 0 and cfg.row_dim <= info.seg_pitch < cfg.row_dim + 64
+    assert info.k_pad == 3 * cfg.heads * info.seg_pitch
+
+
+def test_layout_given_floor_pages_case(golden):
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg, rows=[1024] * 3, hash_floor=64)
+    assert sum(sum(p) for p in L.info.primes) == golden["prime_sum_floor64"]["value"]
+    ref = oracle.layout_at_floor([1024] * 3, 2, 64)
+    assert np.array_equal(np.array(L.info.primes, dtype=np.uint64), ref.primes)
+
+
+def test_layout_real_model_floor_heads8():
+    """Per-order tables at the released floor 16,000,000 with 8 heads: the prime
+    sums of the three orders add up to the page's first-layer row count."""
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg, heads_per_order=8, rows=[130_000_000] * 3, hash_floor=16_000_000)
+    assert sum(L.info.prime_sum) == 384_006_168
+    ref = oracle.layout_at_floor([130_000_000] * 3, 8, 16_000_000)
+    assert np.array_equal(np.array(L.info.primes, dtype=np.uint64), ref.primes)
+
+
+def test_layout_errors():
+    cfg = ei.get_config("tiny")
+    ref = oracle.layout_at_floor([1024] * 3, 2, 64)
+    need = [int(s) for s in ref.primes.sum(axis=1)]
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, rows=[need[0], need[1] - 1, need[2]], hash_floor=64)
+    assert e.value.status == eng.ENGRAM_E_LAYOUT_ROWS
+    _layout(cfg, rows=need, hash_floor=64)
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, compressed_vocab=65537)
+    assert e.value.status == eng.ENGRAM_E_VC_RANGE
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, row_pitch_bytes=120)
+    assert e.value.status == eng.ENGRAM_E_ALIGN
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, row_pitch_bytes=136)  # not a multiple of 16
+    assert e.value.status == eng.ENGRAM_E_ALIGN
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, heads_per_order=9)
+    assert e.value.status == eng.ENGRAM_E_ARG
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, max_ngram=3)
+    assert e.value.status == eng.ENGRAM_E_ARG
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, pad_token_id=cfg.vocab)
+    assert e.value.status == eng.ENGRAM_E_ARG
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, rows=[1, 1, 1])
+    assert e.value.status == eng.ENGRAM_E_NOFIT
+    # bf16 tables need twice the pitch
+    with pytest.raises(eng.EngramError) as e:
+        _layout(cfg, table_dtype=eng.ENGRAM_DTYPE_BF16, row_pitch_bytes=128)
+    assert e.value.status == eng.ENGRAM_E_ALIGN
+
+
+def test_gather_host_argument_errors_need_no_device():
+    """Errors the host sees are returned before any launch."""
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg)
+    lib = eng._lib
+    P = ctypes.c_void_p
+    three = (P * 3)(None, None, None)
+    rc = lib.engram_gather_dequant(L.handle, three, three, None, 4, 99, None, L.info.k_pad, None)
+    assert rc == eng.ENGRAM_E_ARG
+    rc = lib.engram_project(L.handle, None, L.info.k_pad, None, L.info.k_pad, 0, None, 4, None)
+    assert rc == eng.ENGRAM_E_ARG
+    rc = lib.engram_gate_add(L.handle, None, 256, 3, None, None, 4, None)
+    assert rc == eng.ENGRAM_E_UNSUPPORTED
+    rc = lib.engram_gate_add(L.handle, None, 250, 4, None, None, 4, None)
+    assert rc == eng.ENGRAM_E_ALIGN
+    rc = lib.engram_compress_hash(L.handle, P(16), P(16), 5, P(16), 0, None, None, None, 0, None,
+                                  P(16), P(16), None)
+    assert rc == eng.ENGRAM_E_ARG
+    # empty calls are no-ops
+    assert lib.engram_compress_hash(L.handle, P(16), None, 0, None, 0, None, None, None, 0, None,
+                                    None, None, None) == 0
