@@ -4,7 +4,7 @@ The functions below carry the names of the C ABI in ``include/engram.h`` and do
 argument marshalling only: torch tensors provide device memory and the HIP
 stream; every step of the path runs in the library's kernels.  Importing this
 package fails loudly if the library has not been built (there is no fallback).
-Build it with ``python -m hashed_gram_memory_tid2eid_amd._build``.
+Build it with ``python hashed_gram_memory_tid2eid_amd/build_lib.py``.
 """
 from __future__ import annotations
 
@@ -38,14 +38,38 @@ globals().update(STATUS)
 
 class EngramError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {engram_strerror(status)} (status {status})")
+        msg = f"{where}: {engram_strerror(status)} (status {status})"
+        if status == STATUS.get("ENGRAM_E_HIP"):
+            msg += f" [{_lib.engram_last_hip_error().decode()}]"
+        super().__init__(msg)
         self.status = status
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m hashed_gram_memory_tid2eid_amd._build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python hashed_gram_memory_tid2eid_amd/build_lib.py`")
+
+# torch ships its own HIP runtime (libamdhip64.so, soname libamdhip64.so.7).  The
+# library must bind to that same runtime, or torch's streams and the library's
+# launches live in two runtimes that know nothing of each other.  Loading torch
+# first makes the dynamic loader resolve the library's libamdhip64.so.7 to the
+# copy already in the process.
+import torch  # noqa: E402,F401
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process "
+                      f"({_hip_runtimes_mapped()}); import torch before anything that loads "
+                      "/opt/rocm's libamdhip64")
 _P = ctypes.c_void_p
 _i32, _i64 = ctypes.c_int32, ctypes.c_int64
 
@@ -87,6 +111,7 @@ _sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
 _sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
 _sig("engram_get_error", [_P])
+_sig("engram_last_hip_error", [], ctypes.c_char_p)
 
 
 def engram_strerror(status: int) -> str:

@@ -1,6 +1,7 @@
 """Build of libengram.so (gfx950) in-tree with hipcc.
 
-Usage: ``python -m hashed_gram_memory_tid2eid_amd._build``.  Compiles the single
+Usage: ``python hashed_gram_memory_tid2eid_amd/build_lib.py`` (run by path: importing
+the package loads the library this script builds).  Compiles the single
 device translation unit and the host sources to objects under ``_build/`` and
 links ``hashed_gram_memory_tid2eid_amd/libengram.so``.  Always recompiles.
 """

@@ -11,7 +11,13 @@ namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-inline int hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_E_HIP; }
+thread_local hipError_t g_last_hip = hipSuccess;
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ENGRAM_OK;
+  g_last_hip = e;
+  return ENGRAM_E_HIP;
+}
 
 }  // namespace
 
@@ -19,7 +25,8 @@ extern "C" int engram_tid2eid_check(const engram_layout* L, const int32_t* d_tid
                                     int32_t* pad_eid, hipStream_t stream) {
   if (!L || !d_tid2eid || !pad_eid) return ENGRAM_E_ARG;
   int32_t* d_res = nullptr;
-  if (hipMalloc(&d_res, 3 * sizeof(int32_t)) != hipSuccess) return ENGRAM_E_HIP;
+  hipError_t me = hipMalloc(&d_res, 3 * sizeof(int32_t));
+  if (me != hipSuccess) return hip_status(me);
   int32_t h_res[3] = {0, 0, 0};
   hipError_t e = hipMemcpyAsync(d_res, h_res, sizeof h_res, hipMemcpyHostToDevice, stream);
   engram::MapCheckArgs a;
@@ -32,7 +39,7 @@ extern "C" int engram_tid2eid_check(const engram_layout* L, const int32_t* d_tid
   if (e == hipSuccess) e = hipMemcpyAsync(h_res, d_res, sizeof h_res, hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   hipFree(d_res);
-  if (e != hipSuccess) return ENGRAM_E_HIP;
+  if (e != hipSuccess) return hip_status(e);
   if (h_res[0] != 0 || h_res[1] != a.vc - 1) return ENGRAM_E_MAP_RANGE;
   *pad_eid = h_res[2];
   return ENGRAM_OK;
@@ -163,7 +170,7 @@ extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* 
     g.out = static_cast<char*>(d_out) + (size_t)t0 * out_ld * out_elt;
     g.T = (int32_t)tn;
     hipError_t e = engram::launch_gather_dequant(g, stream);
-    if (e != hipSuccess) return ENGRAM_E_HIP;
+    if (e != hipSuccess) return hip_status(e);
   }
   return ENGRAM_OK;
 }
@@ -227,6 +234,9 @@ extern "C" int engram_gated_residual(const engram_layout* L, const void* d_rows,
 
 extern "C" int engram_get_error(hipStream_t stream) {
   int status = 0;
-  if (engram::read_and_clear_device_error(stream, &status) != hipSuccess) return ENGRAM_E_HIP;
+  hipError_t e = engram::read_and_clear_device_error(stream, &status);
+  if (e != hipSuccess) return hip_status(e);
   return status;
 }
+
+extern "C" const char* engram_last_hip_error(void) { return hipGetErrorName(g_last_hip); }

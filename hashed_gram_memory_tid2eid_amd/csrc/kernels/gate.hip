@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
 }
 
 hipError_t launch_gate_add(const GateArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale error another library left on this thread
   if (a.T == 0) return hipSuccess;
   const int nchunks = a.hidden / 8;
   const int cpt = (nchunks + kGateThreads - 1) / kGateThreads;

@@ -176,6 +176,7 @@ static FastDiv make_fastdiv(uint32_t d) {
 }
 
 hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale error another library left on this thread
   GatherKArgs a;
   a.t0 = g.table[0];
   a.t1 = g.table[1];

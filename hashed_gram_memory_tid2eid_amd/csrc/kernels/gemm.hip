@@ -174,6 +174,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmKArgs
 
 template <int BM, int BN>
 static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale error another library left on this thread
   using S = GemmShape<BM, BN>;
   GemmKArgs a;
   a.A = reinterpret_cast<const __bf16*>(g.A);

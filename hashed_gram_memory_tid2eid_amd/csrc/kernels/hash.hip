@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void store_update_kernel(HashArgs a) {
 }
 
 hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale error another library left on this thread
   const int work = a.T > a.S + 1 ? a.T : a.S + 1;
   const int blocks = (work + 255) / 256;
   hipLaunchKernelGGL(compress_hash_kernel, dim3(blocks), dim3(256), 0, stream, a);
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(256) void map_check_kernel(MapCheckArgs a) {
 }
 
 hipError_t launch_map_check(const MapCheckArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale error another library left on this thread
   hipLaunchKernelGGL(map_check_kernel, dim3((a.vocab + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -230,6 +232,7 @@ __global__ __launch_bounds__(256) void store_op_kernel(StoreArgs a) {
 }
 
 hipError_t launch_store_op(const StoreArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale error another library left on this thread
   const int64_t count = (a.slots == nullptr ? (int64_t)a.num_slots : (int64_t)a.n) * 3;
   if (count == 0) return hipSuccess;
   hipLaunchKernelGGL(store_op_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,

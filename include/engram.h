@@ -248,6 +248,9 @@ const char* engram_strerror(int status);
  * the current device since the last call (ENGRAM_OK if none) and clears it.
  * Returns ENGRAM_E_HIP if the synchronisation itself fails. */
 int engram_get_error(hipStream_t stream);
+/* Name of the last HIP runtime error behind an ENGRAM_E_HIP status returned on
+ * this thread ("hipSuccess" if none); a static string. */
+const char* engram_last_hip_error(void);
 
 #ifdef __cplusplus
 }
