@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--config", default="full", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
+                         "(reference for the HBM byte counters of a profiler run)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -255,6 +258,13 @@ def main():
         "wall_s_timed": wall,
         "setup_s": setup_s,
     }
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, batch, tables, weight, streams_host, args.cpu_budget)
     print(json.dumps(result), flush=True)
