@@ -63,6 +63,29 @@ def algorithmic_per_token(cfg):
     }
 
 
+def measured_traffic(cfg):
+    """HBM bytes per gather launch from the committed profiler counters
+    (profiles/gather_dequant_<workload>_traffic.txt), or None when there is no
+    measurement for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    tag = {"full": "full_fp8"}.get(cfg.name, cfg.name)
+    path = os.path.join(ROOT, "profiles", f"gather_dequant_{tag}_traffic.txt")
+    src = os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "csrc", "kernels", "gather.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha256_16") != sha:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(cfg, batch, tables, weight, streams_host_bits, budget_s: float):
     """The oracle as it stands, single-threaded on a host core, on a bounded token
     sample of the same workload (rows read from the device tables by torch)."""
@@ -244,7 +267,7 @@ def main():
                    "k_pad": site.info.k_pad},
         "roofline": {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": gather_bytes,
+                     "traffic": measured_traffic(cfg), "bytes_per_launch": gather_bytes,
                      "avg_launch_ms": kern_ms["gather_dequant"]},
         "kernels": {
             "compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs},
