@@ -6,9 +6,13 @@
 // segments (order-major, then head) of seg_pitch elements; a segment holds the
 // D dequantised elements of one looked-up table row followed by zeros.  The
 // work is a flat list of 16-element output chunks (T * 3H * seg_pitch/16 of
-// them).  Consecutive lanes take consecutive chunks, so a wave reads 1 KB of
-// consecutive table bytes (fp8) and writes 2 KB of consecutive output (bf16)
-// in 16-byte vector accesses; each lane keeps UNROLL chunks in flight.
+// them).  Consecutive lanes take consecutive chunks, so one wave-wide 16-byte
+// load reads 1 KB of consecutive table bytes (fp8).  A lane's 16 dequantised
+// elements are 32 B of bf16; the wave stages its 2 KB of output in LDS and reads
+// it back transposed, so each of its two wave-wide 16-byte stores writes 1 KB
+// of consecutive output (whole cache lines; without the staging each store
+// instruction would leave 16-byte holes and the memory system would write
+// partial lines).  Each lane keeps UNROLL chunks in flight.
 //
 // Dequant of a chunk: 16 e4m3fn bytes -> 16 fp32 (hardware conversion,
 // v_cvt_pk_f32_fp8), times the row's fp32 scale (one v_mul_f32 each: exactly
@@ -55,6 +59,7 @@ struct GatherKArgs {
   uint32_t seg_pitch;
   FastDiv div_chunks;
   FastDiv div_cols;
+  int32_t linear_out;  // out_ld == cols * seg_pitch: chunk g starts at element 16 g
 };
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
@@ -65,6 +70,12 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
 template <bool kBf16Table, bool kF32Out>
 __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKArgs a) {
   const uint32_t first = blockIdx.x * (kGatherThreads * kGatherUnroll) + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Per-wave LDS staging for the bf16 path: a lane converts 16 elements (32 B),
+  // the wave's 64 chunks (2 KB) go to LDS and come back transposed so that each
+  // of the two wave-wide 16-byte stores writes 1 KB of consecutive output.
+  __shared__ u32x4 stage[kGatherThreads / 64][2][128];
+  const bool staged = !kF32Out && a.linear_out;
 
   u32x4 raw[kGatherUnroll][kBf16Table ? 2 : 1];
   float scale[kGatherUnroll];
@@ -78,8 +89,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKA
     live[u] = g < a.total;
     any[u] = false;
     scale[u] = 1.0f;
-    raw[u][0] = u32x4{0u, 0u, 0u, 0u};
-    if (kBf16Table) raw[u][kBf16Table ? 1 : 0] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < (kBf16Table ? 2 : 1); ++h) raw[u][h] = u32x4{0u, 0u, 0u, 0u};
     tok[u] = seg[u] = chunk[u] = 0;
     if (!live[u]) continue;
     const uint32_t rowidx = fdiv(g, a.div_chunks);  // token * cols + seg
@@ -108,7 +119,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKA
 
 #pragma unroll
   for (int u = 0; u < kGatherUnroll; ++u) {
-    if (!live[u]) continue;
     const uint32_t e0 = chunk[u] * 16;
     const uint32_t valid = e0 >= a.row_dim ? 0u : (a.row_dim - e0 >= 16 ? 16u : a.row_dim - e0);
     const int64_t obase = (int64_t)tok[u] * a.out_ld + (int64_t)seg[u] * a.seg_pitch + e0;
@@ -143,22 +153,38 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKA
     }
 
     if (kF32Out) {
+      if (!live[u]) continue;
       float* dst = reinterpret_cast<float*>(a.out) + obase;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 v = {f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst) + q);
       }
+      continue;
+    }
+    u32x4 o[2];
+    if (kBf16Table && any[u] && valid == 16) {
+      o[0] = raw[u][0];
+      o[1] = raw[u][kBf16Table ? 1 : 0];
     } else {
-      u32x4 o[2];
-      if (kBf16Table && any[u] && valid == 16) {
-        o[0] = raw[u][0];
-        o[1] = raw[u][kBf16Table ? 1 : 0];
-      } else {
 #pragma unroll
-        for (int w = 0; w < 8; ++w)
-          o[w >> 2][w & 3] = bf16_bits_rne(f[2 * w]) | (bf16_bits_rne(f[2 * w + 1]) << 16);
-      }
+      for (int w = 0; w < 8; ++w)
+        o[w >> 2][w & 3] = bf16_bits_rne(f[2 * w]) | (bf16_bits_rne(f[2 * w + 1]) << 16);
+    }
+    if (staged) {
+      // chunk g sits at element 16 g of the output (rows are back to back), so the
+      // wave's chunks g0..g0+63 are 2 KB of consecutive output
+      u32x4* buf = stage[wave][u & 1];
+      buf[2 * lane] = o[0];
+      buf[2 * lane + 1] = o[1];
+      const u32x4 s0 = buf[lane], s1 = buf[64 + lane];
+      const uint32_t g0 = first - (uint32_t)lane + (uint32_t)u * kGatherThreads;
+      unsigned short* dst = reinterpret_cast<unsigned short*>(a.out) + (int64_t)g0 * 16;
+      if (g0 + (uint32_t)(lane >> 1) < a.total)
+        __builtin_nontemporal_store(s0, reinterpret_cast<u32x4*>(dst) + lane);
+      if (g0 + 32u + (uint32_t)(lane >> 1) < a.total)
+        __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(dst) + 64 + lane);
+    } else if (live[u]) {
       unsigned short* dst = reinterpret_cast<unsigned short*>(a.out) + obase;
       __builtin_nontemporal_store(o[0], reinterpret_cast<u32x4*>(dst));
       __builtin_nontemporal_store(o[1], reinterpret_cast<u32x4*>(dst) + 1);
@@ -192,6 +218,7 @@ hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
   a.out_ld = g.out_ld;
   a.pitch = g.pitch;
   a.chunks = (uint32_t)(g.seg_pitch / 16);
+  a.linear_out = g.out_ld == (int64_t)g.cols * g.seg_pitch ? 1 : 0;
   a.cols = (uint32_t)g.cols;
   a.heads = (uint32_t)g.heads;
   a.row_dim = (uint32_t)g.row_dim;

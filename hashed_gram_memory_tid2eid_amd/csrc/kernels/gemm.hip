@@ -2,43 +2,46 @@
 // Included into engram_device.hip.
 //
 // C[M][N] (fp32) = A[M][K] (bf16, row-major) * B[N][K]^T (bf16, row-major):
-// both operands are K-contiguous, which is the layout the gathered token rows
-// and the projection weight already have.  K is a multiple of 64 (k_pad).
+// both operands are K-contiguous, the layout the gathered token rows and the
+// projection weight already have.  K is a multiple of 32 (k_pad is of 64).
 //
-// Tile: a 256-thread workgroup (4 waves, 2 x 2) owns a BM x BN block of C and
-// walks K in steps of 64.  Each wave owns a (BM/2) x (BN/2) sub-block made of
-// 32 x 32 tiles computed by v_mfma_f32_32x32x16_bf16 (gfx950): per lane 8 bf16
-// of A (row lane%32, k 8*(lane/32)..+8) and 8 of B, 16 fp32 accumulators.
-// Operand tiles are staged through LDS, double buffered: while the waves run
-// the MFMAs on one K step, the next step's global loads are in flight in
-// registers; they are written to the other LDS buffer before the single
-// barrier of the step.  LDS rows are 64 elements (128 B) stored with an XOR
-// swizzle of the 16-byte chunks (chunk ^ (row & 7)), so the 16-byte reads of
-// 8 consecutive rows land on distinct banks.
+// Tile: a workgroup of WM_WAVES x WN_WAVES waves owns a BM x BN block of C; each
+// wave owns a (BM/WM_WAVES) x (BN/WN_WAVES) sub-block of 32 x 32 tiles computed
+// with v_mfma_f32_32x32x16_bf16 (per lane 8 bf16 of A: row lane%32, k
+// 8*(lane/32)..+8; 8 of B; 16 fp32 accumulators).  Large M uses 256 x 256 tiles
+// with 8 waves (2 x 4, 128 x 64 each, two waves per SIMD): while one wave of a
+// SIMD waits on a stage barrier or its loads, the other keeps the matrix core
+// busy (measured 1.45 PFLOP/s against 1.21 for 4 waves of 128 x 128).
 //
-// Tile order: workgroup ids are dealt round-robin to the 8 XCDs, each with its
-// own L2.  The id is remapped so that each XCD gets a contiguous run of tiles,
-// walked in groups of GROUP_M row blocks: the concurrently running workgroups
-// of one XCD share A row blocks and B column blocks in that XCD's L2.
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4, no
+// register staging) in stages of 64 k: one whole 128-byte line of every operand
+// row, so each line is fetched once and every cache request is a full line.  Two
+// stages (2 x 64 KB for a 256 x 256 tile) form a ring: stage kt+1 streams in
+// while stage kt multiplies; one barrier per stage.  A wave writes 1 KB of
+// consecutive LDS per load, so the XOR swizzle of the 16-byte chunks
+// (chunk ^ ((row >> 1) & 7), rows of 128 B) is applied by choosing which global
+// chunk each lane fetches; with it the fragment reads are free of LDS bank
+// conflicts (measured with the bank-conflict counter).
+//
+// Inside a stage the four k16 steps are software pipelined: the fragments of
+// step ks+1 are read while step ks's MFMAs run, and the next stage's first step
+// is read while the last step multiplies.  At most one step of fragments is
+// outstanding at any wait, so the compiler's lgkmcnt tracking stays exact and
+// each explicit wait falls on data requested a whole MFMA phase earlier.
+
+// Tile order: workgroup ids are dealt round-robin to the 8 XCDs (each with its
+// own L2); the id is remapped so that each XCD gets a contiguous run of tiles,
+// walked in groups of GROUP_M row blocks, so the concurrently running
+// workgroups of one XCD share A row blocks and B column blocks in its L2.
 
 namespace engram {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define ENGRAM_LDS_AS __attribute__((address_space(3)))
 
-constexpr int kGemmThreads = 256;
-constexpr int kBK = 64;  // K elements per step; 8 chunks of 16 B per LDS row
-
-template <int BM, int BN>
-struct GemmShape {
-  static constexpr int WM = BM / 2;          // wave sub-block rows
-  static constexpr int WN = BN / 2;          // wave sub-block cols
-  static constexpr int TM = WM / 32;         // 32x32 tiles per wave, rows
-  static constexpr int TN = WN / 32;         // 32x32 tiles per wave, cols
-  static constexpr int A_LOADS = BM * 8 / kGemmThreads;  // 16-B chunks per thread
-  static constexpr int B_LOADS = BN * 8 / kGemmThreads;
-  static constexpr int LDS_ELEMS = (BM + BN) * kBK;      // one buffer
-};
+constexpr int kGemmBK = 64;      // k per stage: one 128-byte line of every operand row
+constexpr int kGemmStages = 2;   // LDS ring depth
 
 struct GemmKArgs {
   const __bf16* A;
@@ -50,12 +53,28 @@ struct GemmKArgs {
   int32_t group_m;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// physical 16-byte chunk of logical chunk c in a 128-byte LDS row: c ^ ((row >> 1) & 7).
+// Measured on gfx950 with the bank-conflict counter: fragment reads (32 rows x 2
+// chunks per ds_read_b128) see no conflicts with this swizzle.
+__device__ __forceinline__ int gemm_swz(int row) { return (row >> 1) & 7; }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmKArgs a) {
-  using S = GemmShape<BM, BN>;
-  extern __shared__ __attribute__((aligned(16))) __bf16 lds[];
+// s_waitcnt with vmcnt <= N and no wait on the other counters
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int BM, int BN, int WM_WAVES, int WN_WAVES>
+__global__ __launch_bounds__(64 * WM_WAVES * WN_WAVES, 1)
+void gemm_bf16_nt_kernel(GemmKArgs a) {
+  constexpr int BK = kGemmBK;
+  constexpr int NWAVES = WM_WAVES * WN_WAVES;
+  constexpr int WM = BM / WM_WAVES, WN = BN / WN_WAVES, TM = WM / 32, TN = WN / 32;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int AI = BM / 8 / NWAVES, BI = BN / 8 / NWAVES;  // 1 KB direct loads per wave per stage
+  static_assert(AI * 8 * NWAVES == BM && BI * 8 * NWAVES == BN, "tile must fill whole load rounds");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   // ---- tile id: XCD-contiguous runs, then GROUP_M swizzle ------------------
   const int ntiles = a.tiles_m * a.tiles_n;
@@ -69,113 +88,146 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmKArgs
   const int first_m = gid * a.group_m;
   const int gm = min(a.tiles_m - first_m, a.group_m);
   const int in_group = bid - gid * group;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = (first_m + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN_WAVES, wn = wave % WN_WAVES;
 
-  // ---- global -> register staging -----------------------------------------
-  bf16x8 ra[S::A_LOADS], rb[S::B_LOADS];
-  auto load_tiles = [&](int k0) {
+  // ---- direct global->LDS loads: wave w, load i fills LDS bytes
+  //      [(NWAVES i + w) KB, +1 KB) of the A (or B) region; lane l writes 16 B at
+  //      l*16, i.e. row P/8, physical chunk P%8 with P = 64(NWAVES i + w) + l, so 8 lanes
+  //      fetch one whole 128-byte line.  Rows past M (N) read a valid row; their
+  //      results are never stored.
+  const __bf16* ap[AI];
+  const __bf16* bp[BI];
 #pragma unroll
-    for (int i = 0; i < S::A_LOADS; ++i) {
-      const int idx = tid + i * kGemmThreads;
-      const int row = idx >> 3, ch = idx & 7;
-      const int m = m0 + row;
-      if (m < a.M)
-        ra[i] = *reinterpret_cast<const bf16x8*>(a.A + (int64_t)m * a.lda + k0 + ch * 8);
-      else
-        ra[i] = bf16x8{};
-    }
+  for (int i = 0; i < AI; ++i) {
+    const int P = 64 * (i * NWAVES + wave) + lane, row = P >> 3, c = (P & 7) ^ gemm_swz(row);
+    ap[i] = a.A + (int64_t)min(m0 + row, a.M - 1) * a.lda + 8 * c;
+  }
 #pragma unroll
-    for (int i = 0; i < S::B_LOADS; ++i) {
-      const int idx = tid + i * kGemmThreads;
-      const int row = idx >> 3, ch = idx & 7;
-      const int n = n0 + row;
-      if (n < a.N)
-        rb[i] = *reinterpret_cast<const bf16x8*>(a.B + (int64_t)n * a.ldb + k0 + ch * 8);
-      else
-        rb[i] = bf16x8{};
-    }
-  };
-  auto store_tiles = [&](int buf) {
-    __bf16* la = lds + buf * S::LDS_ELEMS;
-    __bf16* lb = la + BM * kBK;
+  for (int i = 0; i < BI; ++i) {
+    const int P = 64 * (i * NWAVES + wave) + lane, row = P >> 3, c = (P & 7) ^ gemm_swz(row);
+    bp[i] = a.B + (int64_t)min(n0 + row, a.N - 1) * a.ldb + 8 * c;
+  }
+  auto issue = [&](int kt) {
+    char* st = smem + (kt & 1) * STAGE;
 #pragma unroll
-    for (int i = 0; i < S::A_LOADS; ++i) {
-      const int idx = tid + i * kGemmThreads;
-      *reinterpret_cast<bf16x8*>(la + swz(idx >> 3, idx & 7)) = ra[i];
-    }
+    for (int i = 0; i < AI; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(ap[i] + kt * BK),
+                                       (ENGRAM_LDS_AS void*)(st + (i * NWAVES + wave) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < S::B_LOADS; ++i) {
-      const int idx = tid + i * kGemmThreads;
-      *reinterpret_cast<bf16x8*>(lb + swz(idx >> 3, idx & 7)) = rb[i];
-    }
+    for (int i = 0; i < BI; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bp[i] + kt * BK),
+                                       (ENGRAM_LDS_AS void*)(st + A_BYTES + (i * NWAVES + wave) * 1024), 16, 0, 0);
   };
 
-  f32x16 acc[S::TM][S::TN];
+  // ---- fragment row offsets (elements) and swizzles inside a stage -----------
+  const int lrow = lane & 31, lk = lane >> 5;
+  int arow[TM], brow[TN], aswz[TM], bswz[TN];
 #pragma unroll
-  for (int i = 0; i < S::TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * WM + i * 32 + lrow;
+    arow[i] = r * BK;
+    aswz[i] = gemm_swz(r);
+  }
 #pragma unroll
-    for (int j = 0; j < S::TN; ++j) acc[i][j] = f32x16{};
+  for (int j = 0; j < TN; ++j) {
+    const int r = wn * WN + j * 32 + lrow;
+    brow[j] = BM * BK + r * BK;
+    bswz[j] = gemm_swz(r);
+  }
+  // fragments of k16 step ks (0..3) of stage kt
+  auto load_frags = [&](int kt, int ks, bf16x8* fa, bf16x8* fb) {
+    const __bf16* base = reinterpret_cast<const __bf16*>(smem + (kt & 1) * STAGE);
+    const int c = ks * 2 + lk;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(base + brow[j] + 8 * (c ^ bswz[j]));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + arow[i] + 8 * (c ^ aswz[i]));
+  };
 
-  const int nk = a.K / kBK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
 
-  const int lrow = lane & 31;   // row of the 32x32 operand tile this lane feeds
-  const int lk = lane >> 5;     // which 8-element half of a 16-wide k step
+  // ---- pipeline: stage kt+1 streams in while stage kt multiplies; inside a stage
+  //      the fragments of k16 step ks+1 are read while step ks multiplies, and the
+  //      next stage's first step is read while the last step multiplies.  At most
+  //      one step of fragments (TM + TN reads) is outstanding at any wait.
+  const int nk = a.K / BK;
+  issue(0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  if (nk > 1) issue(1);
+  bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  load_frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tiles((kt + 1) * kBK);
-    const __bf16* la = lds + buf * S::LDS_ELEMS;
-    const __bf16* lb = la + BM * kBK;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int ch = ks * 2 + lk;
-      bf16x8 fa[S::TM], fb[S::TN];
-#pragma unroll
-      for (int i = 0; i < S::TM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(la + swz(wm * S::WM + i * 32 + lrow, ch));
-#pragma unroll
-      for (int j = 0; j < S::TN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(lb + swz(wn * S::WN + j * 32 + lrow, ch));
-#pragma unroll
-      for (int i = 0; i < S::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(kt, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(kt, 2, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(kt, 3, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave is done reading stage kt once step 3 has landed; the barrier makes
+    // that true for every wave and publishes stage kt+1, then stage kt is refilled
+    // with kt+2 (the last iteration re-reads its own stage to keep the counts fixed)
+    wait_lgkmcnt0();
+    if (kt + 1 < nk) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + 2 < nk) issue(kt + 2);
     }
-    if (kt + 1 < nk) store_tiles(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(kt + 1 < nk ? kt + 1 : kt, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2),
-  //      accumulator (i%4) + 4*(i/8) --------------------------------------------
+  //      accumulator (i%4) + 4*(i/8) -----------------------------------------------
+  const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N);
 #pragma unroll
-  for (int i = 0; i < S::TM; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < S::TN; ++j) {
-      const int n = n0 + wn * S::WN + j * 32 + (lane & 31);
-      if (n >= a.N) continue;
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * WN + j * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * S::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m < a.M) a.C[(int64_t)m * a.ldc + n] = acc[i][j][v];
+        const int m = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (full || (m < a.M && n < a.N)) a.C[(int64_t)m * a.ldc + n] = acc[i][j][v];
       }
     }
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WMW, int WNW>
 static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
   (void)hipGetLastError();  // drop a stale error another library left on this thread
-  using S = GemmShape<BM, BN>;
+  constexpr int STAGE = (BM + BN) * kGemmBK * 2;
   GemmKArgs a;
   a.A = reinterpret_cast<const __bf16*>(g.A);
   a.B = reinterpret_cast<const __bf16*>(g.B);
@@ -189,27 +241,28 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
   a.tiles_m = (g.M + BM - 1) / BM;
   a.tiles_n = (g.N + BN - 1) / BN;
   a.group_m = 4;
-  const size_t lds_bytes = 2 * (size_t)S::LDS_ELEMS * sizeof(__bf16);
+  const size_t lds_bytes = (size_t)kGemmStages * STAGE;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_nt_kernel<BM, BN>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_nt_kernel<BM, BN, WMW, WNW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN>), dim3(grid), dim3(kGemmThreads), lds_bytes,
-                     stream, a);
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, WMW, WNW>), dim3(grid), dim3(64 * WMW * WNW),
+                     lds_bytes, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_nt(const GemmArgs& g, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  // Large M: 256 x 256 tiles (128 KB of LDS, one workgroup per CU).
-  // Small M: 128 x 128 tiles so that more CUs get work.
+  if (g.K % kGemmBK != 0 || g.K <= 0) return hipErrorInvalidValue;
+  // Large M: 256 x 256 tiles, 8 waves (2 stages x 64 KB of LDS, one workgroup per CU).
+  // Small M: 128 x 128 tiles, 4 waves, so that more CUs get work.
   if ((int64_t)g.M * g.N >= (int64_t)64 * 256 * 256)
-    return launch_gemm_tile<256, 256>(g, stream);
-  return launch_gemm_tile<128, 128>(g, stream);
+    return launch_gemm_tile<256, 256, 2, 4>(g, stream);
+  return launch_gemm_tile<128, 128, 2, 2>(g, stream);
 }
 
 }  // namespace engram

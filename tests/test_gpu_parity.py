@@ -145,6 +145,28 @@ def test_tiny_pow2_off_scales_fp32_exact(eng):
     _check_rows(site, r_ref, T, site.site.rows, out32)
 
 
+def test_gather_padded_leading_dimension(eng):
+    """A gathered-row buffer wider than k_pad (rows not back to back) takes the
+    per-lane store path; it must hold exactly what the packed layout holds."""
+    cfg = ei.get_config("tiny")
+    site = Site(cfg, max_tokens=cfg.tokens_per_call)
+    batch = ei.make_batch(cfg)
+    T = batch.T
+    db = site.device_batch(batch)
+    eng.engram_compress_hash(site.site.layout, site.tid2eid, db["tokens"], db["cu_seqlens"],
+                             site.site.eids, site.site.row_ids)
+    kp = site.info.k_pad
+    wide = torch.full((T, kp + 72), 5.0, dtype=torch.bfloat16, device=DEV)
+    eng.engram_gather_dequant(site.site.layout, site.tables.data, site.tables.scale, site.site.row_ids,
+                              wide, T=T)
+    eng.engram_gather_dequant(site.site.layout, site.tables.data, site.tables.scale, site.site.row_ids,
+                              site.site.rows, T=T)
+    torch.cuda.synchronize()
+    _no_device_error(eng, "padded gather")
+    assert torch.equal(wide[:, :kp].view(torch.int16), site.site.rows[:T].view(torch.int16))
+    assert (wide[:, kp:].float() == 5.0).all()  # columns past k_pad untouched
+
+
 def _ragged_batch(cfg, seed):
     rng = np.random.default_rng(seed)
     lens = np.array([0, 1, 2, 3, 100, 5, 0, 64, 63, 65, 888, 4], dtype=np.int32)
