@@ -31,13 +31,15 @@
 
 // Tile order: workgroup ids are dealt round-robin to the 8 XCDs (each with its
 // own L2); the id is remapped so that each XCD gets a contiguous run of tiles,
-// walked in groups of GROUP_M row blocks, so the concurrently running
+// walked in groups of GROUP_M = 2 row blocks (measured best of 1/2/4/8/16), so the
+// concurrently running
 // workgroups of one XCD share A row blocks and B column blocks in its L2.
 
 namespace engram {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define ENGRAM_LDS_AS __attribute__((address_space(3)))
 
 constexpr int kGemmBK = 64;      // k per stage: one 128-byte line of every operand row
@@ -51,6 +53,7 @@ struct GemmKArgs {
   int32_t M, N, K;
   int32_t tiles_m, tiles_n;
   int32_t group_m;
+  int32_t vec_store;  // C 16-byte aligned and ldc % 4 == 0: whole-tile stores may be 16-byte
 };
 
 // physical 16-byte chunk of logical chunk c in a 128-byte LDS row: c ^ ((row >> 1) & 7).
@@ -207,18 +210,44 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2),
-  //      accumulator (i%4) + 4*(i/8) -----------------------------------------------
-  const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+  // ---- epilogue: D[r][c] of a 32x32 tile sits in lane c + 32*((r/4)%2),
+  //      accumulator (r%4) + 4*(r/8).  Each wave stages one 32-row slab of its
+  //      sub-block (32 x WN fp32) in its own LDS area, then writes the slab back
+  //      row by row with 16-byte stores, so every store instruction covers whole
+  //      row segments of C instead of scattering 4-byte values.
+  constexpr int SLAB = 32 * WN;                 // floats per staged slab
+  constexpr int PITCH = WN + 4;                 // LDS row pitch (floats), breaks bank aliasing
+  static_assert(NWAVES * 32 * PITCH * 4 <= 2 * STAGE, "epilogue staging must fit in the ring");
+  (void)SLAB;
+  __builtin_amdgcn_s_barrier();                 // every wave is done with the operand ring
+  float* slab = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
+  const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N) && a.vec_store;
+  constexpr int LANES_PER_ROW = WN / 4;         // 16-byte pieces per staged row
+  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WN + j * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (full || (m < a.M && n < a.N)) a.C[(int64_t)m * a.ldc + n] = acc[i][j][v];
+        const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        slab[r * PITCH + j * 32 + (lane & 31)] = acc[i][j][v];
+      }
+    }
+    const int gm0 = m0 + wm * WM + i * 32;
+    const int gn = n0 + wn * WN + (lane % LANES_PER_ROW) * 4;
+#pragma unroll
+    for (int q = 0; q < 32 / ROWS_PER_PASS; ++q) {
+      const int r = q * ROWS_PER_PASS + lane / LANES_PER_ROW;
+      const f32x4 val = *reinterpret_cast<const f32x4*>(slab + r * PITCH + (lane % LANES_PER_ROW) * 4);
+      const int m = gm0 + r;
+      float* dst = a.C + (int64_t)m * a.ldc + gn;
+      if (full) {
+        *reinterpret_cast<f32x4*>(dst) = val;
+      } else if (m < a.M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gn + e < a.N) dst[e] = val[e];
       }
     }
   }
@@ -240,7 +269,8 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
   a.K = g.K;
   a.tiles_m = (g.M + BM - 1) / BM;
   a.tiles_n = (g.N + BN - 1) / BN;
-  a.group_m = 4;
+  a.group_m = 2;
+  a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
   const size_t lds_bytes = (size_t)kGemmStages * STAGE;
   static bool attr_set = false;
   if (!attr_set) {
