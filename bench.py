@@ -14,7 +14,7 @@ Prints one JSON line: tokens/s, the roofline of the gather kernel (HBM bytes
 the method must move / measured average launch time, against 8 TB/s), the
 per-kernel breakdown, and the oracle's single-core throughput on a bounded
 token sample.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-[--config full|full_bf16|long|prefill|decode|tiny] [--no-cpu-baseline]
+[--config full|full_bf16|long|prefill|decode|tiny] [--path split|fused] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="full", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--path", default="split", choices=["split", "fused"],
+                    help="split: gather_dequant + project (default, faster); fused: gather_project")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -185,7 +187,7 @@ def main():
                       heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
                       table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes,
                       tid2eid=tid2eid, tables=tables.data, scales=tables.scale, weight=weight,
-                      hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=T)
+                      hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=T, path=args.path)
     streams = ei.make_streams(cfg, T, dev)
     streams_host = None
     if not args.no_cpu_baseline:
@@ -208,12 +210,18 @@ def main():
                                  slots=sl, store=store)
         if ev:
             ev[1].record()
-        eng.engram_gather_dequant(L, site.tables, site.scales, site.row_ids, site.rows, T=T)
-        if ev:
-            ev[2].record()
-        eng.engram_project(L, site.rows, site.weight, site.v, T=T)
-        if ev:
-            ev[3].record()
+        if args.path == "fused":
+            eng.engram_gather_project(L, site.tables, site.scales, site.row_ids, site.weight, site.v, T=T)
+            if ev:
+                ev[2].record()
+                ev[3].record()
+        else:
+            eng.engram_gather_dequant(L, site.tables, site.scales, site.row_ids, site.rows, T=T)
+            if ev:
+                ev[2].record()
+            eng.engram_project(L, site.rows, site.weight, site.v, T=T)
+            if ev:
+                ev[3].record()
         eng.engram_gate_add(L, site.v, streams, T=T)
         if ev:
             ev[4].record()
@@ -237,16 +245,40 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
     names = ["compress_hash", "gather_dequant", "project", "gate_add"]
-    kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    if args.path == "fused":
+        names = ["compress_hash", "gather_project", None, "gate_add"]
+    kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+               for j, n in enumerate(names) if n}
 
     per = algorithmic_per_token(cfg)
     def gbs(b, ms):
         return b / (ms * 1e-3) / 1e9
     gather_bytes = per["gather_bytes"] * T
-    gather_gbs = gbs(gather_bytes, kern_ms["gather_dequant"])
-    proj_tflops = per["project_flops"] * T / (kern_ms["project"] * 1e-3) / 1e12
+    proj_flops = per["project_flops"] * T
     gate_gbs = gbs(per["gate_bytes"] * T, kern_ms["gate_add"])
     hash_gbs = gbs(per["hash_bytes"] * T, kern_ms["compress_hash"])
+    kernels = {"compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs}}
+    if args.path == "fused":
+        fused_tflops = proj_flops / (kern_ms["gather_project"] * 1e-3) / 1e12
+        kernels["gather_project"] = {"ms": kern_ms["gather_project"], "bound": "mfma",
+                                     "TFLOP/s": fused_tflops, "frac": fused_tflops / BF16_PEAK_TFLOPS}
+        roofline = {"bound": "mfma", "kernel": "gather_project", "achieved": fused_tflops,
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": fused_tflops / BF16_PEAK_TFLOPS,
+                    "traffic": None, "flops_per_launch": proj_flops,
+                    "avg_launch_ms": kern_ms["gather_project"]}
+    else:
+        gather_gbs = gbs(gather_bytes, kern_ms["gather_dequant"])
+        proj_tflops = proj_flops / (kern_ms["project"] * 1e-3) / 1e12
+        kernels["gather_dequant"] = {"ms": kern_ms["gather_dequant"], "bound": "hbm", "GB/s": gather_gbs,
+                                     "frac": gather_gbs / HBM_PEAK_GBS}
+        kernels["project"] = {"ms": kern_ms["project"], "bound": "mfma", "TFLOP/s": proj_tflops,
+                              "frac": proj_tflops / BF16_PEAK_TFLOPS}
+        roofline = {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
+                    "traffic": measured_traffic(cfg), "bytes_per_launch": gather_bytes,
+                    "avg_launch_ms": kern_ms["gather_dequant"]}
+    kernels["gate_add"] = {"ms": kern_ms["gate_add"], "bound": "hbm", "GB/s": gate_gbs,
+                           "frac": gate_gbs / HBM_PEAK_GBS}
 
     result = {
         "metric": METRIC,
@@ -264,23 +296,38 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[cfg.name], "name": cfg.name, "tokens_per_step": T,
                    "table_dtype": cfg.table_dtype, "rows_per_table": cfg.rows, "row_dim": cfg.row_dim,
                    "heads_per_order": cfg.heads, "hidden": cfg.hidden, "hc_mult": cfg.hc_mult,
-                   "k_pad": site.info.k_pad},
-        "roofline": {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg), "bytes_per_launch": gather_bytes,
-                     "avg_launch_ms": kern_ms["gather_dequant"]},
-        "kernels": {
-            "compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs},
-            "gather_dequant": {"ms": kern_ms["gather_dequant"], "bound": "hbm", "GB/s": gather_gbs,
-                               "frac": gather_gbs / HBM_PEAK_GBS},
-            "project": {"ms": kern_ms["project"], "bound": "mfma", "TFLOP/s": proj_tflops,
-                        "frac": proj_tflops / BF16_PEAK_TFLOPS},
-            "gate_add": {"ms": kern_ms["gate_add"], "bound": "hbm", "GB/s": gate_gbs,
-                         "frac": gate_gbs / HBM_PEAK_GBS},
-        },
+                   "k_pad": site.info.k_pad, "path": args.path},
+        "roofline": roofline,
+        "kernels": kernels,
         "wall_s_timed": wall,
         "setup_s": setup_s,
     }
+    if args.path == "split" and cfg.table_dtype == "fp8":
+        # the other path on the same inputs, outside the timed region: the fused
+        # gather + projection against gather_dequant + project
+        v_alt = torch.empty_like(site.v)
+        reps = max(3, min(args.steps, 10))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        eng.engram_gather_project(L, site.tables, site.scales, site.row_ids, site.weight, v_alt, T=T)
+        e[0].record()
+        for _ in range(reps):
+            eng.engram_gather_project(L, site.tables, site.scales, site.row_ids, site.weight, v_alt, T=T)
+        e[1].record()
+        for _ in range(reps):
+            eng.engram_gather_dequant(L, site.tables, site.scales, site.row_ids, site.rows, T=T)
+            eng.engram_project(L, site.rows, site.weight, site.v, T=T)
+        e[2].record()
+        torch.cuda.synchronize()
+        eng.check_device_error("fused comparison")
+        f_ms, s_ms = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+        result["alt_paths"] = {
+            "gather_project_fused": {"ms": f_ms, "TFLOP/s": proj_flops / (f_ms * 1e-3) / 1e12,
+                                     "bitwise_equal_v": bool(torch.equal(v_alt.view(torch.int32),
+                                                                         site.v.view(torch.int32)))},
+            "gather_dequant_plus_project": {"ms": s_ms},
+            "reps": reps,
+        }
+        del v_alt
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

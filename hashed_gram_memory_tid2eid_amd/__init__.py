@@ -107,6 +107,7 @@ _sig("engram_store_read", [_P, _P, _i32, _P, _i32, _P, _P])
 _sig("engram_compress_hash", [_P, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _P, _P, _P, _P])
 _sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _P])
 _sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
+_sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _P, _i64, _i32, _P, _P])
 _sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
 _sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
@@ -322,6 +323,28 @@ def engram_project(layout: Layout, rows, w, v, *, T: Optional[int] = None, strea
     _check(_lib.engram_project(layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
                                _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
                                _dev(v, torch.float32, "v"), T, _stream(stream)), "engram_project")
+
+
+def engram_gather_project(layout: Layout, tables: Sequence, scales: Sequence, row_ids, w, v, *,
+                          T: Optional[int] = None, stream=None):
+    import torch
+    if T is None:
+        T = row_ids.shape[0]
+    info = layout.info
+    _need(row_ids.numel() >= T * 3 * info.heads, "row_ids too small")
+    _need(w.dim() == 2 and v.dim() == 2 and v.shape[0] >= T and v.shape[1] == w.shape[0],
+          "v must be [T][hidden]")
+    pitch = layout.desc.row_pitch_bytes
+    for n, t in enumerate(tables):
+        _need(t.numel() >= info.rows[n] * pitch, f"table {n} smaller than rows x pitch")
+    for n, sc in enumerate(scales):
+        _need(sc.numel() >= info.rows[n], f"scale {n} smaller than rows")
+    tp = (_P * 3)(*[_dev(t, torch.uint8, "table") for t in tables])
+    sp = (_P * 3)(*[_dev(s, torch.float32, "scale") for s in scales])
+    _check(_lib.engram_gather_project(layout.handle, tp, sp, _dev(row_ids, torch.int32, "row_ids"), T,
+                                      _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
+                                      _dev(v, torch.float32, "v"), _stream(stream)),
+           "engram_gather_project")
 
 
 def engram_gate_add(layout: Layout, v, streams, *, keep=None, T: Optional[int] = None, stream=None):

@@ -198,6 +198,41 @@ extern "C" int engram_project(const engram_layout* L, const void* d_rows, int64_
   return hip_status(engram::launch_gemm_bf16_nt(g, stream));
 }
 
+extern "C" int engram_gather_project(const engram_layout* L, const void* const* d_tables,
+                                     const float* const* d_scales, const int32_t* d_row_ids,
+                                     int32_t T, const void* d_w, int64_t w_ld, int32_t hidden,
+                                     float* d_v, hipStream_t stream) {
+  if (!L || T < 0 || hidden < 1 || !d_tables || !d_scales) return ENGRAM_E_ARG;
+  if (L->desc.table_dtype != ENGRAM_DTYPE_FP8_E4M3FN) return ENGRAM_E_UNSUPPORTED;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_row_ids || !d_w || !d_v) return ENGRAM_E_ARG;
+  const int64_t pitch = L->desc.row_pitch_bytes;
+  if (pitch < L->seg_pitch || pitch % 16 != 0) return ENGRAM_E_ALIGN;
+  if (w_ld < L->k_pad || w_ld % 8 != 0) return ENGRAM_E_ALIGN;
+  if (!aligned(d_w, 16) || !aligned(d_v, 4)) return ENGRAM_E_ALIGN;
+  engram::GatherGemmArgs g;
+  for (int n = 0; n < 3; ++n) {
+    if (!d_tables[n] || !d_scales[n]) return ENGRAM_E_ARG;
+    if (!aligned(d_tables[n], 16) || !aligned(d_scales[n], 4)) return ENGRAM_E_ALIGN;
+    g.table[n] = static_cast<const uint8_t*>(d_tables[n]);
+    g.scale[n] = d_scales[n];
+    g.rows[n] = L->desc.rows[n];
+  }
+  g.row_ids = d_row_ids;
+  g.pitch = pitch;
+  g.row_dim = L->desc.row_dim;
+  g.seg_pitch = (int32_t)L->seg_pitch;
+  g.cols = L->cols;
+  g.heads = L->heads;
+  g.B = d_w;
+  g.ldb = w_ld;
+  g.C = d_v;
+  g.ldc = hidden;
+  g.M = T;
+  g.N = hidden;
+  return hip_status(engram::launch_gemm_gather_fp8(g, stream));
+}
+
 extern "C" int engram_gate_add(const engram_layout* L, const float* d_v, int32_t hidden,
                                int32_t hc_mult, const uint8_t* d_keep, void* d_streams,
                                int32_t T, hipStream_t stream) {

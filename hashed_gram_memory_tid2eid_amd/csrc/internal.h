@@ -88,6 +88,23 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_bf16_nt(const GemmArgs& a, hipStream_t stream);
 
+// Fused gather + dequant + projection for e4m3fn tables: C = A B^T where row t of
+// A is the dequantised concatenation of the rows that row_ids[t] names.
+struct GatherGemmArgs {
+  const uint8_t* table[3];
+  const float* scale[3];
+  int64_t rows[3];
+  const int32_t* row_ids;  // [M][cols]
+  int64_t pitch;           // bytes, >= seg_pitch, multiple of 16
+  int32_t row_dim, seg_pitch, cols, heads;
+  const void* B;           // bf16 [N][ldb], ldb >= cols * seg_pitch
+  int64_t ldb;
+  float* C;                // f32 [M][ldc]
+  int64_t ldc;
+  int32_t M, N;
+};
+hipError_t launch_gemm_gather_fp8(const GatherGemmArgs& a, hipStream_t stream);
+
 struct GateArgs {
   const float* v;         // [T][hidden]
   const uint8_t* keep;    // [T] or NULL

@@ -1,16 +1,19 @@
-"""One Engram site on one GPU: the three C-ABI calls chained over preallocated
+"""One Engram site on one GPU: the C-ABI calls chained over preallocated
 device buffers.
 
 ``Engram.forward`` = engram_compress_hash -> engram_gather_dequant ->
-engram_gated_residual on one stream, no host synchronisation, no allocation.
+engram_gated_residual on one stream, no host synchronisation, no allocation
+(path "split", the default).  Path "fused" (e4m3fn tables only) replaces the
+gather and the projection by engram_gather_project, which keeps the gathered
+rows on chip: no [T][k_pad] bf16 row buffer, at a lower projection rate.
 """
 from __future__ import annotations
 
 from typing import Optional, Sequence
 
 from . import (ENGRAM_DTYPE_BF16, ENGRAM_DTYPE_FP8_E4M3FN, Layout, engram_compress_hash,
-               engram_gather_dequant, engram_gated_residual, engram_layout_create,
-               engram_tid2eid_check)
+               engram_gate_add, engram_gather_dequant, engram_gather_project,
+               engram_gated_residual, engram_layout_create, engram_tid2eid_check)
 
 
 def pad_weight(w, layout: Layout):
@@ -38,8 +41,13 @@ class Engram:
                  heads_per_order: int, rows: Sequence[int], row_dim: int, table_dtype: str,
                  row_pitch_bytes: int, tid2eid, tables: Sequence, scales: Optional[Sequence],
                  weight, hidden: int, hc_mult: int = 4, max_tokens: int, hash_floor: int = 0,
-                 stream=None):
+                 path: str = "split", stream=None):
         import torch
+        if path not in ("split", "fused"):
+            raise ValueError(f"unknown path {path!r}")
+        if path == "fused" and table_dtype != "fp8":
+            raise ValueError("the fused path reads e4m3fn tables only")
+        self.path = path
         dt = ENGRAM_DTYPE_FP8_E4M3FN if table_dtype == "fp8" else ENGRAM_DTYPE_BF16
         self.layout = engram_layout_create(
             vocab_size=vocab_size, compressed_vocab=compressed_vocab, pad_token_id=pad_token_id,
@@ -57,7 +65,8 @@ class Engram:
         self.max_tokens = max_tokens
         self.eids = torch.empty(max_tokens, dtype=torch.int32, device=dev)
         self.row_ids = torch.empty((max_tokens, 3, info.heads), dtype=torch.int32, device=dev)
-        self.rows = torch.empty((max_tokens, info.k_pad), dtype=torch.bfloat16, device=dev)
+        self.rows = (torch.empty((max_tokens, info.k_pad), dtype=torch.bfloat16, device=dev)
+                     if path == "split" else None)
         self.v = torch.empty((max_tokens, hidden), dtype=torch.float32, device=dev)
 
     @property
@@ -79,6 +88,11 @@ class Engram:
         engram_compress_hash(self.layout, self.tid2eid, tokens, cu_seqlens, self.eids,
                              self.row_ids, seq_start=seq_start, slots=slots, store=store,
                              dead=dead, stream=stream)
+        if self.path == "fused":
+            engram_gather_project(self.layout, self.tables, self.scales, self.row_ids, self.weight,
+                                  self.v, T=T, stream=stream)
+            engram_gate_add(self.layout, self.v, streams, keep=keep, T=T, stream=stream)
+            return streams
         engram_gather_dequant(self.layout, self.tables, self.scales, self.row_ids, self.rows,
                               T=T, stream=stream)
         engram_gated_residual(self.layout, self.rows, self.weight, streams, self.v, keep=keep,

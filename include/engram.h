@@ -10,6 +10,8 @@
  *   3. engram_gated_residual  rows -> wkv down-projection (MFMA) -> per-stream
  *                             sigmoid gate -> residual add into the hc streams.
  *                             engram_project + engram_gate_add are its two halves.
+ *   engram_gather_project     steps 2 and the projection in one kernel for
+ *                             e4m3fn tables (rows stay on chip).
  *
  * Pages defining the operations (titles; sections named):
  *  [VeOmni#1370] GitHub PR "feat: support DeepSeek-V4.1-Flash in SeedOmni"
@@ -219,6 +221,24 @@ int engram_gather_dequant(const engram_layout* layout, const void* const* d_tabl
 int engram_project(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
                    const void* d_w, int64_t w_ld, int32_t hidden, float* d_v, int32_t T,
                    hipStream_t stream);
+
+/* Steps 2 and the projection half of step 3 in one kernel, for e4m3fn tables:
+ *   v[t][o] = sum_{k < k_pad} rows[t][k] * W[o][k]
+ * with rows[t] exactly the bf16 rows engram_gather_dequant would write (row-wise
+ * dequant on lookup, [VeOmni#1370] PR summary; wkv projection, [VeOmni#1370]
+ * config commit), built tile by tile in on-chip memory and never stored.
+ * Same accumulation order as engram_project, so v matches the two-call path bit
+ * for bit.
+ *   d_tables, d_scales, d_row_ids as for engram_gather_dequant; the layout's
+ *   row_pitch_bytes must be >= seg_pitch and a multiple of 16 (a row is read in
+ *   64-byte pieces up to seg_pitch; bytes past D are ignored).
+ *   d_w, w_ld, hidden, d_v as for engram_project.
+ * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN, ENGRAM_E_UNSUPPORTED (bf16
+ * tables).  Device error: ENGRAM_E_ROW_RANGE (that segment contributes zero). */
+int engram_gather_project(const engram_layout* layout, const void* const* d_tables,
+                          const float* const* d_scales, const int32_t* d_row_ids, int32_t T,
+                          const void* d_w, int64_t w_ld, int32_t hidden, float* d_v,
+                          hipStream_t stream);
 
 /* For each token t and stream s < hc_mult:
  *   z = <x[t][s][:], v[t][:]> / sqrt(hidden),  g = keep_t * sigmoid(z),

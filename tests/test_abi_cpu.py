@@ -139,3 +139,34 @@ def test_gather_host_argument_errors_need_no_device():
     # empty calls are no-ops
     assert lib.engram_compress_hash(L.handle, P(16), None, 0, None, 0, None, None, None, 0, None,
                                     None, None, None) == 0
+
+
+def test_gather_project_host_errors_need_no_device():
+    """The fused gather+projection refuses what it cannot read, before any launch."""
+    cfg = ei.get_config("tiny")
+    lib = eng._lib
+    P = ctypes.c_void_p
+    some = (P * 3)(P(256), P(256), P(256))
+    # bf16 tables: the fused kernel dequantises e4m3fn only
+    L16 = _layout(cfg, table_dtype=eng.ENGRAM_DTYPE_BF16, row_pitch_bytes=2 * cfg.row_dim)
+    rc = lib.engram_gather_project(L16.handle, some, some, P(256), 4, P(256), L16.info.k_pad,
+                                   cfg.hidden, P(256), None)
+    assert rc == eng.ENGRAM_E_UNSUPPORTED
+    # a row pitch shorter than the 64-aligned segment would read past the row
+    Lshort = _layout(cfg, row_dim=100, row_pitch_bytes=112)
+    assert Lshort.info.seg_pitch == 128
+    rc = lib.engram_gather_project(Lshort.handle, some, some, P(256), 4, P(256), Lshort.info.k_pad,
+                                   cfg.hidden, P(256), None)
+    assert rc == eng.ENGRAM_E_ALIGN
+    L = _layout(cfg)
+    # weight leading dimension below k_pad
+    rc = lib.engram_gather_project(L.handle, some, some, P(256), 4, P(256), L.info.k_pad - 8,
+                                   cfg.hidden, P(256), None)
+    assert rc == eng.ENGRAM_E_ALIGN
+    # missing scales
+    rc = lib.engram_gather_project(L.handle, some, None, P(256), 4, P(256), L.info.k_pad,
+                                   cfg.hidden, P(256), None)
+    assert rc == eng.ENGRAM_E_ARG
+    # empty call is a no-op
+    assert lib.engram_gather_project(L.handle, some, some, None, 0, None, L.info.k_pad,
+                                     cfg.hidden, None, None) == 0

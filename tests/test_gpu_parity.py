@@ -341,6 +341,16 @@ def _large_run(eng, name, f32_sample, stream_sample, tables=None):
     worst = assert_streams_close(bf16_bits_np(streams[torch.from_numpy(idx).to(DEV)]), y_ref,
                                  f"{name} streams")
     log(f"{name}: streams within tolerance on {len(idx)} sampled tokens (worst {worst:.2e})")
+    if cfg.table_dtype == "fp8":
+        # the fused gather + projection at the same size: v equal bit for bit on every token
+        v_f = torch.empty((T, cfg.hidden), dtype=torch.float32, device=DEV)
+        eng.engram_gather_project(site.site.layout, site.tables.data, site.tables.scale,
+                                  site.site.row_ids, site.site.weight, v_f, T=T)
+        torch.cuda.synchronize()
+        _no_device_error(eng, f"{name} fused")
+        assert torch.equal(v_f.view(torch.int32), site.site.v[:T].view(torch.int32))
+        log(f"{name}: fused gather+projection equals the split path on all {T} tokens")
+        del v_f
     return site
 
 
