@@ -14,7 +14,7 @@ Prints one JSON line: tokens/s, the roofline of the gather kernel (HBM bytes
 the method must move / measured average launch time, against 8 TB/s), the
 per-kernel breakdown, and the oracle's single-core throughput on a bounded
 token sample.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-[--config full|full_bf16|long|prefill|decode|tiny] [--path split|fused] [--no-cpu-baseline]
+[--config full|full_bf16|long|prefill|decode|tiny] [--path split|fused] [--graph] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--config", default="full", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--path", default="split", choices=["split", "fused"],
                     help="split: gather_dequant + project (default, faster); fused: gather_project")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step in a HIP graph and time K replays; value = graph rate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -302,6 +304,33 @@ def main():
         "wall_s_timed": wall,
         "setup_s": setup_s,
     }
+    if args.graph:
+        # the same step captured once and replayed K times (launch overhead removed);
+        # the decode step is launch-bound, so this is its production form
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record()
+        for _ in range(args.steps):
+            g.replay()
+        ge.record()
+        torch.cuda.synchronize()
+        eng.check_device_error("graph replays")
+        g_ms = gs.elapsed_time(ge) / args.steps
+        result["eager"] = {"value": result["value"], "ms_per_step": result["ms_per_step"]}
+        result["graph"] = {"value": T / (g_ms * 1e-3), "ms_per_step": g_ms}
+        result["value"] = T / (g_ms * 1e-3)
+        result["ms_per_step"] = g_ms
+        result["config"]["hip_graph"] = True
+        del g
     if args.path == "split" and cfg.table_dtype == "fp8":
         # the other path on the same inputs, outside the timed region: the fused
         # gather + projection against gather_dequant + project

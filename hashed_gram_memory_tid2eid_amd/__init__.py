@@ -104,6 +104,7 @@ _sig("engram_tid2eid_check", [_P, _P, ctypes.POINTER(_i32), _P])
 _sig("engram_store_reset", [_P, _P, _i32, _P, _i32, _i32, _P])
 _sig("engram_store_write", [_P, _P, _i32, _P, _i32, _P, _P])
 _sig("engram_store_read", [_P, _P, _i32, _P, _i32, _P, _P])
+_sig("engram_store_rollback", [_P, _P, _P, _i32, _P, _i32, _P, _i32, _P, _P, _P, _P, _P, _P])
 _sig("engram_compress_hash", [_P, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _P, _P, _P, _P])
 _sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _P])
 _sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
@@ -262,6 +263,30 @@ def engram_store_read(layout: Layout, store, slots, ids, stream=None):
 # ---------------------------------------------------------------------------
 # the three hot calls
 # ---------------------------------------------------------------------------
+
+def engram_store_rollback(layout: Layout, tid2eid, store, slots, cu_seqlens, eids, keep_len, *,
+                          snapshot=None, seq_start=None, dead=None, stream=None):
+    """Roll the slots of a verify call back to the first keep_len[s] tokens of
+    each sequence (see include/engram.h)."""
+    import torch
+    S = slots.numel()
+    T = eids.numel()
+    _need(cu_seqlens.numel() == S + 1 and keep_len.numel() == S, "cu_seqlens / keep_len size")
+    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
+    if snapshot is not None:
+        _need(snapshot.numel() >= 3 * S, "snapshot must be [S][3]")
+    if seq_start is not None:
+        _need(seq_start.numel() == S, "seq_start must be [S]")
+    if dead is not None:
+        _need(dead.numel() >= T, "dead must cover the call's tokens")
+    _check(_lib.engram_store_rollback(
+        layout.handle, _dev(tid2eid, torch.int32, "tid2eid"), _dev(store, torch.int32, "store"),
+        store.shape[0], _dev(slots, torch.int32, "slots"), S, _dev(cu_seqlens, torch.int32, "cu_seqlens"),
+        T, _dev(eids, torch.int32, "eids"), None if dead is None else _dev(dead, torch.uint8, "dead"),
+        None if seq_start is None else _dev(seq_start, torch.uint8, "seq_start"),
+        None if snapshot is None else _dev(snapshot, torch.int32, "snapshot"),
+        _dev(keep_len, torch.int32, "keep_len"), _stream(stream)), "engram_store_rollback")
+
 
 def engram_compress_hash(layout: Layout, tid2eid, tokens, cu_seqlens, eids, row_ids, *,
                          seq_start=None, slots=None, store=None, dead=None, stream=None):

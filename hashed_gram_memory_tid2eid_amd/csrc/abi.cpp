@@ -86,6 +86,35 @@ extern "C" int engram_store_read(const engram_layout* L, const int32_t* d_store,
                   engram::STORE_READ, stream);
 }
 
+extern "C" int engram_store_rollback(const engram_layout* L, const int32_t* d_tid2eid,
+                                    int32_t* d_store, int32_t num_slots, const int32_t* d_slots,
+                                    int32_t S, const int32_t* d_cu_seqlens, int32_t T,
+                                    const int32_t* d_eids, const uint8_t* d_dead,
+                                    const uint8_t* d_seq_start, const int32_t* d_snapshot,
+                                    const int32_t* d_keep_len, hipStream_t stream) {
+  if (!L || S < 0 || T < 0) return ENGRAM_E_ARG;
+  if (S == 0) return ENGRAM_OK;
+  if (!d_tid2eid || !d_store || num_slots < 1 || !d_slots || !d_cu_seqlens || !d_keep_len)
+    return ENGRAM_E_ARG;
+  if (T > 0 && !d_eids) return ENGRAM_E_ARG;
+  if (d_seq_start && !d_snapshot) return ENGRAM_E_ARG;  // continuing sequences need their tails
+  engram::RollbackArgs a;
+  a.store = d_store;
+  a.num_slots = num_slots;
+  a.slots = d_slots;
+  a.S = S;
+  a.T = T;
+  a.cu_seqlens = d_cu_seqlens;
+  a.eids = d_eids;
+  a.dead = d_dead;
+  a.seq_start = d_seq_start;
+  a.snapshot = d_snapshot;
+  a.keep_len = d_keep_len;
+  a.tid2eid = d_tid2eid;
+  a.pad_token_id = (int32_t)L->desc.pad_token_id;
+  return hip_status(engram::launch_store_rollback(a, stream));
+}
+
 // ---- 1. compress + hash -------------------------------------------------------
 
 extern "C" int engram_compress_hash(const engram_layout* L, const int32_t* d_tid2eid,

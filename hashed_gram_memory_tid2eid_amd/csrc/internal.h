@@ -53,6 +53,22 @@ struct MapCheckArgs {
 };
 hipError_t launch_map_check(const MapCheckArgs& a, hipStream_t stream);
 
+struct RollbackArgs {
+  int32_t* store;
+  int32_t num_slots;
+  const int32_t* slots;       // [S]
+  int32_t S, T;
+  const int32_t* cu_seqlens;  // [S+1] of the call being rolled back
+  const int32_t* eids;        // [T] of that call
+  const uint8_t* dead;        // [T] or NULL
+  const uint8_t* seq_start;   // [S] or NULL (= every sequence started in that call)
+  const int32_t* snapshot;    // [S][3] tails before that call
+  const int32_t* keep_len;    // [S]
+  const int32_t* tid2eid;
+  int32_t pad_token_id;
+};
+hipError_t launch_store_rollback(const RollbackArgs& a, hipStream_t stream);
+
 enum StoreOp { STORE_RESET = 0, STORE_WRITE = 1, STORE_READ = 2 };
 struct StoreArgs {
   int32_t* store;

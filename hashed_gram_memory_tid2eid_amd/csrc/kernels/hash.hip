@@ -131,6 +131,39 @@ __global__ __launch_bounds__(256) void compress_hash_kernel(HashArgs a) {
   }
 }
 
+// The three window ids that follow position `last` of a sequence whose
+// positions in this call start at b0, oldest first in out[0..2]: walking back
+// from `last`, a dead position reads PAD and blocks everything before it; the
+// walk continues into the ids before the call (prev, oldest first) unless the
+// sequence starts in this call, which blocks.  last < b0 means no position of
+// the call is kept: the ids before the call (or PAD) stand.
+__device__ __forceinline__ void tail_after(const int32_t* eids, const uint8_t* dead, int b0, int last,
+                                           bool starts, const int32_t* prev, int32_t pad,
+                                           int32_t out[3]) {
+  int32_t w[3];
+  bool blocked = false;
+  for (int j = 0; j <= 2; ++j) {
+    const int q = last - j;
+    int32_t val = pad;
+    if (!blocked) {
+      if (q >= b0) {
+        if (dead != nullptr && dead[q] != 0)
+          blocked = true;
+        else
+          val = eids[q];
+      } else if (starts) {
+        blocked = true;
+      } else {
+        val = prev[3 - (b0 - q)];
+      }
+    }
+    w[j] = blocked ? pad : val;
+  }
+  out[0] = w[2];
+  out[1] = w[1];
+  out[2] = w[0];
+}
+
 // One thread per sequence: the slot keeps the last three window ids of its
 // sequence, oldest first.  Runs after compress_hash_kernel on the same stream,
 // so every read of the old slot content has happened.
@@ -148,34 +181,49 @@ __global__ __launch_bounds__(256) void store_update_kernel(HashArgs a) {
   const int32_t pad = a.tid2eid[a.pad_token_id];
   const bool starts = a.seq_start == nullptr || a.seq_start[s] != 0;
   int32_t* st = a.store + 3 * slot;
-  if (b1 == b0) {
-    if (starts) st[0] = st[1] = st[2] = pad;
+  int32_t w[3];
+  tail_after(a.eids, a.dead, b0, b1 - 1, starts, st, pad, w);
+  st[0] = w[0];
+  st[1] = w[1];
+  st[2] = w[2];
+}
+
+// Speculative rollback: each slot is set to the tail it would hold had the last
+// call covered only the first keep_len[s] tokens of sequence s.  The tail
+// before that call is the caller's snapshot (read with engram_store_read before
+// the call); the call's compressed ids and dead mask supply the rest.  A tail is
+// three ids, so the snapshot is the state itself and the replay touches at most
+// the last three kept positions.
+__global__ __launch_bounds__(256) void store_rollback_kernel(RollbackArgs a) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= a.S) return;
+  const int slot = a.slots[s];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    latch_error(ENGRAM_E_SLOT_RANGE);
     return;
   }
-  const int last = b1 - 1;
-  int32_t w[3];
-  bool blocked = a.dead != nullptr && a.dead[last] != 0;
-  w[0] = blocked ? pad : a.eids[last];
-  for (int j = 1; j <= 2; ++j) {
-    const int q = last - j;
-    int32_t val = pad;
-    if (!blocked) {
-      if (q >= b0) {
-        if (a.dead != nullptr && a.dead[q] != 0)
-          blocked = true;
-        else
-          val = a.eids[q];
-      } else if (starts) {
-        blocked = true;
-      } else {
-        val = st[3 - (b0 - q)];
-      }
-    }
-    w[j] = blocked ? pad : val;
+  const int b0 = a.cu_seqlens[s], b1 = a.cu_seqlens[s + 1];
+  const int keep = a.keep_len[s];
+  if (b0 < 0 || b1 > a.T || b1 < b0 || keep < 0 || keep > b1 - b0) {
+    latch_error(ENGRAM_E_SEQLENS);
+    return;
   }
-  st[0] = w[2];
+  const int32_t pad = a.tid2eid[a.pad_token_id];
+  const bool starts = a.seq_start == nullptr || a.seq_start[s] != 0;
+  int32_t w[3];
+  tail_after(a.eids, a.dead, b0, b0 + keep - 1, starts, a.snapshot + 3 * (int64_t)s, pad, w);
+  int32_t* st = a.store + 3 * (int64_t)slot;
+  st[0] = w[0];
   st[1] = w[1];
-  st[2] = w[0];
+  st[2] = w[2];
+}
+
+hipError_t launch_store_rollback(const RollbackArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale error another library left on this thread
+  if (a.S == 0) return hipSuccess;
+  hipLaunchKernelGGL(store_rollback_kernel, dim3((a.S + 255) / 256), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream) {

@@ -149,6 +149,29 @@ int engram_store_write(const engram_layout* layout, int32_t* d_store, int32_t nu
 int engram_store_read(const engram_layout* layout, const int32_t* d_store, int32_t num_slots,
                       const int32_t* d_slots, int32_t n, int32_t* d_ids, hipStream_t stream);
 
+/* Speculative rollback.  After an engram_compress_hash call that updated the
+ * store for S sequences (a verify pass over draft tokens), sets each slot
+ * d_slots[s] >= 0 to the tail it would hold had that call covered only the
+ * first d_keep_len[s] tokens of sequence s (0 <= keep_len <= its length).
+ * Snapshot = the slots' tails read with engram_store_read (same d_slots order)
+ * before the call; only continuing sequences (d_seq_start[s] == 0) read it.
+ * The other arguments are the call's own: d_cu_seqlens [S+1], T, d_eids [T]
+ * (as the call wrote them), d_dead [T] or NULL, d_seq_start [S] or NULL (= all
+ * started in the call; then d_snapshot may be NULL).
+ * ([VeOmni#1370] n-gram incremental decode cache commit: the cache is a
+ * fixed-width tail of the last three ids; review of the decode-cache
+ * snapshot: state that only grows is rolled back by length, bounded state is
+ * copied.  The tail is bounded, so its snapshot is the 3-id copy and rolling
+ * back to a length replays at most the last three kept ids onto it.)
+ * Host errors: ENGRAM_E_ARG.  Device errors: ENGRAM_E_SLOT_RANGE,
+ * ENGRAM_E_SEQLENS (keep_len outside [0, length] or malformed cu_seqlens; that
+ * slot is left unchanged). */
+int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid, int32_t* d_store,
+                          int32_t num_slots, const int32_t* d_slots, int32_t S,
+                          const int32_t* d_cu_seqlens, int32_t T, const int32_t* d_eids,
+                          const uint8_t* d_dead, const uint8_t* d_seq_start,
+                          const int32_t* d_snapshot, const int32_t* d_keep_len, hipStream_t stream);
+
 /* ---- 1. compress + hash -------------------------------------------------- */
 /* For each token t of each sequence s (tokens cu_seqlens[s] .. cu_seqlens[s+1]-1):
  *   e_t   = dead_t ? PAD : tid2eid[token_t],  PAD = tid2eid[pad_token_id]

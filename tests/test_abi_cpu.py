@@ -170,3 +170,24 @@ def test_gather_project_host_errors_need_no_device():
     # empty call is a no-op
     assert lib.engram_gather_project(L.handle, some, some, None, 0, None, L.info.k_pad,
                                      cfg.hidden, None, None) == 0
+
+
+def test_store_rollback_host_errors_need_no_device():
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg)
+    lib = eng._lib
+    P = ctypes.c_void_p
+    # empty call is a no-op
+    assert lib.engram_store_rollback(L.handle, None, None, 0, None, 0, None, 0, None, None, None,
+                                     None, None, None) == 0
+    # missing store / slots / keep_len
+    rc = lib.engram_store_rollback(L.handle, P(256), None, 4, P(256), 2, P(256), 4, P(256), None, None,
+                                   None, P(256), None)
+    assert rc == eng.ENGRAM_E_ARG
+    rc = lib.engram_store_rollback(L.handle, P(256), P(256), 4, P(256), 2, P(256), 4, P(256), None, None,
+                                   None, None, None)
+    assert rc == eng.ENGRAM_E_ARG
+    # continuing sequences (seq_start given) need the snapshot
+    rc = lib.engram_store_rollback(L.handle, P(256), P(256), 4, P(256), 2, P(256), 4, P(256), None,
+                                   P(256), None, P(256), None)
+    assert rc == eng.ENGRAM_E_ARG
