@@ -14,7 +14,7 @@ Prints one JSON line: tokens/s, the roofline of the gather kernel (HBM bytes
 the method must move / measured average launch time, against 8 TB/s), the
 per-kernel breakdown, and the oracle's single-core throughput on a bounded
 token sample.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-[--config full|full_bf16|long|prefill|decode|tiny] [--path split|fused] [--graph] [--no-cpu-baseline]
+[--config full|full_bf16|long|prefill|decode|tiny|v41|v41_small] [--path split|fused] [--graph] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -44,6 +44,11 @@ WORKLOAD_TEXT = {
                "2 heads per order; wkv 3,072->4,096; hc 4",
     "decode": "decode step: 256 slots x 1 token, rolling store; prefill's tables and wkv",
     "tiny": "tiny: 512 uniform tokens; 3 x 4,096 rows of 128 e4m3fn; 2 heads; wkv 768->256; hc 4",
+    "v41": "released layout: 8 x 8,192 Zipf(1.1) tokens; 2 Engram sites sharing one hash pass; "
+           "3 orders x 8 heads; one table per site of 384,006,168 / 384,016,682 rows of 256 e4m3fn "
+           "with (1,32) e8m0 scales (2 x 98.3 GB); wkv 6,144->4,096 per site; hc 4",
+    "v41_small": "released layout structure at bucket floor 20,000: 4 x 2,048 Zipf(1.1) tokens; "
+                 "2 sites; 3 x 8 heads; D 256; (1,32) e8m0 scales; wkv 6,144->1,024; hc 4",
 }
 
 
@@ -51,11 +56,11 @@ def algorithmic_per_token(cfg):
     """Bytes (or flops) each kernel must move per token, counting rows touched."""
     H, D, hidden = cfg.heads, cfg.row_dim, cfg.hidden
     K = 3 * H * D
-    scale = 4 if cfg.table_dtype == "fp8" else 0
+    scale = 0 if cfg.table_dtype != "fp8" else (D // 32 if cfg.scale_block else 4)
     return {
-        # token id, tid2eid entry, compressed id out, 3H row ids out
-        "hash_bytes": 4 + 4 + 4 + 4 * 3 * H,
-        # 3H rows of D elements + their scale in; K bf16 out
+        # token id, tid2eid entry, compressed id out, 3H row ids per site out
+        "hash_bytes": 4 + 4 + 4 + 4 * 3 * H * cfg.n_sites,
+        # per site: 3H rows of D elements + their scales in; K bf16 out
         "gather_bytes": 3 * H * (D * cfg.elt_bytes + scale) + 2 * K,
         "project_flops": 2 * K * hidden,
         # 4 bf16 streams read and written, v (fp32) read
@@ -86,7 +91,7 @@ def measured_traffic(cfg):
     return float(kv["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, batch, tables, weight, streams_host_bits, budget_s: float):
+def cpu_baseline(cfg, batch, site_tables, weights, streams_host_bits, budget_s: float):
     """The oracle as it stands, single-threaded on a host core, on a bounded token
     sample of the same workload (rows read from the device tables by torch)."""
     import numpy as np
@@ -96,39 +101,62 @@ def cpu_baseline(cfg, batch, tables, weight, streams_host_bits, budget_s: float)
     import oracle
 
     tid2eid = ei.make_tid2eid(cfg.vocab, cfg.vc)
-    L = oracle.fit_layout([cfg.rows] * 3, cfg.heads)
+    per_site = cfg.table_split == "site"
+    if cfg.n_sites > 1 or per_site:
+        layouts = oracle.site_layouts(cfg.n_sites, cfg.heads, cfg.hash_floor, per_site)
+    elif cfg.hash_floor:
+        layouts = [oracle.layout_at_floor([cfg.rows] * 3, cfg.heads, cfg.hash_floor)]
+    else:
+        layouts = [oracle.fit_layout([cfg.rows] * 3, cfg.heads)]
     store = ei.make_store_init(cfg) if batch.slots is not None else None
     t0 = time.perf_counter()
-    _, rows = oracle.compress_hash(L, vocab=cfg.vocab, vc=cfg.vc, pad_token_id=cfg.pad_token_id,
-                                   tid2eid=tid2eid, tokens=batch.tokens, cu_seqlens=batch.cu_seqlens,
-                                   seq_start=batch.seq_start, slots=batch.slots, store=store)
+    site_rows = []
+    for si, L in enumerate(layouts):
+        st = store if si == 0 or store is None else store.copy()
+        _, rows = oracle.compress_hash(L, vocab=cfg.vocab, vc=cfg.vc, pad_token_id=cfg.pad_token_id,
+                                       tid2eid=tid2eid, tokens=batch.tokens,
+                                       cu_seqlens=batch.cu_seqlens, seq_start=batch.seq_start,
+                                       slots=batch.slots, store=st)
+        site_rows.append(rows)
     t_hash_all = time.perf_counter() - t0
-    W = weight.view(torch.int16).cpu().numpy().view(np.uint16)
+    Ws = [w.view(torch.int16).cpu().numpy().view(np.uint16) for w in weights]
     rng = np.random.default_rng(1234)
     order = rng.permutation(batch.T)
     H, D = cfg.heads, cfg.row_dim
+    bf16 = cfg.table_dtype == "bf16"
     done, t_rest = 0, 0.0
     chunk = 4
     while done < batch.T and t_rest + t_hash_all * done / batch.T < budget_s:
         idx = np.sort(order[done:done + chunk])
-        raw = np.zeros((len(idx), 3 * H, D), np.uint16 if cfg.table_dtype == "bf16" else np.uint8)
-        sc = None if cfg.table_dtype == "bf16" else np.zeros((len(idx), 3 * H), np.float32)
-        for o in range(3):
-            view = tables.row_view(o)
-            for h in range(H):
-                ii = torch.from_numpy(rows[idx, o, h].astype(np.int64)).to(view.device)
-                r = view.index_select(0, ii)
-                raw[:, o * H + h] = (r.view(torch.int16).cpu().numpy().view(np.uint16)
-                                     if cfg.table_dtype == "bf16" else r.cpu().numpy())
-                if sc is not None:
-                    sc[:, o * H + h] = tables.scale[o].index_select(0, ii).cpu().numpy()
-        x = streams_host_bits[idx]
-        t1 = time.perf_counter()
-        _, e16 = oracle.dequant_rows(raw.reshape(-1, D), None if sc is None else sc.reshape(-1),
-                                     bf16_table=cfg.table_dtype == "bf16")
-        v = oracle.project(e16.reshape(len(idx), -1), W)
-        oracle.gate_add(x, v)
-        t_rest += time.perf_counter() - t1
+        for si in range(cfg.n_sites):
+            tabs = site_tables[si]
+            raw = np.zeros((len(idx), 3 * H, D), np.uint16 if bf16 else np.uint8)
+            if bf16:
+                sc = None
+            elif cfg.scale_block:
+                sc = np.zeros((len(idx), 3 * H, D // 32), np.uint8)
+            else:
+                sc = np.zeros((len(idx), 3 * H), np.float32)
+            for o in range(3):
+                n = 0 if per_site else o
+                view = tabs.row_view(n)
+                for h in range(H):
+                    ii = torch.from_numpy(site_rows[si][idx, o, h].astype(np.int64)).to(view.device)
+                    r = view.index_select(0, ii)
+                    raw[:, o * H + h] = (r.view(torch.int16).cpu().numpy().view(np.uint16) if bf16
+                                         else r.cpu().numpy())
+                    if sc is not None:
+                        sc[:, o * H + h] = tabs.scale[n].index_select(0, ii).cpu().numpy()
+            x = streams_host_bits[si][idx]
+            t1 = time.perf_counter()
+            if cfg.scale_block:
+                _, e16 = oracle.dequant_rows_block32(raw.reshape(-1, D), sc.reshape(-1, D // 32))
+            else:
+                _, e16 = oracle.dequant_rows(raw.reshape(-1, D), None if sc is None else sc.reshape(-1),
+                                             bf16_table=bf16)
+            v = oracle.project(e16.reshape(len(idx), -1), Ws[si])
+            oracle.gate_add(x, v)
+            t_rest += time.perf_counter() - t1
         done += len(idx)
     total = t_rest + t_hash_all * done / batch.T
     return {
@@ -136,9 +164,9 @@ def cpu_baseline(cfg, batch, tables, weight, streams_host_bits, budget_s: float)
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{done} of {batch.T} tokens of the same batch (seeded), full path per token: "
-                   f"compress+hash (whole batch {t_hash_all:.3f}s, charged pro rata), dequant, "
-                   f"fp64 projection, gate; {total:.1f}s of single-thread C on "
+        "sample": (f"{done} of {batch.T} tokens of the same batch (seeded), full path per token "
+                   f"and site ({cfg.n_sites}): compress+hash (whole batch {t_hash_all:.3f}s, charged "
+                   f"pro rata), dequant, fp64 projection, gate; {total:.1f}s of single-thread C on "
                    f"{platform.processor() or platform.machine()}, {os.cpu_count()} host threads visible"),
     }
 
@@ -183,17 +211,24 @@ def main():
     else:
         batch = ei.make_batch(cfg)
     T = batch.T
-    tables = ei.make_tables(cfg, dev)
-    weight = ei.make_weight(cfg, dev)
+    NS = cfg.n_sites
+    site_tables = [ei.make_tables(cfg, dev, site=s) for s in range(NS)]
+    weights = [ei.make_weight(cfg, dev, site=s) for s in range(NS)]
+    one = NS == 1
     site = eng.Engram(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
-                      heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
-                      table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes,
-                      tid2eid=tid2eid, tables=tables.data, scales=tables.scale, weight=weight,
-                      hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=T, path=args.path)
-    streams = ei.make_streams(cfg, T, dev)
+                      heads_per_order=cfg.heads,
+                      rows=[cfg.rows] if cfg.table_split == "site" else [cfg.rows] * 3,
+                      row_dim=cfg.row_dim, table_dtype=cfg.table_dtype,
+                      row_pitch_bytes=cfg.row_pitch_bytes, tid2eid=tid2eid,
+                      tables=site_tables[0].data if one else [t.data for t in site_tables],
+                      scales=site_tables[0].scale if one else [t.scale for t in site_tables],
+                      weight=weights[0] if one else weights, hidden=cfg.hidden, hc_mult=cfg.hc_mult,
+                      max_tokens=T, path=args.path, num_sites=NS, table_split=cfg.table_split,
+                      scale_block=cfg.scale_block, hash_floor=cfg.hash_floor)
+    site_streams = [ei.make_streams(cfg, T, dev, step=s) for s in range(NS)]
     streams_host = None
     if not args.no_cpu_baseline:
-        streams_host = streams.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+        streams_host = [x.view(torch.int16).cpu().numpy().view(np.uint16).copy() for x in site_streams]
 
     def d(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -205,35 +240,44 @@ def main():
     setup_s = time.perf_counter() - t_setup
     print(f"# setup {setup_s:.1f}s: {cfg.name}, T={T}, k_pad={site.info.k_pad}", file=sys.stderr, flush=True)
 
+    # kernel sequence of one step: the hash, then per site gather (+) project, gate
+    if args.path == "fused":
+        seq = ["compress_hash"] + ["gather_project", "gate_add"] * NS
+    else:
+        seq = ["compress_hash"] + ["gather_dequant", "project", "gate_add"] * NS
+
     def step(ev=None):
-        if ev:
-            ev[0].record()
+        k = 0
+
+        def mark():
+            nonlocal k
+            if ev:
+                ev[k].record()
+            k += 1
+        mark()
         eng.engram_compress_hash(L, tid2eid, tok, cu, site.eids, site.row_ids, seq_start=ss,
                                  slots=sl, store=store)
-        if ev:
-            ev[1].record()
-        if args.path == "fused":
-            eng.engram_gather_project(L, site.tables, site.scales, site.row_ids, site.weight, site.v, T=T)
-            if ev:
-                ev[2].record()
-                ev[3].record()
-        else:
-            eng.engram_gather_dequant(L, site.tables, site.scales, site.row_ids, site.rows, T=T)
-            if ev:
-                ev[2].record()
-            eng.engram_project(L, site.rows, site.weight, site.v, T=T)
-            if ev:
-                ev[3].record()
-        eng.engram_gate_add(L, site.v, streams, T=T)
-        if ev:
-            ev[4].record()
+        mark()
+        for si in range(NS):
+            if args.path == "fused":
+                eng.engram_gather_project(L, site.site_tables[si], site.site_scales[si], site.row_ids,
+                                          site.site_weights[si], site.v, site=si, T=T)
+                mark()
+            else:
+                eng.engram_gather_dequant(L, site.site_tables[si], site.site_scales[si], site.row_ids,
+                                          site.rows, site=si, T=T)
+                mark()
+                eng.engram_project(L, site.rows, site.site_weights[si], site.v, T=T)
+                mark()
+            eng.engram_gate_add(L, site.v, site_streams[si], T=T)
+            mark()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     eng.check_device_error("warmup")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -246,11 +290,11 @@ def main():
     eng.check_device_error("timed steps")
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    names = ["compress_hash", "gather_dequant", "project", "gate_add"]
-    if args.path == "fused":
-        names = ["compress_hash", "gather_project", None, "gate_add"]
-    kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
-               for j, n in enumerate(names) if n}
+    # average time per launch of each kernel (a step launches the per-site kernels NS times)
+    kern_ms = {}
+    for n in dict.fromkeys(seq):
+        js = [j for j, m in enumerate(seq) if m == n]
+        kern_ms[n] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs for j in js]))
 
     per = algorithmic_per_token(cfg)
     def gbs(b, ms):
@@ -259,7 +303,8 @@ def main():
     proj_flops = per["project_flops"] * T
     gate_gbs = gbs(per["gate_bytes"] * T, kern_ms["gate_add"])
     hash_gbs = gbs(per["hash_bytes"] * T, kern_ms["compress_hash"])
-    kernels = {"compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs}}
+    kernels = {"compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs,
+                                 "launches_per_step": 1}}
     if args.path == "fused":
         fused_tflops = proj_flops / (kern_ms["gather_project"] * 1e-3) / 1e12
         kernels["gather_project"] = {"ms": kern_ms["gather_project"], "bound": "mfma",
@@ -281,6 +326,8 @@ def main():
                     "avg_launch_ms": kern_ms["gather_dequant"]}
     kernels["gate_add"] = {"ms": kern_ms["gate_add"], "bound": "hbm", "GB/s": gate_gbs,
                            "frac": gate_gbs / HBM_PEAK_GBS}
+    for n in kernels:
+        kernels[n].setdefault("launches_per_step", NS)
 
     result = {
         "metric": METRIC,
@@ -298,7 +345,8 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[cfg.name], "name": cfg.name, "tokens_per_step": T,
                    "table_dtype": cfg.table_dtype, "rows_per_table": cfg.rows, "row_dim": cfg.row_dim,
                    "heads_per_order": cfg.heads, "hidden": cfg.hidden, "hc_mult": cfg.hc_mult,
-                   "k_pad": site.info.k_pad, "path": args.path},
+                   "k_pad": site.info.k_pad, "path": args.path, "sites": NS,
+                   "table_split": cfg.table_split, "scale_block": cfg.scale_block},
         "roofline": roofline,
         "kernels": kernels,
         "wall_s_timed": wall,
@@ -331,7 +379,7 @@ def main():
         result["ms_per_step"] = g_ms
         result["config"]["hip_graph"] = True
         del g
-    if args.path == "split" and cfg.table_dtype == "fp8":
+    if args.path == "split" and cfg.table_dtype == "fp8" and NS == 1 and not cfg.scale_block:
         # the other path on the same inputs, outside the timed region: the fused
         # gather + projection against gather_dequant + project
         v_alt = torch.empty_like(site.v)
@@ -365,7 +413,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, batch, tables, weight, streams_host, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(cfg, batch, site_tables, weights, streams_host,
+                                              args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

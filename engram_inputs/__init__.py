@@ -16,10 +16,18 @@ Workloads (tokens per call; tables per order; heads per order; row dim; hidden):
   full        8 x 8,192 Zipf(1.1); 3 x 5,040,000 (15.12M) rows; H=1; D=6,500
               FP8 e4m3fn plus an fp32 scale per row; hidden 4,096
   full_bf16   full with BF16 tables (no scale)
+  v41         the released layout: 2 Engram sites sharing one hash pass, 3 orders
+              x 8 heads, D=256, one table per site of 384,006,168 / 384,016,682
+              rows (bucket floor 16,000,000), (1, 32) e8m0 block scales;
+              8 x 8,192 Zipf(1.1) tokens; hidden 4,096
+  v41_small   the same structure at bucket floor 20,000 (~0.49M rows per site);
+              4 x 2,048 Zipf(1.1) tokens; hidden 1,024
 
 Table rows are N(0,1) per element, quantised per row to e4m3fn with a
 power-of-two fp32 scale 2^ceil(log2(amax/448)) ("amax" mode uses amax/448
-itself, a scale that is not a power of two).  W ~ N(0, 0.02) in bf16 with
+itself, a scale that is not a power of two); with (1, 32) block scales each
+32-element block gets its own exponent e = ceil(log2(amax_block/448)), stored
+as the e8m0 byte e + 127.  W ~ N(0, 0.02) in bf16 with
 logical shape [hidden][3*H*D].  Streams ~ N(0,1) in bf16, [T][hc][hidden].
 Token ids: uniform, or truncated Zipf over ranks 1..vocab with P(k) ~ k^-s,
 drawn by inverse CDF, token = rank - 1.  tid2eid is one random surjection of
@@ -59,6 +67,10 @@ class EngramConfig:
     pad_token_id: int = PAD_TOKEN_ID
     zipf_s: float = 1.1
     w_std: float = 0.02
+    n_sites: int = 1          # Engram sites sharing one hash pass
+    table_split: str = "order"  # "order": 3 tables per site; "site": 1 table per site
+    scale_block: int = 0      # 0: fp32 scale per row; 32: e8m0 exponent per 32 elements
+    hash_floor: int = 0       # 0: fit the largest floor the tables hold
 
     @property
     def tokens_per_call(self) -> int:
@@ -89,6 +101,10 @@ CONFIGS = {
     "full": EngramConfig("full", 4, 8, 8192, "zipf", 5_040_000, 1, 6500, 4096),
     "full_bf16": EngramConfig("full_bf16", 4, 8, 8192, "zipf", 5_040_000, 1, 6500, 4096,
                               table_dtype="bf16"),
+    "v41": EngramConfig("v41", 5, 8, 8192, "zipf", 384_016_682, 8, 256, 4096, n_sites=2,
+                        table_split="site", scale_block=32, hash_floor=16_000_000),
+    "v41_small": EngramConfig("v41_small", 6, 4, 2048, "zipf", 500_000, 8, 256, 1024, n_sites=2,
+                              table_split="site", scale_block=32, hash_floor=20_000),
 }
 
 
@@ -248,10 +264,12 @@ def make_dead_spans(T: int, seed: int, n_spans: int, max_len: int) -> np.ndarray
 
 @dataclass
 class Tables:
-    """Three per-order tables in storage layout.
+    """The tables of one site in storage layout: three per-order tables, or one
+    table for the site (table_split "site").
 
     fp8:  data[n] uint8 [rows][pitch] (first D bytes of a row are e4m3fn codes, the
-          rest zero), scale[n] float32 [rows].
+          rest zero), scale[n] float32 [rows], or uint8 [rows][D/32] e8m0 bytes
+          with (1, 32) block scales.
     bf16: data[n] uint8 [rows][pitch] holding D little-endian bf16 values, scale None.
     """
     data: list
@@ -270,25 +288,40 @@ class Tables:
 
 
 def make_tables(cfg: EngramConfig, device, scale_mode: str = "pow2",
-                rows_per_chunk: Optional[int] = None) -> Tables:
+                rows_per_chunk: Optional[int] = None, site: int = 0) -> Tables:
+    """The tables of one site (seeded per site and table)."""
     import torch
     D, R, pitch = cfg.row_dim, cfg.rows, cfg.row_pitch_bytes
     if rows_per_chunk is None:
         rows_per_chunk = max(1, min(R, (1 << 27) // max(D, 1)))
+    n_tables = 1 if cfg.table_split == "site" else 3
     gen = torch.Generator(device=device)
     data, scales = [], []
-    for n in range(3):
-        gen.manual_seed(_torch_seed(cfg.seed, _TABLES, n))
+    for n in range(n_tables):
+        gen.manual_seed(_torch_seed(cfg.seed, _TABLES, 3 * site + n))
         buf = torch.empty((R, pitch), dtype=torch.uint8, device=device)
         elt = cfg.elt_bytes
         if pitch > D * elt:
             buf[:, D * elt:].zero_()
-        sc = torch.empty(R, dtype=torch.float32, device=device) if cfg.table_dtype == "fp8" else None
+        sc = None
+        if cfg.table_dtype == "fp8":
+            sc = (torch.empty((R, D // 32), dtype=torch.uint8, device=device) if cfg.scale_block
+                  else torch.empty(R, dtype=torch.float32, device=device))
         for r0 in range(0, R, rows_per_chunk):
             r1 = min(R, r0 + rows_per_chunk)
             x = torch.randn((r1 - r0, D), generator=gen, device=device, dtype=torch.float32)
             if cfg.table_dtype == "bf16":
                 buf[r0:r1, : 2 * D].view(torch.bfloat16).copy_(x.to(torch.bfloat16))
+                continue
+            if cfg.scale_block:
+                xb = x.view(r1 - r0, D // 32, 32)
+                amax = xb.abs().amax(dim=2).clamp_min(1e-30)
+                e = torch.ceil(torch.log2(amax / E4M3_MAX))
+                e = torch.where(amax / torch.exp2(e) > E4M3_MAX, e + 1, e).clamp_(-127, 127)
+                q = (xb / torch.exp2(e)[:, :, None]).clamp_(-E4M3_MAX, E4M3_MAX)
+                buf[r0:r1, :D].copy_(q.reshape(r1 - r0, D).to(torch.float8_e4m3fn).view(torch.uint8))
+                sc[r0:r1] = (e + 127).to(torch.uint8)
+                del x, xb, q
                 continue
             amax = x.abs().amax(dim=1).clamp_min(1e-30)
             if scale_mode == "pow2":
@@ -308,11 +341,11 @@ def make_tables(cfg: EngramConfig, device, scale_mode: str = "pow2",
                   pitch=pitch, dtype=cfg.table_dtype)
 
 
-def make_weight(cfg: EngramConfig, device):
-    """Down-projection W, bf16 [hidden][K] (logical, unpadded), N(0, w_std)."""
+def make_weight(cfg: EngramConfig, device, site: int = 0):
+    """Down-projection W of one site, bf16 [hidden][K] (logical, unpadded), N(0, w_std)."""
     import torch
     gen = torch.Generator(device=device)
-    gen.manual_seed(_torch_seed(cfg.seed, _W))
+    gen.manual_seed(_torch_seed(cfg.seed, _W, site))
     w = torch.randn((cfg.hidden, cfg.K), generator=gen, device=device, dtype=torch.float32)
     return (w * cfg.w_std).to(torch.bfloat16)
 

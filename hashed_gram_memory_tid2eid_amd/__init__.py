@@ -22,6 +22,12 @@ ENGRAM_DTYPE_FP8_E4M3FN = 1
 ENGRAM_DTYPE_BF16 = 2
 ENGRAM_DTYPE_F32 = 3
 ENGRAM_MAX_HEADS = 8
+ENGRAM_MAX_SITES = 4
+ENGRAM_TABLES_PER_ORDER = 0
+ENGRAM_TABLE_PER_SITE = 1
+ENGRAM_SCALE_ROW_F32 = 0
+ENGRAM_SCALE_BLOCK32_E8M0 = 32
+_MAX_COLUMNS = ENGRAM_MAX_SITES * 3 * ENGRAM_MAX_HEADS
 
 
 def _status_codes():
@@ -79,14 +85,16 @@ class engram_layout_desc(ctypes.Structure):
         ("vocab_size", _i64), ("compressed_vocab", _i64), ("pad_token_id", _i64),
         ("max_ngram", _i32), ("heads_per_order", _i32), ("rows", _i64 * 3), ("hash_floor", _i64),
         ("row_dim", _i32), ("table_dtype", _i32), ("row_pitch_bytes", _i64),
+        ("num_sites", _i32), ("table_split", _i32), ("scale_layout", _i32), ("reserved", _i32),
     ]
 
 
 class engram_layout_info(ctypes.Structure):
     _fields_ = [
         ("hash_floor", _i64), ("heads_per_order", _i32), ("row_dim", _i32), ("rows", _i64 * 3),
-        ("primes", _i64 * (3 * ENGRAM_MAX_HEADS)), ("offsets", _i64 * (3 * ENGRAM_MAX_HEADS)),
-        ("prime_sum", _i64 * 3), ("seg_pitch", _i64), ("k_pad", _i64),
+        ("primes", _i64 * _MAX_COLUMNS), ("offsets", _i64 * _MAX_COLUMNS),
+        ("prime_sum", _i64 * (3 * ENGRAM_MAX_SITES)), ("seg_pitch", _i64), ("k_pad", _i64),
+        ("num_sites", _i32), ("table_split", _i32), ("scale_layout", _i32), ("reserved", _i32),
     ]
 
 
@@ -106,9 +114,9 @@ _sig("engram_store_write", [_P, _P, _i32, _P, _i32, _P, _P])
 _sig("engram_store_read", [_P, _P, _i32, _P, _i32, _P, _P])
 _sig("engram_store_rollback", [_P, _P, _P, _i32, _P, _i32, _P, _i32, _P, _P, _P, _P, _P, _P])
 _sig("engram_compress_hash", [_P, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _P, _P, _P, _P])
-_sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _P])
+_sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _i32, _P, _i64, _P])
 _sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
-_sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _P, _i64, _i32, _P, _P])
+_sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _i32, _P, _P])
 _sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
 _sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
@@ -167,11 +175,25 @@ class LayoutInfo:
     heads: int
     row_dim: int
     rows: tuple
-    primes: list      # [3][H]
-    offsets: list     # [3][H]
-    prime_sum: tuple
+    primes: list      # [3][H] of site 0
+    offsets: list     # [3][H] of site 0
+    prime_sum: tuple  # [3] of site 0
     seg_pitch: int
     k_pad: int
+    num_sites: int = 1
+    table_split: int = 0
+    scale_layout: int = 0
+    site_primes: list = None      # [site][3][H]
+    site_offsets: list = None     # [site][3][H]
+    site_prime_sum: list = None   # [site][3]
+
+    @property
+    def cols(self) -> int:
+        return 3 * self.heads
+
+    def site_rows(self, site: int) -> int:
+        """Buckets of one site: the rows its table (one per site) must hold."""
+        return int(sum(self.site_prime_sum[site]))
 
 
 class Layout:
@@ -195,13 +217,16 @@ class Layout:
 def engram_layout_create(*, vocab_size: int, compressed_vocab: int, pad_token_id: int,
                          heads_per_order: int, rows: Sequence[int], row_dim: int,
                          table_dtype: int, row_pitch_bytes: int, hash_floor: int = 0,
-                         max_ngram: int = 4) -> Layout:
+                         max_ngram: int = 4, num_sites: int = 1,
+                         table_split: int = ENGRAM_TABLES_PER_ORDER,
+                         scale_layout: int = ENGRAM_SCALE_ROW_F32) -> Layout:
     d = engram_layout_desc()
     d.vocab_size, d.compressed_vocab, d.pad_token_id = vocab_size, compressed_vocab, pad_token_id
     d.max_ngram, d.heads_per_order = max_ngram, heads_per_order
     for i in range(3):
         d.rows[i] = int(rows[i])
     d.hash_floor, d.row_dim, d.table_dtype, d.row_pitch_bytes = hash_floor, row_dim, table_dtype, row_pitch_bytes
+    d.num_sites, d.table_split, d.scale_layout = num_sites, table_split, scale_layout
     h = _P()
     _check(_lib.engram_layout_create(ctypes.byref(d), ctypes.byref(h)), "engram_layout_create")
     return Layout(h.value, d)
@@ -211,11 +236,15 @@ def engram_layout_query(layout: Layout) -> LayoutInfo:
     info = engram_layout_info()
     _check(_lib.engram_layout_query(layout.handle, ctypes.byref(info)), "engram_layout_query")
     H = info.heads_per_order
+    S = info.num_sites
+    sp = [[[info.primes[(s * 3 + n) * H + h] for h in range(H)] for n in range(3)] for s in range(S)]
+    so = [[[info.offsets[(s * 3 + n) * H + h] for h in range(H)] for n in range(3)] for s in range(S)]
+    ss = [[info.prime_sum[s * 3 + n] for n in range(3)] for s in range(S)]
     return LayoutInfo(
         hash_floor=info.hash_floor, heads=H, row_dim=info.row_dim, rows=tuple(info.rows),
-        primes=[[info.primes[n * H + h] for h in range(H)] for n in range(3)],
-        offsets=[[info.offsets[n * H + h] for h in range(H)] for n in range(3)],
-        prime_sum=tuple(info.prime_sum), seg_pitch=info.seg_pitch, k_pad=info.k_pad)
+        primes=sp[0], offsets=so[0], prime_sum=tuple(ss[0]), seg_pitch=info.seg_pitch,
+        k_pad=info.k_pad, num_sites=S, table_split=info.table_split,
+        scale_layout=info.scale_layout, site_primes=sp, site_offsets=so, site_prime_sum=ss)
 
 
 def engram_tid2eid_check(layout: Layout, tid2eid, stream=None) -> int:
@@ -293,8 +322,9 @@ def engram_compress_hash(layout: Layout, tid2eid, tokens, cu_seqlens, eids, row_
     import torch
     T = tokens.numel()
     S = cu_seqlens.numel() - 1
-    H = layout.info.heads
-    _need(eids.numel() >= T and row_ids.numel() >= T * 3 * H, "eids / row_ids too small")
+    info = layout.info
+    _need(eids.numel() >= T and row_ids.numel() >= T * info.num_sites * info.cols,
+          "eids / row_ids too small")
     _need(tid2eid.numel() == layout.desc.vocab_size, "tid2eid must hold vocab_size entries")
     _need(seq_start is None or seq_start.numel() >= S, "seq_start too small")
     _need(slots is None or slots.numel() >= S, "slots too small")
@@ -309,32 +339,52 @@ def engram_compress_hash(layout: Layout, tid2eid, tokens, cu_seqlens, eids, row_
         "engram_compress_hash")
 
 
+def _site_pointers(layout: Layout, tables: Sequence, scales: Optional[Sequence]):
+    """ctypes arrays of the tables (and scales) one gather reads, after checking
+    their sizes against the layout."""
+    import torch
+    info = layout.info
+    per_site = info.table_split == ENGRAM_TABLE_PER_SITE
+    used = 1 if per_site else 3
+    _need(len(tables) >= used, f"{used} table(s) expected")
+    pitch = layout.desc.row_pitch_bytes
+    for n in range(used):
+        _need(tables[n].numel() >= info.rows[n] * pitch, f"table {n} smaller than rows x pitch")
+    tp = (_P * 3)(*[_dev(tables[min(n, used - 1)], torch.uint8, "table") for n in range(3)])
+    if scales is None:
+        return tp, None
+    _need(len(scales) >= used, f"{used} scale tensor(s) expected")
+    sp = []
+    for n in range(3):
+        sc = scales[min(n, used - 1)]
+        if info.scale_layout == ENGRAM_SCALE_BLOCK32_E8M0:
+            _need(sc.numel() >= info.rows[min(n, used - 1)] * (info.row_dim // 32),
+                  "e8m0 scales must be [rows][D/32]")
+            sp.append(_dev(sc, torch.uint8, "scale"))
+        else:
+            _need(sc.numel() >= info.rows[min(n, used - 1)], "scales smaller than rows")
+            sp.append(_dev(sc, torch.float32, "scale"))
+    return tp, (_P * 3)(*sp)
+
+
 def engram_gather_dequant(layout: Layout, tables: Sequence, scales: Optional[Sequence], row_ids,
-                          out, *, T: Optional[int] = None, stream=None):
+                          out, *, site: int = 0, T: Optional[int] = None, stream=None):
     import torch
     if T is None:
         T = row_ids.shape[0]
     info = layout.info
-    _need(row_ids.numel() >= T * 3 * info.heads, "row_ids too small")
+    _need(0 <= site < info.num_sites, "site out of range")
+    _need(row_ids.numel() >= T * info.num_sites * info.cols, "row_ids too small")
     _need(out.dim() == 2 and out.shape[0] >= T and out.shape[1] >= info.k_pad, "out too small")
-    pitch = layout.desc.row_pitch_bytes
-    for n, t in enumerate(tables):
-        _need(t.numel() >= info.rows[n] * pitch, f"table {n} smaller than rows x pitch")
-    if scales is not None:
-        for n, sc in enumerate(scales):
-            _need(sc.numel() >= info.rows[n], f"scale {n} smaller than rows")
-    tp = (_P * 3)(*[_dev(t, torch.uint8, "table") for t in tables])
-    sp = None
-    if scales is not None:
-        sp = (_P * 3)(*[_dev(s, torch.float32, "scale") for s in scales])
+    tp, sp = _site_pointers(layout, tables, scales)
     if out.dtype == torch.bfloat16:
         odt = ENGRAM_DTYPE_BF16
     elif out.dtype == torch.float32:
         odt = ENGRAM_DTYPE_F32
     else:
         raise TypeError("out must be bfloat16 or float32")
-    _check(_lib.engram_gather_dequant(layout.handle, tp, sp, _dev(row_ids, torch.int32, "row_ids"), T,
-                                      odt, _dev(out, None, "out"), out.shape[1], _stream(stream)),
+    _check(_lib.engram_gather_dequant(layout.handle, tp, sp, _dev(row_ids, torch.int32, "row_ids"), site,
+                                      T, odt, _dev(out, None, "out"), out.shape[1], _stream(stream)),
            "engram_gather_dequant")
 
 
@@ -351,23 +401,18 @@ def engram_project(layout: Layout, rows, w, v, *, T: Optional[int] = None, strea
 
 
 def engram_gather_project(layout: Layout, tables: Sequence, scales: Sequence, row_ids, w, v, *,
-                          T: Optional[int] = None, stream=None):
+                          site: int = 0, T: Optional[int] = None, stream=None):
     import torch
     if T is None:
         T = row_ids.shape[0]
     info = layout.info
-    _need(row_ids.numel() >= T * 3 * info.heads, "row_ids too small")
+    _need(0 <= site < info.num_sites, "site out of range")
+    _need(row_ids.numel() >= T * info.num_sites * info.cols, "row_ids too small")
     _need(w.dim() == 2 and v.dim() == 2 and v.shape[0] >= T and v.shape[1] == w.shape[0],
           "v must be [T][hidden]")
-    pitch = layout.desc.row_pitch_bytes
-    for n, t in enumerate(tables):
-        _need(t.numel() >= info.rows[n] * pitch, f"table {n} smaller than rows x pitch")
-    for n, sc in enumerate(scales):
-        _need(sc.numel() >= info.rows[n], f"scale {n} smaller than rows")
-    tp = (_P * 3)(*[_dev(t, torch.uint8, "table") for t in tables])
-    sp = (_P * 3)(*[_dev(s, torch.float32, "scale") for s in scales])
-    _check(_lib.engram_gather_project(layout.handle, tp, sp, _dev(row_ids, torch.int32, "row_ids"), T,
-                                      _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
+    tp, sp = _site_pointers(layout, tables, scales)
+    _check(_lib.engram_gather_project(layout.handle, tp, sp, _dev(row_ids, torch.int32, "row_ids"), site,
+                                      T, _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
                                       _dev(v, torch.float32, "v"), _stream(stream)),
            "engram_gather_project")
 

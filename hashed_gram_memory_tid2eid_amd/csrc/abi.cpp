@@ -143,6 +143,7 @@ extern "C" int engram_compress_hash(const engram_layout* L, const int32_t* d_tid
   a.S = S;
   a.num_slots = num_slots;
   a.heads = L->heads;
+  a.num_sites = L->num_sites;
   a.vocab = (int32_t)L->desc.vocab_size;
   a.pad_token_id = (int32_t)L->desc.pad_token_id;
   a.vc1 = L->vc_pow[1];
@@ -156,11 +157,35 @@ extern "C" int engram_compress_hash(const engram_layout* L, const int32_t* d_tid
 
 // ---- 2. gather + dequant -------------------------------------------------------
 
+// Resolves the tables and scales one gather reads: the site's three order
+// tables, or its one table (entry 0) repeated for every order.
+static int site_tables(const engram_layout* L, const void* const* d_tables,
+                       const void* const* d_scales, const uint8_t* table[3], const void* scale[3],
+                       int64_t rows[3]) {
+  const bool bf16_table = L->desc.table_dtype == ENGRAM_DTYPE_BF16;
+  const int used = L->per_site_table ? 1 : 3;
+  for (int n = 0; n < 3; ++n) {
+    const int src = n < used ? n : 0;
+    if (!d_tables[src]) return ENGRAM_E_ARG;
+    if (!aligned(d_tables[src], 16)) return ENGRAM_E_ALIGN;
+    table[n] = static_cast<const uint8_t*>(d_tables[src]);
+    scale[n] = nullptr;
+    if (!bf16_table) {
+      if (!d_scales[src]) return ENGRAM_E_ARG;
+      if (L->scale_block == 0 && !aligned(d_scales[src], 4)) return ENGRAM_E_ALIGN;
+      scale[n] = d_scales[src];
+    }
+    rows[n] = L->desc.rows[src];
+  }
+  return ENGRAM_OK;
+}
+
 extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* d_tables,
-                                     const float* const* d_scales, const int32_t* d_row_ids,
-                                     int32_t T, int32_t out_dtype, void* d_out, int64_t out_ld,
-                                     hipStream_t stream) {
+                                     const void* const* d_scales, const int32_t* d_row_ids,
+                                     int32_t site, int32_t T, int32_t out_dtype, void* d_out,
+                                     int64_t out_ld, hipStream_t stream) {
   if (!L || T < 0 || !d_tables) return ENGRAM_E_ARG;
+  if (site < 0 || site >= L->num_sites) return ENGRAM_E_ARG;
   if (out_dtype != ENGRAM_DTYPE_BF16 && out_dtype != ENGRAM_DTYPE_F32) return ENGRAM_E_ARG;
   const bool bf16_table = L->desc.table_dtype == ENGRAM_DTYPE_BF16;
   if (!bf16_table && !d_scales) return ENGRAM_E_ARG;
@@ -169,18 +194,11 @@ extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* 
   if (out_ld < L->k_pad || out_ld % 8 != 0) return ENGRAM_E_ALIGN;
   if (!aligned(d_out, 16)) return ENGRAM_E_ALIGN;
   engram::GatherArgs g;
-  for (int n = 0; n < 3; ++n) {
-    if (!d_tables[n]) return ENGRAM_E_ARG;
-    if (!aligned(d_tables[n], 16)) return ENGRAM_E_ALIGN;
-    g.table[n] = static_cast<const uint8_t*>(d_tables[n]);
-    g.scale[n] = nullptr;
-    if (!bf16_table) {
-      if (!d_scales[n]) return ENGRAM_E_ARG;
-      if (!aligned(d_scales[n], 4)) return ENGRAM_E_ALIGN;
-      g.scale[n] = d_scales[n];
-    }
-    g.rows[n] = L->desc.rows[n];
-  }
+  const int rc = site_tables(L, d_tables, d_scales, g.table, g.scale, g.rows);
+  if (rc != ENGRAM_OK) return rc;
+  g.rid_ld = L->all_cols;
+  g.per_site_table = L->per_site_table;
+  g.scale_block = L->scale_block;
   g.pitch = L->desc.row_pitch_bytes;
   g.heads = L->heads;
   g.cols = L->cols;
@@ -193,9 +211,10 @@ extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* 
   // one launch covers fewer than 2^31 output chunks; split bigger calls by tokens
   const int64_t chunks_per_token = (int64_t)L->cols * (L->seg_pitch / 16);
   const int64_t max_tokens = ((int64_t)1 << 31) / chunks_per_token - 1;
+  const int32_t* site_rows = d_row_ids + (int64_t)site * L->cols;
   for (int64_t t0 = 0; t0 < T; t0 += max_tokens) {
     const int64_t tn = (T - t0 < max_tokens) ? T - t0 : max_tokens;
-    g.row_ids = d_row_ids + t0 * L->cols;
+    g.row_ids = site_rows + t0 * L->all_cols;
     g.out = static_cast<char*>(d_out) + (size_t)t0 * out_ld * out_elt;
     g.T = (int32_t)tn;
     hipError_t e = engram::launch_gather_dequant(g, stream);
@@ -228,11 +247,13 @@ extern "C" int engram_project(const engram_layout* L, const void* d_rows, int64_
 }
 
 extern "C" int engram_gather_project(const engram_layout* L, const void* const* d_tables,
-                                     const float* const* d_scales, const int32_t* d_row_ids,
-                                     int32_t T, const void* d_w, int64_t w_ld, int32_t hidden,
-                                     float* d_v, hipStream_t stream) {
+                                     const void* const* d_scales, const int32_t* d_row_ids,
+                                     int32_t site, int32_t T, const void* d_w, int64_t w_ld,
+                                     int32_t hidden, float* d_v, hipStream_t stream) {
   if (!L || T < 0 || hidden < 1 || !d_tables || !d_scales) return ENGRAM_E_ARG;
+  if (site < 0 || site >= L->num_sites) return ENGRAM_E_ARG;
   if (L->desc.table_dtype != ENGRAM_DTYPE_FP8_E4M3FN) return ENGRAM_E_UNSUPPORTED;
+  if (L->scale_block != 0) return ENGRAM_E_UNSUPPORTED;
   if (T == 0) return ENGRAM_OK;
   if (!d_row_ids || !d_w || !d_v) return ENGRAM_E_ARG;
   const int64_t pitch = L->desc.row_pitch_bytes;
@@ -240,14 +261,13 @@ extern "C" int engram_gather_project(const engram_layout* L, const void* const* 
   if (w_ld < L->k_pad || w_ld % 8 != 0) return ENGRAM_E_ALIGN;
   if (!aligned(d_w, 16) || !aligned(d_v, 4)) return ENGRAM_E_ALIGN;
   engram::GatherGemmArgs g;
-  for (int n = 0; n < 3; ++n) {
-    if (!d_tables[n] || !d_scales[n]) return ENGRAM_E_ARG;
-    if (!aligned(d_tables[n], 16) || !aligned(d_scales[n], 4)) return ENGRAM_E_ALIGN;
-    g.table[n] = static_cast<const uint8_t*>(d_tables[n]);
-    g.scale[n] = d_scales[n];
-    g.rows[n] = L->desc.rows[n];
-  }
-  g.row_ids = d_row_ids;
+  const void* scale[3];
+  const int rc = site_tables(L, d_tables, d_scales, g.table, scale, g.rows);
+  if (rc != ENGRAM_OK) return rc;
+  for (int n = 0; n < 3; ++n) g.scale[n] = static_cast<const float*>(scale[n]);
+  g.row_ids = d_row_ids + (int64_t)site * L->cols;
+  g.rid_ld = L->all_cols;
+  g.per_site_table = L->per_site_table;
   g.pitch = pitch;
   g.row_dim = L->desc.row_dim;
   g.seg_pitch = (int32_t)L->seg_pitch;

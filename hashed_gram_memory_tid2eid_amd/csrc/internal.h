@@ -6,17 +6,19 @@
 
 #include "../../include/engram.h"
 
-#define ENGRAM_MAX_COLS (3 * ENGRAM_MAX_HEADS)
-
 struct engram_layout {
   engram_layout_desc desc;
   int64_t floor;
   int32_t heads;
-  int32_t cols;                          // 3 * heads
-  uint32_t prime[ENGRAM_MAX_COLS];       // [order][head]
-  uint32_t offset[ENGRAM_MAX_COLS];
-  uint64_t barrett[ENGRAM_MAX_COLS];     // floor((2^64 - 1) / prime)
-  int64_t prime_sum[3];
+  int32_t cols;                          // 3 * heads: hash columns of one site
+  int32_t num_sites;
+  int32_t all_cols;                      // num_sites * cols: ints per token of row_ids
+  int32_t per_site_table;                // ENGRAM_TABLE_PER_SITE
+  int32_t scale_block;                   // 0 (fp32 per row) or 32 (e8m0 per 32 elements)
+  uint32_t prime[ENGRAM_MAX_COLUMNS];    // [site][order][head]
+  uint32_t offset[ENGRAM_MAX_COLUMNS];
+  uint64_t barrett[ENGRAM_MAX_COLUMNS];  // floor((2^64 - 1) / prime)
+  int64_t prime_sum[ENGRAM_MAX_SITES][3];
   int64_t seg_pitch;                     // round_up(D, 64) elements
   int64_t k_pad;                         // cols * seg_pitch
   uint64_t vc_pow[4];                    // V_c^0 .. V_c^3
@@ -38,11 +40,12 @@ struct HashArgs {
   int32_t* eids;
   int32_t* row_ids;
   int32_t T, S, num_slots, heads;
+  int32_t num_sites;
   int32_t vocab, pad_token_id;
   uint64_t vc1, vc2, vc3;
-  uint32_t prime[ENGRAM_MAX_COLS];
-  uint32_t offset[ENGRAM_MAX_COLS];
-  uint64_t barrett[ENGRAM_MAX_COLS];
+  uint32_t prime[ENGRAM_MAX_COLUMNS];
+  uint32_t offset[ENGRAM_MAX_COLUMNS];
+  uint64_t barrett[ENGRAM_MAX_COLUMNS];
 };
 hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream);
 
@@ -83,9 +86,12 @@ hipError_t launch_store_op(const StoreArgs& a, hipStream_t stream);
 
 struct GatherArgs {
   const uint8_t* table[3];
-  const float* scale[3];
+  const void* scale[3];    // float [rows] or uint8 e8m0 [rows][D/32]
   int64_t rows[3];
-  const int32_t* row_ids;
+  const int32_t* row_ids;  // the site's first column; tokens rid_ld ints apart
+  int32_t rid_ld;
+  int32_t per_site_table;  // every segment reads table[0]
+  int32_t scale_block;     // 0 or 32
   void* out;
   int64_t out_ld;          // elements
   int64_t pitch;           // bytes
@@ -110,7 +116,9 @@ struct GatherGemmArgs {
   const uint8_t* table[3];
   const float* scale[3];
   int64_t rows[3];
-  const int32_t* row_ids;  // [M][cols]
+  const int32_t* row_ids;  // the site's first column; tokens rid_ld ints apart
+  int32_t rid_ld;
+  int32_t per_site_table;  // every segment reads table[0]
   int64_t pitch;           // bytes, >= seg_pitch, multiple of 16
   int32_t row_dim, seg_pitch, cols, heads;
   const void* B;           // bf16 [N][ldb], ldb >= cols * seg_pitch

@@ -15,9 +15,17 @@
 // partial lines).  Each lane keeps UNROLL chunks in flight.
 //
 // Dequant of a chunk: 16 e4m3fn bytes -> 16 fp32 (hardware conversion,
-// v_cvt_pk_f32_fp8), times the row's fp32 scale (one v_mul_f32 each: exactly
-// the IEEE product), then round-to-nearest-even to bf16 (v_cvt_pk_bf16_f32)
-// or kept as fp32.  BF16 tables are copied (or widened to fp32).
+// v_cvt_pk_f32_fp8), times the scale (one v_mul_f32 each: exactly the IEEE
+// product), then round-to-nearest-even to bf16 (v_cvt_pk_bf16_f32) or kept as
+// fp32.  The scale is the row's fp32 scale, or, for (1, 32)-blocked tables
+// ([VeOmni#1370] per-row-scale commit: one exponent per row per 32 columns),
+// the e8m0 byte b of the chunk's block as the float 2^(b-127) (b = 0 is the
+// subnormal 2^-127, b = 255 NaN); a 16-element chunk never straddles a block.
+// BF16 tables are copied (or widened to fp32).
+//
+// Several Engram sites share one row-id array [T][sites][3][H]; a call gathers
+// one site's columns (row_ids points at them, tokens rid_ld ints apart).  A
+// site's buckets live in three per-order tables or in one table for the site.
 
 namespace engram {
 
@@ -43,11 +51,14 @@ struct GatherKArgs {
   const uint8_t* t0;
   const uint8_t* t1;
   const uint8_t* t2;
-  const float* s0;
-  const float* s1;
-  const float* s2;
+  const void* s0;
+  const void* s1;
+  const void* s2;
   int32_t r0, r1, r2;  // rows per table
   const int32_t* row_ids;
+  int32_t rid_extra;   // rid_ld - cols: extra ints between consecutive tokens' row ids
+  uint32_t split;      // heads (per-order tables) or 2^30 (one table: every segment is n = 0)
+  uint32_t nblk;       // e8m0 bytes per row (row_dim / 32)
   void* out;
   int64_t out_ld;
   int64_t pitch;
@@ -67,7 +78,11 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   return (uint32_t)__builtin_bit_cast(unsigned short, b);
 }
 
-template <bool kBf16Table, bool kF32Out>
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return __uint_as_float(b == 0 ? 0x00400000u : (b == 255 ? 0x7FC00000u : b << 23));
+}
+
+template <bool kBf16Table, bool kF32Out, bool kBlockScale>
 __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKArgs a) {
   const uint32_t first = blockIdx.x * (kGatherThreads * kGatherUnroll) + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -97,9 +112,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKA
     chunk[u] = g - rowidx * a.chunks;
     tok[u] = fdiv(rowidx, a.div_cols);
     seg[u] = rowidx - tok[u] * a.cols;
-    const uint32_t n = (seg[u] >= a.heads) + (seg[u] >= 2 * a.heads);
+    const uint32_t n = (seg[u] >= a.split) + (seg[u] >= 2 * a.split);
     if (chunk[u] * 16 >= a.row_dim) continue;  // pure padding: zeros
-    const int32_t row = a.row_ids[rowidx];
+    const int32_t row = a.row_ids[(int64_t)rowidx + (int64_t)tok[u] * a.rid_extra];
     const int32_t rows = n == 0 ? a.r0 : (n == 1 ? a.r1 : a.r2);
     if (row < 0 || row >= rows) {
       latch_error(ENGRAM_E_ROW_RANGE);
@@ -110,8 +125,11 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKA
     raw[u][0] = *reinterpret_cast<const u32x4*>(src);
     if (kBf16Table) {
       raw[u][kBf16Table ? 1 : 0] = *reinterpret_cast<const u32x4*>(src + 16);
+    } else if (kBlockScale) {
+      const uint8_t* sc = static_cast<const uint8_t*>(n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2));
+      scale[u] = e8m0_value(sc[(int64_t)row * a.nblk + (chunk[u] >> 1)]);
     } else {
-      const float* sc = n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2);
+      const float* sc = static_cast<const float*>(n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2));
       scale[u] = sc[row];
     }
     any[u] = true;
@@ -214,6 +232,9 @@ hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
   a.r1 = (int32_t)g.rows[1];
   a.r2 = (int32_t)g.rows[2];
   a.row_ids = g.row_ids;
+  a.rid_extra = g.rid_ld - g.cols;
+  a.split = g.per_site_table ? (1u << 30) : (uint32_t)g.heads;
+  a.nblk = (uint32_t)(g.row_dim / 32);
   a.out = g.out;
   a.out_ld = g.out_ld;
   a.pitch = g.pitch;
@@ -231,16 +252,22 @@ hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
   a.div_cols = make_fastdiv(a.cols);
   const uint32_t per_block = kGatherThreads * kGatherUnroll;
   const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+  const dim3 block(kGatherThreads);
   if (g.bf16_table) {
     if (g.f32_out)
-      hipLaunchKernelGGL((gather_dequant_kernel<true, true>), grid, dim3(kGatherThreads), 0, stream, a);
+      hipLaunchKernelGGL((gather_dequant_kernel<true, true, false>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((gather_dequant_kernel<true, false>), grid, dim3(kGatherThreads), 0, stream, a);
+      hipLaunchKernelGGL((gather_dequant_kernel<true, false, false>), grid, block, 0, stream, a);
+  } else if (g.scale_block == 32) {
+    if (g.f32_out)
+      hipLaunchKernelGGL((gather_dequant_kernel<false, true, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gather_dequant_kernel<false, false, true>), grid, block, 0, stream, a);
   } else {
     if (g.f32_out)
-      hipLaunchKernelGGL((gather_dequant_kernel<false, true>), grid, dim3(kGatherThreads), 0, stream, a);
+      hipLaunchKernelGGL((gather_dequant_kernel<false, true, false>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((gather_dequant_kernel<false, false>), grid, dim3(kGatherThreads), 0, stream, a);
+      hipLaunchKernelGGL((gather_dequant_kernel<false, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

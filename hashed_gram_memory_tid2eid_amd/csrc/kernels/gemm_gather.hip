@@ -30,7 +30,9 @@ struct GatherGemmKArgs {
   const float* s1;
   const float* s2;
   int32_t r0, r1, r2;       // rows per table
-  const int32_t* row_ids;   // [M][cols]
+  const int32_t* row_ids;   // the site's first column; tokens rid_ld ints apart
+  int32_t rid_ld;
+  int32_t split;            // heads (per-order tables) or 2^29 (one table per site)
   int64_t pitch;            // table row pitch, bytes (>= seg_pitch)
   int32_t row_dim, seg_pitch, cols, heads;
   const __bf16* B;          // [N][ldb]
@@ -49,6 +51,9 @@ constexpr int kGgA8_BYTES = kGgBM * kGgBK;       // 16 KB
 constexpr int kGgB_OFF = 0, kGgA16_OFF = 2 * kGgB_BYTES, kGgA8_OFF = kGgA16_OFF + 2 * kGgA16_BYTES;
 constexpr int kGgLDS = kGgA8_OFF + 2 * kGgA8_BYTES;  // 160 KB
 
+__device__ __forceinline__ int gg_order(const GatherGemmKArgs& a, int seg) {
+  return (seg >= a.split) + (seg >= 2 * a.split);
+}
 __device__ __forceinline__ const uint8_t* gg_table(const GatherGemmKArgs& a, int n) {
   return n == 0 ? a.t0 : (n == 1 ? a.t1 : a.t2);
 }
@@ -113,13 +118,13 @@ __global__ __launch_bounds__(kGgThreads, 1) void gemm_gather_fp8_kernel(GatherGe
   }
   int dma_seg = -1;
   auto set_dma_segment = [&](int seg) {
-    const int n = seg / a.heads;
+    const int n = gg_order(a, seg);
     const uint8_t* tb = gg_table(a, n);
     const int rows = gg_rows(a, n);
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int m = m0 + a_row[i];
-      int r = m < a.M ? a.row_ids[(int64_t)m * a.cols + seg] : 0;
+      int r = m < a.M ? a.row_ids[(int64_t)m * a.rid_ld + seg] : 0;
       if (r < 0 || r >= rows) r = 0;  // reported by the converting thread; keep the read in bounds
       ap[i] = tb + (int64_t)r * a.pitch + 16 * a_piece[i];
     }
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(kGgThreads, 1) void gemm_gather_fp8_kernel(GatherGe
   int conv_seg = -1;
   float cscale[4];  // per phase row; 0 for rows past M and bad row ids (they convert to zeros)
   auto set_conv_segment = [&](int seg) {
-    const int n = seg / a.heads;
+    const int n = gg_order(a, seg);
     const float* sc = gg_scale(a, n);
     const int rows = gg_rows(a, n);
 #pragma unroll
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(kGgThreads, 1) void gemm_gather_fp8_kernel(GatherGe
       const int m = m0 + 64 * q + (tid >> 3);
       cscale[q] = 0.f;
       if (m < a.M) {
-        const int r = a.row_ids[(int64_t)m * a.cols + seg];
+        const int r = a.row_ids[(int64_t)m * a.rid_ld + seg];
         if (r < 0 || r >= rows)
           latch_error(ENGRAM_E_ROW_RANGE);
         else
@@ -338,6 +343,8 @@ hipError_t launch_gemm_gather_fp8(const GatherGemmArgs& g, hipStream_t stream) {
   a.r1 = (int32_t)g.rows[1];
   a.r2 = (int32_t)g.rows[2];
   a.row_ids = g.row_ids;
+  a.rid_ld = g.rid_ld;
+  a.split = g.per_site_table ? (1 << 29) : g.heads;  // 2 * split stays below 2^31
   a.pitch = g.pitch;
   a.row_dim = g.row_dim;
   a.seg_pitch = g.seg_pitch;

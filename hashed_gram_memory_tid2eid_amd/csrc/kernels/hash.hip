@@ -121,13 +121,19 @@ __global__ __launch_bounds__(256) void compress_hash_kernel(HashArgs a) {
   const uint64_t k3 = k2 + (uint64_t)w[2] * a.vc2;
   const uint64_t k4 = k3 + (uint64_t)w[3] * a.vc3;
   a.eids[t] = (int32_t)w[0];
-  int32_t* out = a.row_ids + (int64_t)t * (3 * a.heads);
-  for (int h = 0; h < a.heads; ++h) {
-    out[h] = (int32_t)(a.offset[h] + mod_barrett(k2, a.prime[h], a.barrett[h]));
-    const int c3 = a.heads + h;
-    out[c3] = (int32_t)(a.offset[c3] + mod_barrett(k3, a.prime[c3], a.barrett[c3]));
-    const int c4 = 2 * a.heads + h;
-    out[c4] = (int32_t)(a.offset[c4] + mod_barrett(k4, a.prime[c4], a.barrett[c4]));
+  // every site from the same keys: [site][order][head]
+  const int cols = 3 * a.heads;
+  int32_t* out = a.row_ids + (int64_t)t * (cols * a.num_sites);
+  for (int st = 0; st < a.num_sites; ++st) {
+    const int base = st * cols;
+    for (int h = 0; h < a.heads; ++h) {
+      const int c2 = base + h;
+      out[c2] = (int32_t)(a.offset[c2] + mod_barrett(k2, a.prime[c2], a.barrett[c2]));
+      const int c3 = base + a.heads + h;
+      out[c3] = (int32_t)(a.offset[c3] + mod_barrett(k3, a.prime[c3], a.barrett[c3]));
+      const int c4 = base + 2 * a.heads + h;
+      out[c4] = (int32_t)(a.offset[c4] + mod_barrett(k4, a.prime[c4], a.barrett[c4]));
+    }
   }
 }
 

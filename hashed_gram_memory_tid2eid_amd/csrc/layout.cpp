@@ -1,19 +1,22 @@
-// layout.cpp -- host-side bucket layout of one Engram site (no HIP calls).
+// layout.cpp -- host-side bucket layout of the Engram sites sharing one hash
+// pass (no HIP calls).
 //
 // Bucket primes ([VeOmni#1370] "feat: support DeepSeek-V4.1-Flash in SeedOmni",
 // n-gram memory lookup commit and the validate_bucket_layout review thread):
-// for each order 2..4 and each head, the smallest prime at or above the floor
-// that no earlier (order, head) drew.  With one layer this is simply the first
-// 3*H primes at or above the floor, dealt out order-major; that is how it is
-// computed here (Miller-Rabin on a walk upward from the floor).
+// for each site (layer), each order 2..4 and each head, the smallest prime at
+// or above the floor that no earlier (site, order, head) drew.  That is the
+// first num_sites*3*H primes at or above the floor, dealt out site-major, then
+// order, then head; that is how it is computed here (Miller-Rabin on a walk
+// upward from the floor).
 //
 // Table split: one table per order (PR summary: 3-table lookup over 2-/3-/4-gram
-// tables), so each order's buckets start at offset 0 of its own table and the
-// row-count guard of the review thread (fewer rows than the prime sum is an
-// error, more is allowed) applies per table.  With no floor given, the floor
-// is the largest one whose primes fit every table; it is found by walking the
-// floor down from min(rows)/H while keeping the window of the first 3*H primes
-// at or above it.
+// tables), so each order's buckets start at offset 0 of its own table; or one
+// table per site (the released checkpoint's one embedding per Engram layer),
+// with offsets running across the orders.  The row-count guard of the review
+// thread (fewer rows than the prime sum is an error, more is allowed) applies
+// per table.  With no floor given, the floor is the largest one whose primes
+// fit every table; it is found by walking the floor down from an upper bound
+// while keeping the window of the first num_sites*3*H primes at or above it.
 #include <stdlib.h>
 #include <string.h>
 
@@ -75,14 +78,20 @@ std::vector<uint64_t> primes_from(uint64_t floor_, int count) {
   return out;
 }
 
-bool window_fits(const std::vector<uint64_t>& p, int heads, const int64_t rows[3],
-                 int64_t sums[3]) {
+// Bucket rows per (site, order) of a draw; does every table hold its buckets?
+bool window_fits(const std::vector<uint64_t>& p, int sites, int heads, bool per_site,
+                 const int64_t rows[3], int64_t sums[ENGRAM_MAX_SITES][3]) {
   bool ok = true;
-  for (int n = 0; n < 3; ++n) {
-    int64_t s = 0;
-    for (int h = 0; h < heads; ++h) s += (int64_t)p[n * heads + h];
-    sums[n] = s;
-    if (s > rows[n]) ok = false;
+  for (int st = 0; st < sites; ++st) {
+    int64_t site_total = 0;
+    for (int n = 0; n < 3; ++n) {
+      int64_t s = 0;
+      for (int h = 0; h < heads; ++h) s += (int64_t)p[(st * 3 + n) * heads + h];
+      sums[st][n] = s;
+      site_total += s;
+      if (!per_site && s > rows[n]) ok = false;
+    }
+    if (per_site && site_total > rows[0]) ok = false;
   }
   return ok;
 }
@@ -100,7 +109,12 @@ extern "C" int engram_layout_create(const engram_layout_desc* d, engram_layout**
   if (d->pad_token_id < 0 || d->pad_token_id >= d->vocab_size) return ENGRAM_E_ARG;
   if (d->row_dim < 1) return ENGRAM_E_ARG;
   if (d->hash_floor < 0) return ENGRAM_E_ARG;
-  for (int n = 0; n < 3; ++n)
+  const int S = d->num_sites == 0 ? 1 : d->num_sites;
+  if (S < 1 || S > ENGRAM_MAX_SITES) return ENGRAM_E_ARG;
+  if (d->table_split != ENGRAM_TABLES_PER_ORDER && d->table_split != ENGRAM_TABLE_PER_SITE)
+    return ENGRAM_E_ARG;
+  const bool per_site = d->table_split == ENGRAM_TABLE_PER_SITE;
+  for (int n = 0; n < (per_site ? 1 : 3); ++n)
     if (d->rows[n] < 1 || d->rows[n] > INT32_MAX) return ENGRAM_E_ARG;
   int elt;
   if (d->table_dtype == ENGRAM_DTYPE_FP8_E4M3FN)
@@ -109,25 +123,39 @@ extern "C" int engram_layout_create(const engram_layout_desc* d, engram_layout**
     elt = 2;
   else
     return ENGRAM_E_ARG;
+  if (d->scale_layout != ENGRAM_SCALE_ROW_F32 && d->scale_layout != ENGRAM_SCALE_BLOCK32_E8M0)
+    return ENGRAM_E_ARG;
+  if (d->scale_layout == ENGRAM_SCALE_BLOCK32_E8M0) {
+    if (d->table_dtype != ENGRAM_DTYPE_FP8_E4M3FN) return ENGRAM_E_ARG;
+    if (d->row_dim % 32 != 0) return ENGRAM_E_ALIGN;
+  }
   const int64_t min_pitch = ((int64_t)(d->row_dim + 15) / 16) * 16 * elt;
   if (d->row_pitch_bytes % 16 != 0 || d->row_pitch_bytes < min_pitch) return ENGRAM_E_ALIGN;
 
   const int cols = 3 * H;
+  const int count = S * cols;
+  int64_t rows[3] = {d->rows[0], d->rows[1], d->rows[2]};
   std::vector<uint64_t> p;
-  int64_t sums[3];
+  int64_t sums[ENGRAM_MAX_SITES][3];
   uint64_t floor_;
   if (d->hash_floor > 0) {
     floor_ = (uint64_t)d->hash_floor;
-    p = primes_from(floor_, cols);
-    if (!window_fits(p, H, d->rows, sums)) return ENGRAM_E_LAYOUT_ROWS;
+    p = primes_from(floor_, count);
+    if (!window_fits(p, S, H, per_site, rows, sums)) return ENGRAM_E_LAYOUT_ROWS;
   } else {
-    int64_t rmin = d->rows[0];
-    if (d->rows[1] < rmin) rmin = d->rows[1];
-    if (d->rows[2] < rmin) rmin = d->rows[2];
-    floor_ = (uint64_t)(rmin / H);
+    int64_t start;
+    if (per_site) {
+      start = rows[0] / cols;
+    } else {
+      start = rows[0];
+      if (rows[1] < start) start = rows[1];
+      if (rows[2] < start) start = rows[2];
+      start /= H;
+    }
+    floor_ = (uint64_t)start;
     if (floor_ < 2) return ENGRAM_E_NOFIT;
-    p = primes_from(floor_, cols);
-    while (!window_fits(p, H, d->rows, sums)) {
+    p = primes_from(floor_, count);
+    while (!window_fits(p, S, H, per_site, rows, sums)) {
       if (floor_ <= 2) return ENGRAM_E_NOFIT;
       --floor_;
       if (is_prime(floor_)) {  // it joins the window at the front, the largest leaves
@@ -140,19 +168,27 @@ extern "C" int engram_layout_create(const engram_layout_desc* d, engram_layout**
   engram_layout* L = (engram_layout*)calloc(1, sizeof(engram_layout));
   if (!L) return ENGRAM_E_ARG;
   L->desc = *d;
+  L->desc.num_sites = S;
   L->floor = (int64_t)floor_;
   L->heads = H;
   L->cols = cols;
-  for (int n = 0; n < 3; ++n) {
-    uint64_t acc = 0;
-    for (int h = 0; h < H; ++h) {
-      const int c = n * H + h;
-      L->prime[c] = (uint32_t)p[c];
-      L->offset[c] = (uint32_t)acc;
-      L->barrett[c] = UINT64_MAX / p[c];
-      acc += p[c];
+  L->num_sites = S;
+  L->all_cols = count;
+  L->per_site_table = per_site ? 1 : 0;
+  L->scale_block = d->scale_layout == ENGRAM_SCALE_BLOCK32_E8M0 ? 32 : 0;
+  for (int st = 0; st < S; ++st) {
+    uint64_t acc = 0;  // a site's table: offsets run across its orders
+    for (int n = 0; n < 3; ++n) {
+      if (!per_site) acc = 0;  // an order's table: offsets restart
+      for (int h = 0; h < H; ++h) {
+        const int c = (st * 3 + n) * H + h;
+        L->prime[c] = (uint32_t)p[c];
+        L->offset[c] = (uint32_t)acc;
+        L->barrett[c] = UINT64_MAX / p[c];
+        acc += p[c];
+      }
+      L->prime_sum[st][n] = sums[st][n];
     }
-    L->prime_sum[n] = sums[n];
   }
   L->seg_pitch = ((int64_t)d->row_dim + 63) / 64 * 64;
   L->k_pad = (int64_t)cols * L->seg_pitch;
@@ -173,16 +209,18 @@ extern "C" int engram_layout_query(const engram_layout* L, engram_layout_info* i
   info->hash_floor = L->floor;
   info->heads_per_order = L->heads;
   info->row_dim = L->desc.row_dim;
-  for (int n = 0; n < 3; ++n) {
-    info->rows[n] = L->desc.rows[n];
-    info->prime_sum[n] = L->prime_sum[n];
-  }
-  for (int c = 0; c < L->cols; ++c) {
+  for (int n = 0; n < 3; ++n) info->rows[n] = L->desc.rows[n];
+  for (int st = 0; st < L->num_sites; ++st)
+    for (int n = 0; n < 3; ++n) info->prime_sum[st][n] = L->prime_sum[st][n];
+  for (int c = 0; c < L->all_cols; ++c) {
     info->primes[c] = L->prime[c];
     info->offsets[c] = L->offset[c];
   }
   info->seg_pitch = L->seg_pitch;
   info->k_pad = L->k_pad;
+  info->num_sites = L->num_sites;
+  info->table_split = L->per_site_table ? ENGRAM_TABLE_PER_SITE : ENGRAM_TABLES_PER_ORDER;
+  info->scale_layout = L->scale_block == 32 ? ENGRAM_SCALE_BLOCK32_E8M0 : ENGRAM_SCALE_ROW_F32;
   return ENGRAM_OK;
 }
 

@@ -1,9 +1,9 @@
 """One Engram site on one GPU: the C-ABI calls chained over preallocated
 device buffers.
 
-``Engram.forward`` = engram_compress_hash -> engram_gather_dequant ->
-engram_gated_residual on one stream, no host synchronisation, no allocation
-(path "split", the default).  Path "fused" (e4m3fn tables only) replaces the
+``Engram.forward`` = engram_compress_hash (every site in one pass) -> for each
+site engram_gather_dequant -> engram_gated_residual, on one stream, no host
+synchronisation, no allocation (path "split", the default).  Path "fused" (e4m3fn tables only) replaces the
 gather and the projection by engram_gather_project, which keeps the gathered
 rows on chip: no [T][k_pad] bf16 row buffer, at a lower projection rate.
 """
@@ -11,7 +11,9 @@ from __future__ import annotations
 
 from typing import Optional, Sequence
 
-from . import (ENGRAM_DTYPE_BF16, ENGRAM_DTYPE_FP8_E4M3FN, Layout, engram_compress_hash,
+from . import (ENGRAM_DTYPE_BF16, ENGRAM_DTYPE_FP8_E4M3FN, ENGRAM_SCALE_BLOCK32_E8M0,
+               ENGRAM_SCALE_ROW_F32, ENGRAM_TABLE_PER_SITE, ENGRAM_TABLES_PER_ORDER, Layout,
+               engram_compress_hash,
                engram_gate_add, engram_gather_dequant, engram_gather_project,
                engram_gated_residual, engram_layout_create, engram_tid2eid_check)
 
@@ -34,67 +36,117 @@ def pad_weight(w, layout: Layout):
 
 
 class Engram:
-    """Device state of one Engram site: layout, compression map, tables, padded
-    weight, and the per-call work buffers sized for ``max_tokens``."""
+    """Device state of the Engram sites that share one hash pass: layout,
+    compression map, each site's tables, scales and padded weight, and the
+    per-call work buffers sized for ``max_tokens`` (rows and v are reused site
+    after site).
+
+    One site: ``tables`` / ``scales`` are the site's table list, ``weight`` its
+    [hidden][3*H*D] matrix.  Several sites: one such list (and one weight) per
+    site, in site order."""
 
     def __init__(self, *, vocab_size: int, compressed_vocab: int, pad_token_id: int,
                  heads_per_order: int, rows: Sequence[int], row_dim: int, table_dtype: str,
                  row_pitch_bytes: int, tid2eid, tables: Sequence, scales: Optional[Sequence],
                  weight, hidden: int, hc_mult: int = 4, max_tokens: int, hash_floor: int = 0,
-                 path: str = "split", stream=None):
+                 path: str = "split", num_sites: int = 1, table_split: str = "order",
+                 scale_block: int = 0, stream=None):
         import torch
         if path not in ("split", "fused"):
             raise ValueError(f"unknown path {path!r}")
-        if path == "fused" and table_dtype != "fp8":
-            raise ValueError("the fused path reads e4m3fn tables only")
+        if path == "fused" and (table_dtype != "fp8" or scale_block):
+            raise ValueError("the fused path reads e4m3fn tables with a per-row fp32 scale only")
+        if table_split not in ("order", "site"):
+            raise ValueError(f"unknown table split {table_split!r}")
         self.path = path
         dt = ENGRAM_DTYPE_FP8_E4M3FN if table_dtype == "fp8" else ENGRAM_DTYPE_BF16
         self.layout = engram_layout_create(
             vocab_size=vocab_size, compressed_vocab=compressed_vocab, pad_token_id=pad_token_id,
-            heads_per_order=heads_per_order, rows=rows, row_dim=row_dim, table_dtype=dt,
-            row_pitch_bytes=row_pitch_bytes, hash_floor=hash_floor)
+            heads_per_order=heads_per_order, rows=list(rows) + [0] * (3 - len(rows)),
+            row_dim=row_dim, table_dtype=dt, row_pitch_bytes=row_pitch_bytes, hash_floor=hash_floor,
+            num_sites=num_sites,
+            table_split=ENGRAM_TABLE_PER_SITE if table_split == "site" else ENGRAM_TABLES_PER_ORDER,
+            scale_layout=ENGRAM_SCALE_BLOCK32_E8M0 if scale_block == 32 else ENGRAM_SCALE_ROW_F32)
         info = self.layout.info
         dev = tid2eid.device
+        self.num_sites = num_sites
         self.tid2eid = tid2eid
         self.pad_eid = engram_tid2eid_check(self.layout, tid2eid, stream)
-        self.tables = list(tables)
-        self.scales = None if scales is None else list(scales)
-        self.weight = pad_weight(weight, self.layout) if weight.shape[1] != info.k_pad else weight
+        if num_sites == 1:
+            tables, scales, weight = [tables], [scales], [weight]
+        if len(tables) != num_sites or len(weight) != num_sites or (scales is not None and
+                                                                      len(scales) != num_sites):
+            raise ValueError("one table list, scale list and weight per site")
+        self.site_tables = [list(t) for t in tables]
+        self.site_scales = [None if sc is None else list(sc) for sc in
+                            (scales if scales is not None else [None] * num_sites)]
+        self.site_weights = [pad_weight(w, self.layout) if w.shape[1] != info.k_pad else w
+                             for w in weight]
         self.hidden = hidden
         self.hc_mult = hc_mult
         self.max_tokens = max_tokens
         self.eids = torch.empty(max_tokens, dtype=torch.int32, device=dev)
-        self.row_ids = torch.empty((max_tokens, 3, info.heads), dtype=torch.int32, device=dev)
+        rid_shape = ((max_tokens, 3, info.heads) if num_sites == 1
+                     else (max_tokens, num_sites, 3, info.heads))
+        self.row_ids = torch.empty(rid_shape, dtype=torch.int32, device=dev)
         self.rows = (torch.empty((max_tokens, info.k_pad), dtype=torch.bfloat16, device=dev)
                      if path == "split" else None)
         self.v = torch.empty((max_tokens, hidden), dtype=torch.float32, device=dev)
+
+    # single-site views
+    @property
+    def tables(self):
+        return self.site_tables[0]
+
+    @property
+    def scales(self):
+        return self.site_scales[0]
+
+    @property
+    def weight(self):
+        return self.site_weights[0]
 
     @property
     def info(self):
         return self.layout.info
 
+    def hash(self, tokens, cu_seqlens, *, seq_start=None, slots=None, store=None, dead=None,
+             stream=None):
+        """Compressed ids and every site's row ids of one call, in one pass."""
+        engram_compress_hash(self.layout, self.tid2eid, tokens, cu_seqlens, self.eids,
+                             self.row_ids, seq_start=seq_start, slots=slots, store=store,
+                             dead=dead, stream=stream)
+
+    def site_forward(self, site: int, streams, T: int, *, keep=None, stream=None):
+        """Gather, project and gate of one site from the row ids of the last hash."""
+        if self.path == "fused":
+            engram_gather_project(self.layout, self.site_tables[site], self.site_scales[site],
+                                  self.row_ids, self.site_weights[site], self.v, site=site, T=T,
+                                  stream=stream)
+            engram_gate_add(self.layout, self.v, streams, keep=keep, T=T, stream=stream)
+            return streams
+        engram_gather_dequant(self.layout, self.site_tables[site], self.site_scales[site],
+                              self.row_ids, self.rows, site=site, T=T, stream=stream)
+        engram_gated_residual(self.layout, self.rows, self.site_weights[site], streams, self.v,
+                              keep=keep, T=T, stream=stream)
+        return streams
+
     def forward(self, tokens, cu_seqlens, streams, *, seq_start=None, slots=None, store=None,
                 dead=None, keep=None, stream=None):
         """Adds the Engram memory of ``tokens`` into ``streams`` (bf16 [T][hc][hidden],
-        in place).  With a dead mask the caller passes ``keep`` (1 = keep the gate),
-        the complement of ``dead``."""
+        in place; with several sites, one such tensor per site, in site order).  With a
+        dead mask the caller passes ``keep`` (1 = keep the gate), the complement of
+        ``dead``."""
         T = tokens.numel()
         if T > self.max_tokens:
             raise ValueError(f"{T} tokens > max_tokens {self.max_tokens}")
         if dead is not None and keep is None:
             raise ValueError("a dead mask needs the matching keep mask")
-        if streams.shape[0] != T:
-            raise ValueError("streams must hold one row per token")
-        engram_compress_hash(self.layout, self.tid2eid, tokens, cu_seqlens, self.eids,
-                             self.row_ids, seq_start=seq_start, slots=slots, store=store,
-                             dead=dead, stream=stream)
-        if self.path == "fused":
-            engram_gather_project(self.layout, self.tables, self.scales, self.row_ids, self.weight,
-                                  self.v, T=T, stream=stream)
-            engram_gate_add(self.layout, self.v, streams, keep=keep, T=T, stream=stream)
-            return streams
-        engram_gather_dequant(self.layout, self.tables, self.scales, self.row_ids, self.rows,
-                              T=T, stream=stream)
-        engram_gated_residual(self.layout, self.rows, self.weight, streams, self.v, keep=keep,
-                              T=T, stream=stream)
+        per_site = [streams] if self.num_sites == 1 else list(streams)
+        if len(per_site) != self.num_sites or any(x.shape[0] != T for x in per_site):
+            raise ValueError("streams must hold one row per token (one tensor per site)")
+        self.hash(tokens, cu_seqlens, seq_start=seq_start, slots=slots, store=store, dead=dead,
+                  stream=stream)
+        for s in range(self.num_sites):
+            self.site_forward(s, per_site[s], T, keep=keep, stream=stream)
         return streams

@@ -69,11 +69,32 @@ typedef enum engram_dtype {
 } engram_dtype;
 
 #define ENGRAM_MAX_HEADS 8 /* hash heads per n-gram order */
+#define ENGRAM_MAX_SITES 4 /* Engram sites sharing one hash pass */
+
+/* How a site's buckets are laid out in memory. */
+typedef enum engram_table_split {
+  /* one table per n-gram order (PR summary: 3-table lookup over 2-/3-/4-gram
+     tables); bucket offsets restart at 0 in each order's table */
+  ENGRAM_TABLES_PER_ORDER = 0,
+  /* one table per site holding all 3*H buckets back to back (order-major, then
+     head), as the released checkpoint stores one embedding per Engram layer
+     ([VeOmni#1370] n-gram memory lookup commit: 384,006,168 / 384,016,682 rows) */
+  ENGRAM_TABLE_PER_SITE = 1
+} engram_table_split;
+
+/* Scales of e4m3fn tables. */
+typedef enum engram_scale_layout {
+  ENGRAM_SCALE_ROW_F32 = 0,      /* one fp32 scale per row                        */
+  ENGRAM_SCALE_BLOCK32_E8M0 = 32 /* one e8m0 exponent byte per 32 elements of a row
+                                    ([VeOmni#1370] per-row-scale commit: the tables
+                                    are blocked (1, 32)); value 2^(b - 127), 0xFF NaN */
+} engram_scale_layout;
 
 /* ---- layout ------------------------------------------------------------- */
-/* Description of one Engram site: three hashed tables, one per n-gram order
- * 2, 3, 4 ([VeOmni#1370] PR summary: 3-table hashed n-gram lookup over 2-/3-/
- * 4-gram tables), each with `heads_per_order` prime-sized hash buckets. */
+/* Description of the Engram sites that share one hash pass ([vLLM-V41]
+ * DeepseekV4Model.forward: one gather of hashes feeds every layer, each taking
+ * its columns through layer_hash_index).  Each site has 3 n-gram orders 2, 3, 4
+ * with `heads_per_order` prime-sized hash buckets each. */
 typedef struct engram_layout_desc {
   int64_t vocab_size;       /* tokenizer vocabulary = length of tid2eid ([VeOmni#1370]
                                vocab_size / engram_vocab_size commit: 129,280)        */
@@ -81,17 +102,26 @@ typedef struct engram_layout_desc {
   int64_t pad_token_id;     /* its compressed id is the pad id of blocked lookbacks    */
   int32_t max_ngram;        /* must be 4 (orders 2, 3, 4)                              */
   int32_t heads_per_order;  /* H, 1..ENGRAM_MAX_HEADS                                  */
-  int64_t rows[3];          /* rows of the 2-, 3-, 4-gram tables                        */
+  int64_t rows[3];          /* TABLES_PER_ORDER: rows of each site's 2-, 3-, 4-gram
+                               tables.  TABLE_PER_SITE: rows[0] = rows of each site's
+                               table; rows[1], rows[2] ignored                         */
   int64_t hash_floor;       /* primes are drawn at and above this floor (the pages'
                                hash_vocab_size); 0 = fit the largest floor whose
                                primes fit every table                                  */
   int32_t row_dim;          /* D, elements per table row                                */
-  int32_t table_dtype;      /* ENGRAM_DTYPE_FP8_E4M3FN (+ fp32 scale per row) or BF16   */
+  int32_t table_dtype;      /* ENGRAM_DTYPE_FP8_E4M3FN (+ scales) or BF16               */
   int64_t row_pitch_bytes;  /* bytes between rows: multiple of 16 and at least
                                round_up(D, 16) * element size                           */
+  int32_t num_sites;        /* sites sharing the hash pass, 1..ENGRAM_MAX_SITES (0 = 1);
+                               site s draws its primes after sites 0..s-1            */
+  int32_t table_split;      /* engram_table_split                                      */
+  int32_t scale_layout;     /* engram_scale_layout (fp8 tables; BLOCK32 needs D % 32 == 0) */
+  int32_t reserved;         /* 0 */
 } engram_layout_desc;
 
 typedef struct engram_layout engram_layout; /* opaque, immutable after creation */
+
+#define ENGRAM_MAX_COLUMNS (ENGRAM_MAX_SITES * 3 * ENGRAM_MAX_HEADS)
 
 /* Read-back of a created layout. */
 typedef struct engram_layout_info {
@@ -99,24 +129,31 @@ typedef struct engram_layout_info {
   int32_t heads_per_order;
   int32_t row_dim;
   int64_t rows[3];
-  int64_t primes[3 * ENGRAM_MAX_HEADS];     /* [order][head]; first 3*H entries used    */
-  int64_t offsets[3 * ENGRAM_MAX_HEADS];    /* bucket start inside its order's table    */
-  int64_t prime_sum[3];                     /* addressable rows of each table           */
+  int64_t primes[ENGRAM_MAX_COLUMNS];       /* [site][order][head]; first num_sites*3*H
+                                               entries used                             */
+  int64_t offsets[ENGRAM_MAX_COLUMNS];      /* bucket start inside its table (the order's
+                                               table, or the site's table)              */
+  int64_t prime_sum[ENGRAM_MAX_SITES][3];   /* bucket rows per (site, order)            */
   int64_t seg_pitch;                        /* elements between the (order, head)
                                                segments of one gathered token row:
                                                round_up(D, 64); the tail is zero        */
   int64_t k_pad;                            /* 3 * H * seg_pitch: width of a gathered
                                                token row and of the projection's K      */
+  int32_t num_sites;
+  int32_t table_split;
+  int32_t scale_layout;
+  int32_t reserved;
 } engram_layout_info;
 
-/* Creates the layout: draws the bucket primes (for each order, for each head,
- * the smallest prime at or above the floor not yet drawn, [VeOmni#1370]
- * n-gram memory lookup commit and the validate_bucket_layout review thread),
- * fixes offsets as prefix sums inside each order's table, and checks every
- * table against its prime sum (fewer rows -> ENGRAM_E_LAYOUT_ROWS, more rows
- * allowed, as that review thread proposes).  Host only: no HIP call.
+/* Creates the layout: draws the bucket primes (site by site, for each order,
+ * for each head, the smallest prime at or above the floor not yet drawn,
+ * [VeOmni#1370] n-gram memory lookup commit and the validate_bucket_layout
+ * review thread), fixes offsets as prefix sums inside each table, and checks
+ * every table against its prime sum (fewer rows -> ENGRAM_E_LAYOUT_ROWS, more
+ * rows allowed, as that review thread proposes).  Host only: no HIP call.
  * Errors: ENGRAM_E_ARG, ENGRAM_E_LAYOUT_ROWS, ENGRAM_E_VC_RANGE, ENGRAM_E_NOFIT,
- * ENGRAM_E_ALIGN (pitch).  On success *out owns host memory freed by destroy. */
+ * ENGRAM_E_ALIGN (pitch; D not a multiple of 32 with block scales).  On success
+ * *out owns host memory freed by destroy. */
 int engram_layout_create(const engram_layout_desc* desc, engram_layout** out);
 void engram_layout_destroy(engram_layout* layout);
 int engram_layout_query(const engram_layout* layout, engram_layout_info* info);
@@ -184,10 +221,11 @@ int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid,
  *           dead token's own window is all PAD; positions before a continuing
  *           sequence are read from its store slot;
  *   key_n = sum_{j<n} w_j * V_c^j (exact in 64 bits), n = 2, 3, 4;
- *   row_ids[t][n-2][h] = offsets[n][h] + key_n mod primes[n][h]
- *           ([NeMo-V41] DeepseekV41Block.forward: logical memory rows
- *           [batch, sequence, hash_heads]; [vLLM-V41] forward: one hash pass
- *           over the flattened batch).
+ *   row_ids[t][site][n-2][h] = offsets[site][n][h] + key_n mod primes[site][n][h]
+ *           for every site of the layout in the same pass ([NeMo-V41]
+ *           DeepseekV41Block.forward: logical memory rows [batch, sequence,
+ *           hash_heads]; [vLLM-V41] forward: one hash pass over the flattened
+ *           batch, each layer reading its columns through layer_hash_index).
  * After the call, each sequence with a slot leaves its last three window ids
  * (oldest first) in the store; an empty sequence that starts here leaves PAD.
  * Arguments:
@@ -200,7 +238,7 @@ int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid,
  *   d_store     int32 [num_slots][3] or NULL
  *   d_dead      uint8 [T] or NULL (= no dead position)
  *   d_eids      int32 [T] out: e_t
- *   d_row_ids   int32 [T][3][H] out
+ *   d_row_ids   int32 [T][num_sites][3][H] out
  * Host errors: ENGRAM_E_ARG.  Device errors: ENGRAM_E_TOKEN_RANGE,
  * ENGRAM_E_SEQLENS, ENGRAM_E_SLOT_RANGE, ENGRAM_E_NEED_STORE. */
 int engram_compress_hash(const engram_layout* layout, const int32_t* d_tid2eid,
@@ -210,26 +248,33 @@ int engram_compress_hash(const engram_layout* layout, const int32_t* d_tid2eid,
                          int32_t* d_eids, int32_t* d_row_ids, hipStream_t stream);
 
 /* ---- 2. gather + dequant -------------------------------------------------- */
-/* For each token t, order n, head h, element d < D:
- *   out[t][(n*H + h)*seg_pitch + d] = fp32(q * scale_n[row]) rounded to
- *   out_dtype, q = e4m3fn value of table_n[row][d], row = row_ids[t][n][h]
- *   ([VeOmni#1370] PR summary: native FP8 row-wise dequantization on lookup).
- *   BF16 tables carry no scale and are copied (or widened to fp32).
- *   Elements d in [D, seg_pitch) of every segment are written as zero.
+/* For each token t, order n, head h, element d < D of site `site`:
+ *   out[t][(n*H + h)*seg_pitch + d] = fp32(q * scale) rounded to out_dtype,
+ *   q = e4m3fn value of table[row][d], row = row_ids[t][site][n][h], scale =
+ *   the row's fp32 scale or the e8m0 exponent of its block d / 32 ([VeOmni#1370]
+ *   PR summary: native FP8 row-wise dequantization on lookup; per-row-scale
+ *   commit: (1, 32) blocks).  BF16 tables carry no scale and are copied (or
+ *   widened to fp32).  Elements d in [D, seg_pitch) of every segment are
+ *   written as zero.
  * Arguments:
- *   d_tables   host array of 3 device pointers, table_n uint8 [rows_n][pitch],
- *              16-byte aligned
- *   d_scales   host array of 3 device pointers to float [rows_n] (fp8 tables),
- *              or NULL (bf16 tables)
- *   d_row_ids  int32 [T][3][H], as written by engram_compress_hash
+ *   d_tables   host array of 3 device pointers (TABLES_PER_ORDER: the site's
+ *              order-n table uint8 [rows[n]][pitch]; TABLE_PER_SITE: entry 0 is
+ *              the site's table [rows[0]][pitch], entries 1, 2 ignored), 16-byte
+ *              aligned
+ *   d_scales   host array of 3 device pointers, same tables: float [rows] for
+ *              ROW_F32 scales, uint8 [rows][D/32] e8m0 bytes for BLOCK32 scales;
+ *              NULL for bf16 tables
+ *   d_row_ids  int32 [T][num_sites][3][H], as written by engram_compress_hash
+ *   site       0 .. num_sites-1: whose columns (and tables) this call gathers
  *   out_dtype  ENGRAM_DTYPE_BF16 (hot path) or ENGRAM_DTYPE_F32 (exact check)
  *   d_out      [T][out_ld] of out_dtype, 16-byte aligned; out_ld >= k_pad and a
  *              multiple of 8
  * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN.  Device error: ENGRAM_E_ROW_RANGE
  * (that segment is written as zero). */
 int engram_gather_dequant(const engram_layout* layout, const void* const* d_tables,
-                          const float* const* d_scales, const int32_t* d_row_ids, int32_t T,
-                          int32_t out_dtype, void* d_out, int64_t out_ld, hipStream_t stream);
+                          const void* const* d_scales, const int32_t* d_row_ids, int32_t site,
+                          int32_t T, int32_t out_dtype, void* d_out, int64_t out_ld,
+                          hipStream_t stream);
 
 /* ---- 3. projection + gated residual ---------------------------------------- */
 /* v[t][o] = sum_{k < k_pad} rows[t][k] * W[o][k], bf16 x bf16 accumulated in
@@ -252,15 +297,16 @@ int engram_project(const engram_layout* layout, const void* d_rows, int64_t rows
  * config commit), built tile by tile in on-chip memory and never stored.
  * Same accumulation order as engram_project, so v matches the two-call path bit
  * for bit.
- *   d_tables, d_scales, d_row_ids as for engram_gather_dequant; the layout's
- *   row_pitch_bytes must be >= seg_pitch and a multiple of 16 (a row is read in
- *   64-byte pieces up to seg_pitch; bytes past D are ignored).
+ *   d_tables, d_scales, d_row_ids, site as for engram_gather_dequant; the
+ *   layout's row_pitch_bytes must be >= seg_pitch and a multiple of 16 (a row is
+ *   read in 64-byte pieces up to seg_pitch; bytes past D are ignored).
  *   d_w, w_ld, hidden, d_v as for engram_project.
- * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN, ENGRAM_E_UNSUPPORTED (bf16
- * tables).  Device error: ENGRAM_E_ROW_RANGE (that segment contributes zero). */
+ * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN, ENGRAM_E_UNSUPPORTED (bf16 tables,
+ * BLOCK32 scales).  Device error: ENGRAM_E_ROW_RANGE (that segment contributes
+ * zero). */
 int engram_gather_project(const engram_layout* layout, const void* const* d_tables,
-                          const float* const* d_scales, const int32_t* d_row_ids, int32_t T,
-                          const void* d_w, int64_t w_ld, int32_t hidden, float* d_v,
+                          const void* const* d_scales, const int32_t* d_row_ids, int32_t site,
+                          int32_t T, const void* d_w, int64_t w_ld, int32_t hidden, float* d_v,
                           hipStream_t stream);
 
 /* For each token t and stream s < hc_mult:

@@ -73,6 +73,10 @@ def lib():
         L.oracle_dequant_rows.argtypes = [P, P, i64, i64, i32, P, P]
         L.oracle_project.argtypes = [P, P, i64, i64, i64, P]
         L.oracle_gate_add.argtypes = [P, P, P, i64, i64, i64, P, P]
+        L.oracle_site_layout.argtypes = [i32, i32, u64, i32, P, P]
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_decode.restype = ctypes.c_double
+        L.oracle_dequant_rows_block32.argtypes = [P, P, i64, i64, P, P]
         _lib = L
     return _lib
 
@@ -124,6 +128,18 @@ def layout_at_floor(rows, n_heads: int, floor_: int) -> OracleLayout:
     _check(lib().oracle_layout_at_floor(_ptr(rows), n_heads, floor_, _ptr(primes), _ptr(offs)),
            "layout_at_floor")
     return OracleLayout(int(floor_), primes.reshape(3, n_heads), offs.reshape(3, n_heads))
+
+
+def site_layouts(n_sites: int, n_heads: int, floor_: int, per_site_table: bool) -> list:
+    """One OracleLayout per site of a shared hash pass (site s draws its primes
+    after sites 0..s-1)."""
+    primes = np.zeros(n_sites * 3 * n_heads, dtype=np.uint64)
+    offs = np.zeros(n_sites * 3 * n_heads, dtype=np.uint64)
+    _check(lib().oracle_site_layout(n_sites, n_heads, floor_, 1 if per_site_table else 0,
+                                    _ptr(primes), _ptr(offs)), "site_layout")
+    p = primes.reshape(n_sites, 3, n_heads)
+    o = offs.reshape(n_sites, 3, n_heads)
+    return [OracleLayout(int(floor_), p[s].copy(), o[s].copy()) for s in range(n_sites)]
 
 
 def _opt(a, dtype):
@@ -178,6 +194,24 @@ def dequant_rows(rows, scales, *, bf16_table: bool = False):
     rc = lib().oracle_dequant_rows(_ptr(raw), _ptr(sc), n, D, 1 if bf16_table else 0,
                                    _ptr(f32), _ptr(b16))
     _check(rc, "dequant_rows")
+    return f32, b16
+
+
+def e8m0_decode(b: int) -> float:
+    return float(lib().oracle_e8m0_decode(b))
+
+
+def dequant_rows_block32(rows, scales):
+    """rows: uint8 [n][D] e4m3fn bytes; scales: uint8 [n][D/32] e8m0 bytes.
+    Returns (f32 [n][D], bf16 bits uint16 [n][D])."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    n, D = rows.shape
+    assert sc.shape == (n, D // 32)
+    f32 = np.zeros((n, D), dtype=np.float32)
+    b16 = np.zeros((n, D), dtype=np.uint16)
+    _check(lib().oracle_dequant_rows_block32(_ptr(rows), _ptr(sc), n, D, _ptr(f32), _ptr(b16)),
+           "dequant_rows_block32")
     return f32, b16
 
 

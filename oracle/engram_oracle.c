@@ -87,6 +87,32 @@ int oracle_layout_at_floor(const uint64_t rows[3], int n_heads, uint64_t floor_,
   return sums_fit(primes_out, n_heads, rows) ? ORC_OK : ORC_E_ROWS;
 }
 
+/* Layout of the Engram sites that share one hash pass: site s takes the 3H
+ * primes drawn after sites 0..s-1 ([vLLM-V41] DeepseekV4Model.forward: one
+ * gather of hashes feeds every layer, each reading its columns through
+ * layer_hash_index; [VeOmni#1370] n-gram memory lookup commit: the two
+ * layers' tables hold 384,006,168 and 384,016,682 rows).  per_site_table = 1:
+ * one table per site, each bucket starting where the previous (order, head)
+ * bucket of the site ended; 0: one table per order, offsets restarting at 0. */
+int oracle_site_layout(int n_sites, int n_heads, uint64_t floor_, int per_site_table,
+                       uint64_t *primes_out, uint64_t *offsets_out) {
+  if (n_sites < 1 || n_heads < 1 || !primes_out || !offsets_out) return ORC_E_ARG;
+  int rc = oracle_draw_primes(n_sites, 4, n_heads, floor_, primes_out);
+  if (rc) return rc;
+  for (int s = 0; s < n_sites; ++s) {
+    uint64_t acc = 0;
+    for (int t = 0; t < 3; ++t) {
+      if (!per_site_table) acc = 0;
+      for (int h = 0; h < n_heads; ++h) {
+        const int c = (s * 3 + t) * n_heads + h;
+        offsets_out[c] = acc;
+        acc += primes_out[c];
+      }
+    }
+  }
+  return ORC_OK;
+}
+
 /* Three per-order tables of given row counts: the largest floor whose draw fits
  * every table (reading of the pages' one-table-per-layer layout split at the
  * order boundaries). */
@@ -288,6 +314,37 @@ int oracle_dequant_rows(const uint8_t *rows, const float *scales, int64_t n, int
         const float s = scales[r];
         e = q * s;
       }
+      if (out_f32) out_f32[r * D + d] = e;
+      if (out_bf16) out_bf16[r * D + d] = oracle_bf16_rne((double)e);
+    }
+  }
+  return rc;
+}
+
+/* OCP MX E8M0 scale byte: an unsigned exponent with bias 127, value
+ * 2^(b - 127); 0xFF is NaN; there is no zero and no sign.  [VeOmni#1370]
+ * per-row-scale commit: the released tables carry one such exponent per row
+ * per 32 columns. */
+double oracle_e8m0_decode(uint8_t b) {
+  if (b == 0xFF) return NAN;
+  return ldexp(1.0, (int)b - 127);
+}
+
+/* Dequant with (1, 32) blocks: element d of row r is fp32(q * s) with s the
+ * fp32 value of the e8m0 byte scales[r][d / 32] (2^-127 is an fp32 subnormal,
+ * so every byte but 0xFF is exact) and one IEEE multiply, then one round to
+ * bf16. */
+int oracle_dequant_rows_block32(const uint8_t *rows, const uint8_t *scales, int64_t n, int64_t D,
+                                float *out_f32, uint16_t *out_bf16) {
+  if (n < 0 || D < 0 || D % 32 != 0 || (n > 0 && D > 0 && (!rows || !scales))) return ORC_E_ARG;
+  const int64_t nblk = D / 32;
+  int rc = ORC_OK;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t d = 0; d < D; ++d) {
+      const float q = oracle_e4m3fn_decode(rows[r * D + d]);
+      if (isnan(q)) rc = ORC_E_NAN;
+      const float s = (float)oracle_e8m0_decode(scales[r * nblk + d / 32]);
+      const float e = q * s;
       if (out_f32) out_f32[r * D + d] = e;
       if (out_bf16) out_bf16[r * D + d] = oracle_bf16_rne((double)e);
     }

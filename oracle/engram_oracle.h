@@ -81,6 +81,12 @@ int oracle_compress_hash(int64_t vocab, int64_t vc, int64_t pad_token_id, int n_
                          const int32_t *slots, int32_t *store, int64_t num_slots,
                          const uint8_t *dead, int32_t *eids, int32_t *row_ids);
 
+/* Primes [site][order][head] and bucket offsets of n_sites sites sharing one hash
+ * pass (site s draws after sites 0..s-1); per_site_table selects one table per
+ * site (offsets run across its orders) or one table per order (offsets restart). */
+int oracle_site_layout(int n_sites, int n_heads, uint64_t floor_, int per_site_table,
+                       uint64_t *primes_out, uint64_t *offsets_out);
+
 /* Decode one OCP e4m3fn byte to its exact value (NaN for 0x7F / 0xFF). */
 float oracle_e4m3fn_decode(uint8_t b);
 
@@ -93,6 +99,14 @@ uint16_t oracle_bf16_rne(double x);
  * (2 bytes each, little endian) and are widened exactly. */
 int oracle_dequant_rows(const uint8_t *rows, const float *scales, int64_t n, int64_t D,
                         int is_bf16_table, float *out_f32, uint16_t *out_bf16);
+
+/* Value of an OCP MX e8m0 scale byte: 2^(b - 127), NaN for 0xFF. */
+double oracle_e8m0_decode(uint8_t b);
+
+/* Dequantize n rows of D e4m3fn bytes with (1, 32) e8m0 block scales
+ * (scales [n][D/32]): out_f32 = fp32(q * 2^(b-127)), out_bf16 = RNE_bf16(out_f32). */
+int oracle_dequant_rows_block32(const uint8_t *rows, const uint8_t *scales, int64_t n, int64_t D,
+                                float *out_f32, uint16_t *out_bf16);
 
 /* Down-projection v[t][o] = sum_k E[t][k] * W[o][k] in fp64 (E, W given as bf16). */
 int oracle_project(const uint16_t *E, const uint16_t *W, int64_t T, int64_t K,

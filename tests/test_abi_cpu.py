@@ -125,7 +125,11 @@ def test_gather_host_argument_errors_need_no_device():
     lib = eng._lib
     P = ctypes.c_void_p
     three = (P * 3)(None, None, None)
-    rc = lib.engram_gather_dequant(L.handle, three, three, None, 4, 99, None, L.info.k_pad, None)
+    rc = lib.engram_gather_dequant(L.handle, three, three, None, 0, 4, 99, None, L.info.k_pad, None)
+    assert rc == eng.ENGRAM_E_ARG
+    # a site the layout does not have
+    rc = lib.engram_gather_dequant(L.handle, three, three, None, 1, 4, eng.ENGRAM_DTYPE_BF16, None,
+                                   L.info.k_pad, None)
     assert rc == eng.ENGRAM_E_ARG
     rc = lib.engram_project(L.handle, None, L.info.k_pad, None, L.info.k_pad, 0, None, 4, None)
     assert rc == eng.ENGRAM_E_ARG
@@ -149,26 +153,26 @@ def test_gather_project_host_errors_need_no_device():
     some = (P * 3)(P(256), P(256), P(256))
     # bf16 tables: the fused kernel dequantises e4m3fn only
     L16 = _layout(cfg, table_dtype=eng.ENGRAM_DTYPE_BF16, row_pitch_bytes=2 * cfg.row_dim)
-    rc = lib.engram_gather_project(L16.handle, some, some, P(256), 4, P(256), L16.info.k_pad,
+    rc = lib.engram_gather_project(L16.handle, some, some, P(256), 0, 4, P(256), L16.info.k_pad,
                                    cfg.hidden, P(256), None)
     assert rc == eng.ENGRAM_E_UNSUPPORTED
     # a row pitch shorter than the 64-aligned segment would read past the row
     Lshort = _layout(cfg, row_dim=100, row_pitch_bytes=112)
     assert Lshort.info.seg_pitch == 128
-    rc = lib.engram_gather_project(Lshort.handle, some, some, P(256), 4, P(256), Lshort.info.k_pad,
+    rc = lib.engram_gather_project(Lshort.handle, some, some, P(256), 0, 4, P(256), Lshort.info.k_pad,
                                    cfg.hidden, P(256), None)
     assert rc == eng.ENGRAM_E_ALIGN
     L = _layout(cfg)
     # weight leading dimension below k_pad
-    rc = lib.engram_gather_project(L.handle, some, some, P(256), 4, P(256), L.info.k_pad - 8,
+    rc = lib.engram_gather_project(L.handle, some, some, P(256), 0, 4, P(256), L.info.k_pad - 8,
                                    cfg.hidden, P(256), None)
     assert rc == eng.ENGRAM_E_ALIGN
     # missing scales
-    rc = lib.engram_gather_project(L.handle, some, None, P(256), 4, P(256), L.info.k_pad,
+    rc = lib.engram_gather_project(L.handle, some, None, P(256), 0, 4, P(256), L.info.k_pad,
                                    cfg.hidden, P(256), None)
     assert rc == eng.ENGRAM_E_ARG
     # empty call is a no-op
-    assert lib.engram_gather_project(L.handle, some, some, None, 0, None, L.info.k_pad,
+    assert lib.engram_gather_project(L.handle, some, some, None, 0, 0, None, L.info.k_pad,
                                      cfg.hidden, None, None) == 0
 
 
@@ -191,3 +195,58 @@ def test_store_rollback_host_errors_need_no_device():
     rc = lib.engram_store_rollback(L.handle, P(256), P(256), 4, P(256), 2, P(256), 4, P(256), None,
                                    P(256), None, P(256), None)
     assert rc == eng.ENGRAM_E_ARG
+
+
+def test_multi_site_layout_matches_oracle_and_pages(golden):
+    """Two sites, 8 heads, floor 16,000,000, one table per site: the product's
+    primes and offsets equal the oracle's, and each site's table size is the
+    row count the pages print."""
+    g = golden["engram_num_embeddings"]
+    floor_, H = g["args"]["floor"], g["heads_reading"]
+    rows = max(g["value"])
+    args = dict(vocab_size=129280, compressed_vocab=65536, pad_token_id=129279, heads_per_order=H,
+                rows=[rows, 0, 0], row_dim=256, table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN,
+                row_pitch_bytes=256, hash_floor=floor_, num_sites=2,
+                table_split=eng.ENGRAM_TABLE_PER_SITE, scale_layout=eng.ENGRAM_SCALE_BLOCK32_E8M0)
+    L = eng.engram_layout_create(**args)
+    info = L.info
+    assert info.num_sites == 2 and info.k_pad == 24 * 256
+    assert [info.site_rows(s) for s in range(2)] == g["value"]
+    ref = oracle.site_layouts(2, H, floor_, True)
+    for s in range(2):
+        assert np.array_equal(np.array(info.site_primes[s], dtype=np.uint64), ref[s].primes)
+        assert np.array_equal(np.array(info.site_offsets[s], dtype=np.uint64), ref[s].offsets)
+    # one row short of the second site's buckets
+    with pytest.raises(eng.EngramError) as e:
+        eng.engram_layout_create(**{**args, "rows": [rows - 1, 0, 0]})
+    assert e.value.status == eng.ENGRAM_E_LAYOUT_ROWS
+    # block scales need D % 32 == 0
+    with pytest.raises(eng.EngramError) as e:
+        eng.engram_layout_create(**{**args, "row_dim": 250})
+    assert e.value.status == eng.ENGRAM_E_ALIGN
+    # per-order tables, three sites: offsets restart per order, as the oracle's
+    L3 = eng.engram_layout_create(vocab_size=129280, compressed_vocab=65536, pad_token_id=129279,
+                                  heads_per_order=2, rows=[10_000] * 3, row_dim=128,
+                                  table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN, row_pitch_bytes=128,
+                                  hash_floor=64, num_sites=3)
+    ref3 = oracle.site_layouts(3, 2, 64, False)
+    for s in range(3):
+        assert np.array_equal(np.array(L3.info.site_primes[s], dtype=np.uint64), ref3[s].primes)
+        assert np.array_equal(np.array(L3.info.site_offsets[s], dtype=np.uint64), ref3[s].offsets)
+    with pytest.raises(eng.EngramError) as e:
+        eng.engram_layout_create(**{**args, "num_sites": 5})
+    assert e.value.status == eng.ENGRAM_E_ARG
+
+
+def test_multi_site_fit_is_largest_floor():
+    """With no floor given, the fitted floor is the largest at which every site's
+    buckets fit, and one floor above it does not fit (oracle draw)."""
+    rows = 50_000
+    L = eng.engram_layout_create(vocab_size=16, compressed_vocab=8, pad_token_id=15, heads_per_order=2,
+                                 rows=[rows, 0, 0], row_dim=64, table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN,
+                                 row_pitch_bytes=64, num_sites=2, table_split=eng.ENGRAM_TABLE_PER_SITE)
+    f = L.info.hash_floor
+
+    def fits(fl):
+        return all(int(l.primes.sum()) <= rows for l in oracle.site_layouts(2, 2, fl, True))
+    assert fits(f) and not fits(f + 1)

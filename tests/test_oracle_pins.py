@@ -527,3 +527,82 @@ def test_gate_matches_expit_closed_form():
     got = bits_to_f64(y)
     # one bf16 rounding of the fp64 value: within half an ulp (2^-9 relative)
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# sites sharing one hash pass; (1, 32) e8m0 block scales
+# ---------------------------------------------------------------------------
+
+def test_site_layout_released_tables(golden):
+    """One table per site: each site's last bucket ends at its table's row count,
+    which the pages print (384,006,168 / 384,016,682)."""
+    g = golden["engram_num_embeddings"]
+    L = oracle.site_layouts(g["args"]["layers"], g["heads_reading"], g["args"]["floor"], True)
+    ends = [int(l.offsets[2, -1] + l.primes[2, -1]) for l in L]
+    assert ends == g["value"]
+    for l in L:
+        flat_p = l.primes.reshape(-1).astype(np.int64)
+        flat_o = l.offsets.reshape(-1).astype(np.int64)
+        assert flat_o[0] == 0
+        assert np.array_equal(flat_o[1:], np.cumsum(flat_p)[:-1])  # buckets back to back
+    # site 1 draws after site 0: every prime larger, none shared
+    assert L[1].primes.min() > L[0].primes.max()
+
+
+def test_site_layout_per_order_tables_restart_offsets():
+    L = oracle.site_layouts(3, 2, 64, False)
+    p = oracle.draw_primes(3, 4, 2, 64)
+    for s, l in enumerate(L):
+        assert np.array_equal(l.primes, p[s])
+        assert (l.offsets[:, 0] == 0).all()
+        assert np.array_equal(l.offsets[:, 1], l.primes[:, 0])
+    # one site is the single-site layout at the same floor
+    one = oracle.layout_at_floor([10_000] * 3, 2, 64)
+    assert np.array_equal(L[0].primes, one.primes) and np.array_equal(L[0].offsets, one.offsets)
+
+
+def test_e8m0_decode_closed_forms():
+    assert oracle.e8m0_decode(127) == 1.0
+    assert oracle.e8m0_decode(128) == 2.0
+    assert oracle.e8m0_decode(120) == 2.0 ** -7
+    assert oracle.e8m0_decode(254) == 2.0 ** 127
+    assert oracle.e8m0_decode(0) == 2.0 ** -127
+    assert math.isnan(oracle.e8m0_decode(255))
+
+
+def test_dequant_block32_against_torch_float8():
+    """fp32(e4m3fn(q) * e8m0(b)) and its bf16 rounding against torch's own
+    float8_e4m3fn / float8_e8m0fnu conversions and an fp32 multiply, over every
+    e4m3 code, with a different exponent in every 32-element block (including
+    the subnormal 2^-127 scale and the largest ones)."""
+    import torch
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    D = 256
+    n = 12
+    rng = np.random.default_rng(3)
+    rows = rng.choice(codes, size=(n, D)).astype(np.uint8)
+    rows[0, :len(codes)] = codes  # every finite code once
+    scales = rng.integers(100, 140, size=(n, D // 32)).astype(np.uint8)
+    scales[1] = [0, 1, 2, 127, 128, 200, 253, 254]
+    scales[2] = [0] * (D // 32)
+    rows[2] = codes[np.arange(D) % len(codes)]
+    f32, b16 = oracle.dequant_rows_block32(rows, scales)
+    q = torch.from_numpy(rows).view(torch.float8_e4m3fn).float()
+    s = torch.from_numpy(scales).view(torch.float8_e8m0fnu).float()
+    ref = q * s.repeat_interleave(32, dim=1)
+    assert np.array_equal(f32.view(np.uint32), ref.numpy().view(np.uint32))
+    ref16 = ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16, ref16)
+
+
+def test_dequant_block32_uniform_blocks_equal_row_scale():
+    """With the same exponent in every block, block dequant equals the per-row
+    scale path at scale 2^(b-127)."""
+    rng = np.random.default_rng(4)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    rows = rng.choice(codes, size=(6, 64)).astype(np.uint8)
+    b = np.array([90, 110, 120, 127, 130, 160], dtype=np.uint8)
+    f_blk, b_blk = oracle.dequant_rows_block32(rows, np.repeat(b[:, None], 2, axis=1))
+    f_row, b_row = oracle.dequant_rows(rows, (2.0 ** (b.astype(np.float64) - 127)).astype(np.float32))
+    assert np.array_equal(f_blk.view(np.uint32), f_row.view(np.uint32))
+    assert np.array_equal(b_blk, b_row)
