@@ -182,6 +182,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step in a HIP graph and time K replays; value = graph rate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-alt-paths", action="store_true",
+                    help="skip the fused-path comparison after the timed steps (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
@@ -379,7 +381,8 @@ def main():
         result["ms_per_step"] = g_ms
         result["config"]["hip_graph"] = True
         del g
-    if args.path == "split" and cfg.table_dtype == "fp8" and NS == 1 and not cfg.scale_block:
+    if (args.path == "split" and cfg.table_dtype == "fp8" and NS == 1 and not cfg.scale_block
+            and not args.no_alt_paths):
         # the other path on the same inputs, outside the timed region: the fused
         # gather + projection against gather_dequant + project
         v_alt = torch.empty_like(site.v)
