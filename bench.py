@@ -181,6 +181,11 @@ def main():
                     help="split: gather_dequant + project (default, faster); fused: gather_project")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step in a HIP graph and time K replays; value = graph rate")
+    ap.add_argument("--host-tables", action="store_true",
+                    help="keep the tables in pinned host memory (read over the host link)")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="also time the pipelined loop: hash + gather of step i+1 on a prefetch "
+                         "stream while step i projects and gates; value = pipelined rate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alt-paths", action="store_true",
                     help="skip the fused-path comparison after the timed steps (profiler runs)")
@@ -217,6 +222,16 @@ def main():
     site_tables = [ei.make_tables(cfg, dev, site=s) for s in range(NS)]
     weights = [ei.make_weight(cfg, dev, site=s) for s in range(NS)]
     one = NS == 1
+    if args.host_tables:
+        # tables move to pinned host memory; the device copies are dropped
+        for t in site_tables:
+            for lst in (t.data, t.scale):
+                for j in range(len(lst or [])):
+                    h = torch.empty(lst[j].shape, dtype=lst[j].dtype, pin_memory=True)
+                    h.copy_(lst[j])
+                    lst[j] = h
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     site = eng.Engram(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
                       heads_per_order=cfg.heads,
                       rows=[cfg.rows] if cfg.table_split == "site" else [cfg.rows] * 3,
@@ -226,7 +241,8 @@ def main():
                       scales=site_tables[0].scale if one else [t.scale for t in site_tables],
                       weight=weights[0] if one else weights, hidden=cfg.hidden, hc_mult=cfg.hc_mult,
                       max_tokens=T, path=args.path, num_sites=NS, table_split=cfg.table_split,
-                      scale_block=cfg.scale_block, hash_floor=cfg.hash_floor)
+                      scale_block=cfg.scale_block, hash_floor=cfg.hash_floor,
+                      prefetch_slots=2 if args.prefetch else 0)
     site_streams = [ei.make_streams(cfg, T, dev, step=s) for s in range(NS)]
     streams_host = None
     if not args.no_cpu_baseline:
@@ -348,7 +364,8 @@ def main():
                    "table_dtype": cfg.table_dtype, "rows_per_table": cfg.rows, "row_dim": cfg.row_dim,
                    "heads_per_order": cfg.heads, "hidden": cfg.hidden, "hc_mult": cfg.hc_mult,
                    "k_pad": site.info.k_pad, "path": args.path, "sites": NS,
-                   "table_split": cfg.table_split, "scale_block": cfg.scale_block},
+                   "table_split": cfg.table_split, "scale_block": cfg.scale_block,
+                   "tables_in": "pinned host memory" if args.host_tables else "HBM"},
         "roofline": roofline,
         "kernels": kernels,
         "wall_s_timed": wall,
@@ -381,8 +398,40 @@ def main():
         result["ms_per_step"] = g_ms
         result["config"]["hip_graph"] = True
         del g
+    if args.prefetch:
+        # steady state of the prefetch pipeline: step i+1's hash and gathers run on a
+        # stream of their own while step i's projections and gates run on the main one
+        if args.path != "split" or cfg.decode_steps:
+            raise SystemExit("--prefetch applies to the split path of a prefill workload")
+        side = torch.cuda.Stream()
+        main = torch.cuda.current_stream()
+
+        def pipelined(n):
+            pre = site.prefetch(tok, cu, stream=side, seq_start=ss)
+            for i in range(n):
+                nxt = site.prefetch(tok, cu, stream=side, seq_start=ss) if i + 1 < n else None
+                for si in range(NS):
+                    site.apply(pre, si, site_streams[si], stream=main)
+                pre = nxt
+        side.wait_stream(main)
+        pipelined(args.warmup)
+        torch.cuda.synchronize()
+        ps, pe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ps.record()
+        side.wait_stream(main)
+        pipelined(args.steps)
+        main.wait_stream(side)
+        pe.record()
+        torch.cuda.synchronize()
+        eng.check_device_error("prefetch pipeline")
+        p_ms = ps.elapsed_time(pe) / args.steps
+        result["sequential"] = {"value": result["value"], "ms_per_step": result["ms_per_step"]}
+        result["prefetch_pipeline"] = {"value": T / (p_ms * 1e-3), "ms_per_step": p_ms}
+        result["value"] = T / (p_ms * 1e-3)
+        result["ms_per_step"] = p_ms
+        result["config"]["prefetch_stream"] = True
     if (args.path == "split" and cfg.table_dtype == "fp8" and NS == 1 and not cfg.scale_block
-            and not args.no_alt_paths):
+            and not args.no_alt_paths and not args.host_tables):
         # the other path on the same inputs, outside the timed region: the fused
         # gather + projection against gather_dequant + project
         v_alt = torch.empty_like(site.v)

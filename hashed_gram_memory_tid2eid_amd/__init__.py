@@ -120,6 +120,7 @@ _sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _
 _sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
 _sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
+_sig("engram_host_device_pointer", [_P, ctypes.POINTER(_P)])
 _sig("engram_get_error", [_P])
 _sig("engram_last_hip_error", [], ctypes.c_char_p)
 
@@ -151,18 +152,27 @@ def _need(cond: bool, what: str):
         raise ValueError(what)
 
 
-def _dev(t, dtype=None, name="tensor"):
-    """Device pointer of a contiguous CUDA tensor (or None)."""
+def _dev(t, dtype=None, name="tensor", host_ok=False):
+    """Device pointer of a contiguous CUDA tensor (or None).  With host_ok, a pinned
+    host tensor is accepted too and its device-side address is returned (tables
+    kept in host memory are read by the kernels over the host link)."""
     if t is None:
         return None
     import torch
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a device tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return t.data_ptr()
+    if t.is_cuda:
+        return t.data_ptr()
+    if host_ok and t.is_pinned():
+        dp = _P()
+        _check(_lib.engram_host_device_pointer(_P(t.data_ptr()), ctypes.byref(dp)),
+               f"{name}: device address of pinned host memory")
+        return dp.value
+    raise TypeError(f"{name} must be a device tensor" + (" or pinned host tensor" if host_ok else ""))
 
 
 # ---------------------------------------------------------------------------
@@ -350,7 +360,7 @@ def _site_pointers(layout: Layout, tables: Sequence, scales: Optional[Sequence])
     pitch = layout.desc.row_pitch_bytes
     for n in range(used):
         _need(tables[n].numel() >= info.rows[n] * pitch, f"table {n} smaller than rows x pitch")
-    tp = (_P * 3)(*[_dev(tables[min(n, used - 1)], torch.uint8, "table") for n in range(3)])
+    tp = (_P * 3)(*[_dev(tables[min(n, used - 1)], torch.uint8, "table", host_ok=True) for n in range(3)])
     if scales is None:
         return tp, None
     _need(len(scales) >= used, f"{used} scale tensor(s) expected")
@@ -360,10 +370,10 @@ def _site_pointers(layout: Layout, tables: Sequence, scales: Optional[Sequence])
         if info.scale_layout == ENGRAM_SCALE_BLOCK32_E8M0:
             _need(sc.numel() >= info.rows[min(n, used - 1)] * (info.row_dim // 32),
                   "e8m0 scales must be [rows][D/32]")
-            sp.append(_dev(sc, torch.uint8, "scale"))
+            sp.append(_dev(sc, torch.uint8, "scale", host_ok=True))
         else:
             _need(sc.numel() >= info.rows[min(n, used - 1)], "scales smaller than rows")
-            sp.append(_dev(sc, torch.float32, "scale"))
+            sp.append(_dev(sc, torch.float32, "scale", host_ok=True))
     return tp, (_P * 3)(*sp)
 
 

@@ -157,6 +157,20 @@ extern "C" int engram_compress_hash(const engram_layout* L, const int32_t* d_tid
 
 // ---- 2. gather + dequant -------------------------------------------------------
 
+// Workgroups of a gather whose tables live in host memory: enough requests in
+// flight to fill the host link (~64 KB per workgroup), few enough CUs to leave the
+// others free.
+constexpr int kHostGatherBlocks = 64;
+
+static bool in_host_memory(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // unknown to HIP: not pinned host memory
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost;
+}
+
 // Resolves the tables and scales one gather reads: the site's three order
 // tables, or its one table (entry 0) repeated for every order.
 static int site_tables(const engram_layout* L, const void* const* d_tables,
@@ -206,6 +220,12 @@ extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* 
   g.seg_pitch = (int32_t)L->seg_pitch;
   g.bf16_table = bf16_table ? 1 : 0;
   g.f32_out = out_dtype == ENGRAM_DTYPE_F32 ? 1 : 0;
+  // Tables in host memory: the host link bounds the gather long before the CUs do,
+  // so it runs as a grid-stride kernel on a few workgroups and leaves the rest of the
+  // chip to work overlapping it (the next projection, on another stream).
+  g.max_blocks = 0;
+  for (int n = 0; n < 3; ++n)
+    if (in_host_memory(g.table[n])) g.max_blocks = kHostGatherBlocks;
   const size_t out_elt = out_dtype == ENGRAM_DTYPE_F32 ? 4 : 2;
   g.out_ld = out_ld;
   // one launch covers fewer than 2^31 output chunks; split bigger calls by tokens
@@ -324,3 +344,9 @@ extern "C" int engram_get_error(hipStream_t stream) {
 }
 
 extern "C" const char* engram_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
+
+extern "C" int engram_host_device_pointer(const void* host, void** dev) {
+  if (!host || !dev) return ENGRAM_E_ARG;
+  *dev = nullptr;
+  return hip_status(hipHostGetDevicePointer(dev, const_cast<void*>(host), 0));
+}

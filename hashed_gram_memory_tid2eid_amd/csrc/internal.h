@@ -98,6 +98,7 @@ struct GatherArgs {
   int32_t T, heads, cols, row_dim, seg_pitch;
   int32_t bf16_table;      // 0: e4m3fn + fp32 scale, 1: bf16
   int32_t f32_out;         // 0: bf16 out, 1: fp32 out
+  int32_t max_blocks;      // > 0: at most this many workgroups (grid-stride), 0: one per block
 };
 hipError_t launch_gather_dequant(const GatherArgs& a, hipStream_t stream);
 

@@ -84,128 +84,133 @@ __device__ __forceinline__ float e8m0_value(uint32_t b) {
 
 template <bool kBf16Table, bool kF32Out, bool kBlockScale>
 __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKArgs a) {
-  const uint32_t first = blockIdx.x * (kGatherThreads * kGatherUnroll) + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // Per-wave LDS staging for the bf16 path: a lane converts 16 elements (32 B),
   // the wave's 64 chunks (2 KB) go to LDS and come back transposed so that each
   // of the two wave-wide 16-byte stores writes 1 KB of consecutive output.
   __shared__ u32x4 stage[kGatherThreads / 64][2][128];
   const bool staged = !kF32Out && a.linear_out;
+  // Grid-stride over blocks of kGatherThreads * kGatherUnroll chunks: one block per
+  // workgroup normally; a capped grid (tables in host memory) walks several.
+  const uint32_t per_block = kGatherThreads * kGatherUnroll;
+  for (uint32_t base = blockIdx.x * per_block; base < a.total; base += gridDim.x * per_block) {
+    const uint32_t first = base + threadIdx.x;
 
-  u32x4 raw[kGatherUnroll][kBf16Table ? 2 : 1];
-  float scale[kGatherUnroll];
-  uint32_t tok[kGatherUnroll], seg[kGatherUnroll], chunk[kGatherUnroll];
-  bool live[kGatherUnroll], any[kGatherUnroll];
+    u32x4 raw[kGatherUnroll][kBf16Table ? 2 : 1];
+    float scale[kGatherUnroll];
+    uint32_t tok[kGatherUnroll], seg[kGatherUnroll], chunk[kGatherUnroll];
+    bool live[kGatherUnroll], any[kGatherUnroll];
 
-  // Issue every load first so that UNROLL row reads are in flight per lane.
+    // Issue every load first so that UNROLL row reads are in flight per lane.
 #pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
-    const uint32_t g = first + (uint32_t)u * kGatherThreads;
-    live[u] = g < a.total;
-    any[u] = false;
-    scale[u] = 1.0f;
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const uint32_t g = first + (uint32_t)u * kGatherThreads;
+      live[u] = g < a.total;
+      any[u] = false;
+      scale[u] = 1.0f;
 #pragma unroll
-    for (int h = 0; h < (kBf16Table ? 2 : 1); ++h) raw[u][h] = u32x4{0u, 0u, 0u, 0u};
-    tok[u] = seg[u] = chunk[u] = 0;
-    if (!live[u]) continue;
-    const uint32_t rowidx = fdiv(g, a.div_chunks);  // token * cols + seg
-    chunk[u] = g - rowidx * a.chunks;
-    tok[u] = fdiv(rowidx, a.div_cols);
-    seg[u] = rowidx - tok[u] * a.cols;
-    const uint32_t n = (seg[u] >= a.split) + (seg[u] >= 2 * a.split);
-    if (chunk[u] * 16 >= a.row_dim) continue;  // pure padding: zeros
-    const int32_t row = a.row_ids[(int64_t)rowidx + (int64_t)tok[u] * a.rid_extra];
-    const int32_t rows = n == 0 ? a.r0 : (n == 1 ? a.r1 : a.r2);
-    if (row < 0 || row >= rows) {
-      latch_error(ENGRAM_E_ROW_RANGE);
-      continue;
-    }
-    const uint8_t* tb = n == 0 ? a.t0 : (n == 1 ? a.t1 : a.t2);
-    const uint8_t* src = tb + (int64_t)row * a.pitch + (int64_t)chunk[u] * 16 * (kBf16Table ? 2 : 1);
-    raw[u][0] = *reinterpret_cast<const u32x4*>(src);
-    if (kBf16Table) {
-      raw[u][kBf16Table ? 1 : 0] = *reinterpret_cast<const u32x4*>(src + 16);
-    } else if (kBlockScale) {
-      const uint8_t* sc = static_cast<const uint8_t*>(n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2));
-      scale[u] = e8m0_value(sc[(int64_t)row * a.nblk + (chunk[u] >> 1)]);
-    } else {
-      const float* sc = static_cast<const float*>(n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2));
-      scale[u] = sc[row];
-    }
-    any[u] = true;
-  }
-
-#pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
-    const uint32_t e0 = chunk[u] * 16;
-    const uint32_t valid = e0 >= a.row_dim ? 0u : (a.row_dim - e0 >= 16 ? 16u : a.row_dim - e0);
-    const int64_t obase = (int64_t)tok[u] * a.out_ld + (int64_t)seg[u] * a.seg_pitch + e0;
-
-    float f[16];
-    if (kBf16Table) {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const uint32_t word = raw[u][w >> 2][w & 3];
-        f[2 * w] = __uint_as_float(word << 16);
-        f[2 * w + 1] = __uint_as_float(word & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t word = raw[u][0][w];
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-        f[4 * w + 0] = lo[0] * scale[u];
-        f[4 * w + 1] = lo[1] * scale[u];
-        f[4 * w + 2] = hi[0] * scale[u];
-        f[4 * w + 3] = hi[1] * scale[u];
-      }
-    }
-    if (!any[u]) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] = 0.0f;
-    } else if (valid < 16) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((uint32_t)i >= valid) f[i] = 0.0f;
-    }
-
-    if (kF32Out) {
+      for (int h = 0; h < (kBf16Table ? 2 : 1); ++h) raw[u][h] = u32x4{0u, 0u, 0u, 0u};
+      tok[u] = seg[u] = chunk[u] = 0;
       if (!live[u]) continue;
-      float* dst = reinterpret_cast<float*>(a.out) + obase;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst) + q);
+      const uint32_t rowidx = fdiv(g, a.div_chunks);  // token * cols + seg
+      chunk[u] = g - rowidx * a.chunks;
+      tok[u] = fdiv(rowidx, a.div_cols);
+      seg[u] = rowidx - tok[u] * a.cols;
+      const uint32_t n = (seg[u] >= a.split) + (seg[u] >= 2 * a.split);
+      if (chunk[u] * 16 >= a.row_dim) continue;  // pure padding: zeros
+      const int32_t row = a.row_ids[(int64_t)rowidx + (int64_t)tok[u] * a.rid_extra];
+      const int32_t rows = n == 0 ? a.r0 : (n == 1 ? a.r1 : a.r2);
+      if (row < 0 || row >= rows) {
+        latch_error(ENGRAM_E_ROW_RANGE);
+        continue;
       }
-      continue;
+      const uint8_t* tb = n == 0 ? a.t0 : (n == 1 ? a.t1 : a.t2);
+      const uint8_t* src = tb + (int64_t)row * a.pitch + (int64_t)chunk[u] * 16 * (kBf16Table ? 2 : 1);
+      raw[u][0] = *reinterpret_cast<const u32x4*>(src);
+      if (kBf16Table) {
+        raw[u][kBf16Table ? 1 : 0] = *reinterpret_cast<const u32x4*>(src + 16);
+      } else if (kBlockScale) {
+        const uint8_t* sc = static_cast<const uint8_t*>(n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2));
+        scale[u] = e8m0_value(sc[(int64_t)row * a.nblk + (chunk[u] >> 1)]);
+      } else {
+        const float* sc = static_cast<const float*>(n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2));
+        scale[u] = sc[row];
+      }
+      any[u] = true;
     }
-    u32x4 o[2];
-    if (kBf16Table && any[u] && valid == 16) {
-      o[0] = raw[u][0];
-      o[1] = raw[u][kBf16Table ? 1 : 0];
-    } else {
+
 #pragma unroll
-      for (int w = 0; w < 8; ++w)
-        o[w >> 2][w & 3] = bf16_bits_rne(f[2 * w]) | (bf16_bits_rne(f[2 * w + 1]) << 16);
-    }
-    if (staged) {
-      // chunk g sits at element 16 g of the output (rows are back to back), so the
-      // wave's chunks g0..g0+63 are 2 KB of consecutive output
-      u32x4* buf = stage[wave][u & 1];
-      buf[2 * lane] = o[0];
-      buf[2 * lane + 1] = o[1];
-      const u32x4 s0 = buf[lane], s1 = buf[64 + lane];
-      const uint32_t g0 = first - (uint32_t)lane + (uint32_t)u * kGatherThreads;
-      unsigned short* dst = reinterpret_cast<unsigned short*>(a.out) + (int64_t)g0 * 16;
-      if (g0 + (uint32_t)(lane >> 1) < a.total)
-        __builtin_nontemporal_store(s0, reinterpret_cast<u32x4*>(dst) + lane);
-      if (g0 + 32u + (uint32_t)(lane >> 1) < a.total)
-        __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(dst) + 64 + lane);
-    } else if (live[u]) {
-      unsigned short* dst = reinterpret_cast<unsigned short*>(a.out) + obase;
-      __builtin_nontemporal_store(o[0], reinterpret_cast<u32x4*>(dst));
-      __builtin_nontemporal_store(o[1], reinterpret_cast<u32x4*>(dst) + 1);
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const uint32_t e0 = chunk[u] * 16;
+      const uint32_t valid = e0 >= a.row_dim ? 0u : (a.row_dim - e0 >= 16 ? 16u : a.row_dim - e0);
+      const int64_t obase = (int64_t)tok[u] * a.out_ld + (int64_t)seg[u] * a.seg_pitch + e0;
+
+      float f[16];
+      if (kBf16Table) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const uint32_t word = raw[u][w >> 2][w & 3];
+          f[2 * w] = __uint_as_float(word << 16);
+          f[2 * w + 1] = __uint_as_float(word & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t word = raw[u][0][w];
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+          f[4 * w + 0] = lo[0] * scale[u];
+          f[4 * w + 1] = lo[1] * scale[u];
+          f[4 * w + 2] = hi[0] * scale[u];
+          f[4 * w + 3] = hi[1] * scale[u];
+        }
+      }
+      if (!any[u]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] = 0.0f;
+      } else if (valid < 16) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((uint32_t)i >= valid) f[i] = 0.0f;
+      }
+
+      if (kF32Out) {
+        if (!live[u]) continue;
+        float* dst = reinterpret_cast<float*>(a.out) + obase;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst) + q);
+        }
+        continue;
+      }
+      u32x4 o[2];
+      if (kBf16Table && any[u] && valid == 16) {
+        o[0] = raw[u][0];
+        o[1] = raw[u][kBf16Table ? 1 : 0];
+      } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          o[w >> 2][w & 3] = bf16_bits_rne(f[2 * w]) | (bf16_bits_rne(f[2 * w + 1]) << 16);
+      }
+      if (staged) {
+        // chunk g sits at element 16 g of the output (rows are back to back), so the
+        // wave's chunks g0..g0+63 are 2 KB of consecutive output
+        u32x4* buf = stage[wave][u & 1];
+        buf[2 * lane] = o[0];
+        buf[2 * lane + 1] = o[1];
+        const u32x4 s0 = buf[lane], s1 = buf[64 + lane];
+        const uint32_t g0 = first - (uint32_t)lane + (uint32_t)u * kGatherThreads;
+        unsigned short* dst = reinterpret_cast<unsigned short*>(a.out) + (int64_t)g0 * 16;
+        if (g0 + (uint32_t)(lane >> 1) < a.total)
+          __builtin_nontemporal_store(s0, reinterpret_cast<u32x4*>(dst) + lane);
+        if (g0 + 32u + (uint32_t)(lane >> 1) < a.total)
+          __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(dst) + 64 + lane);
+      } else if (live[u]) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(a.out) + obase;
+        __builtin_nontemporal_store(o[0], reinterpret_cast<u32x4*>(dst));
+        __builtin_nontemporal_store(o[1], reinterpret_cast<u32x4*>(dst) + 1);
+      }
     }
   }
 }
@@ -251,7 +256,9 @@ hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
   a.div_chunks = make_fastdiv(a.chunks);
   a.div_cols = make_fastdiv(a.cols);
   const uint32_t per_block = kGatherThreads * kGatherUnroll;
-  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+  uint64_t blocks = (total + per_block - 1) / per_block;
+  if (g.max_blocks > 0 && blocks > (uint64_t)g.max_blocks) blocks = (uint64_t)g.max_blocks;
+  const dim3 grid((unsigned)blocks);
   const dim3 block(kGatherThreads);
   if (g.bf16_table) {
     if (g.f32_out)

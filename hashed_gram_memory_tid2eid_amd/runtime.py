@@ -50,7 +50,7 @@ class Engram:
                  row_pitch_bytes: int, tid2eid, tables: Sequence, scales: Optional[Sequence],
                  weight, hidden: int, hc_mult: int = 4, max_tokens: int, hash_floor: int = 0,
                  path: str = "split", num_sites: int = 1, table_split: str = "order",
-                 scale_block: int = 0, stream=None):
+                 scale_block: int = 0, prefetch_slots: int = 0, stream=None):
         import torch
         if path not in ("split", "fused"):
             raise ValueError(f"unknown path {path!r}")
@@ -92,6 +92,14 @@ class Engram:
         self.rows = (torch.empty((max_tokens, info.k_pad), dtype=torch.bfloat16, device=dev)
                      if path == "split" else None)
         self.v = torch.empty((max_tokens, hidden), dtype=torch.float32, device=dev)
+        # prefetch ring: slot -> per-site gathered rows, and the event after which the
+        # slot's last reader (apply) is done with it
+        if prefetch_slots and path != "split":
+            raise ValueError("prefetching gathers rows, which the split path alone keeps")
+        self.pre_rows = [[torch.empty((max_tokens, info.k_pad), dtype=torch.bfloat16, device=dev)
+                          for _ in range(num_sites)] for _ in range(prefetch_slots)]
+        self.pre_free = [None] * prefetch_slots
+        self._next_slot = 0
 
     # single-site views
     @property
@@ -150,3 +158,50 @@ class Engram:
         for s in range(self.num_sites):
             self.site_forward(s, per_site[s], T, keep=keep, stream=stream)
         return streams
+
+    # ---- prefetch: gather ahead on a stream of its own ------------------------------
+    def prefetch(self, tokens, cu_seqlens, *, stream, seq_start=None, slots=None, store=None,
+                 dead=None) -> "Prefetched":
+        """Hash and every site's gather of one call, enqueued on ``stream`` (the
+        prefetch stream) into the next slot of the ring; returns the handle that
+        ``apply`` waits on.  The slot is reused only after the apply calls of the
+        call that last filled it (their stream's work up to then) are done."""
+        import torch
+        if not self.pre_rows:
+            raise ValueError("construct with prefetch_slots > 0 to prefetch")
+        T = tokens.numel()
+        if T > self.max_tokens:
+            raise ValueError(f"{T} tokens > max_tokens {self.max_tokens}")
+        slot = self._next_slot
+        self._next_slot = (slot + 1) % len(self.pre_rows)
+        if self.pre_free[slot] is not None:
+            stream.wait_event(self.pre_free[slot])
+        self.hash(tokens, cu_seqlens, seq_start=seq_start, slots=slots, store=store, dead=dead,
+                  stream=stream)
+        for s in range(self.num_sites):
+            engram_gather_dequant(self.layout, self.site_tables[s], self.site_scales[s], self.row_ids,
+                                  self.pre_rows[slot][s], site=s, T=T, stream=stream)
+        ready = torch.cuda.Event()
+        ready.record(stream)
+        self.pre_free[slot] = None
+        return Prefetched(slot=slot, T=T, ready=ready)
+
+    def apply(self, pre: "Prefetched", site: int, streams, *, keep=None, stream=None):
+        """Projection and gate of one site of a prefetched call, on ``stream``
+        (default: the current stream), after the prefetch has landed."""
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream()
+        st.wait_event(pre.ready)
+        engram_gated_residual(self.layout, self.pre_rows[pre.slot][site], self.site_weights[site],
+                              streams, self.v, keep=keep, T=pre.T, stream=st)
+        done = torch.cuda.Event()
+        done.record(st)
+        self.pre_free[pre.slot] = done
+        return streams
+
+
+class Prefetched:
+    """One prefetched call: its ring slot, token count and readiness event."""
+
+    def __init__(self, slot: int, T: int, ready):
+        self.slot, self.T, self.ready = slot, T, ready

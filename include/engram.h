@@ -341,6 +341,15 @@ int engram_get_error(hipStream_t stream);
  * this thread ("hipSuccess" if none); a static string. */
 const char* engram_last_hip_error(void);
 
+/* ---- host-resident tables -------------------------------------------------- */
+/* Tables too large for HBM may live in pinned host memory (hipHostMalloc); the
+ * gather kernels then read their rows over the host link ([vLLM-V41]
+ * DeepseekV4Model.__init__: Engram tables offloaded to the CPU get a prefetch
+ * stream of their own).  Writes to *dev the device-side address of pinned host
+ * memory `host`, to be passed as a table or scale pointer.  Not a hot call.
+ * Errors: ENGRAM_E_ARG, ENGRAM_E_HIP (memory that is not pinned). */
+int engram_host_device_pointer(const void* host, void** dev);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,122 @@
+"""Host-resident tables and the prefetch stream.
+
+Bars: a gather that reads its tables from pinned host memory writes the same
+bytes as one reading the same tables from HBM (fp32 and bf16 outputs, every
+token); a pipeline that hashes and gathers call i+1 on a prefetch stream while
+call i projects and gates on the main stream leaves every call's streams bit for
+bit equal to the plain sequential forward.  (The sequential forward is itself
+checked against the oracle by the parity tests.)
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import engram_inputs as ei
+from engram_harness import DEV, Site, bf16_bits_np, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def eng():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import hashed_gram_memory_tid2eid_amd as e
+    return e
+
+
+def _free():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _pinned_copy(t):
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+def _d(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.mark.parametrize("name", ["prefill", "v41_small"])
+def test_host_resident_tables_equal_device_tables(eng, name):
+    cfg = ei.get_config(name)
+    batch = ei.make_batch(cfg)
+    T = batch.T
+    tid = _d(ei.make_tid2eid(cfg.vocab, cfg.vc))
+    tabs = ei.make_tables(cfg, DEV)
+    L = eng.engram_layout_create(
+        vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+        heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+        table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN, row_pitch_bytes=cfg.row_pitch_bytes,
+        hash_floor=cfg.hash_floor, num_sites=cfg.n_sites,
+        table_split=eng.ENGRAM_TABLE_PER_SITE if cfg.table_split == "site" else eng.ENGRAM_TABLES_PER_ORDER,
+        scale_layout=eng.ENGRAM_SCALE_BLOCK32_E8M0 if cfg.scale_block else eng.ENGRAM_SCALE_ROW_F32)
+    info = L.info
+    eids = torch.empty(T, dtype=torch.int32, device=DEV)
+    rid = torch.empty((T, cfg.n_sites, 3, cfg.heads), dtype=torch.int32, device=DEV)
+    eng.engram_compress_hash(L, tid, _d(batch.tokens), _d(batch.cu_seqlens), eids, rid)
+    h_data = [_pinned_copy(t) for t in tabs.data]
+    h_scale = [_pinned_copy(s) for s in tabs.scale]
+    torch.cuda.synchronize()
+    for dtype in (torch.float32, torch.bfloat16):
+        a = torch.empty((T, info.k_pad), dtype=dtype, device=DEV)
+        b = torch.full((T, info.k_pad), 7, dtype=dtype, device=DEV)
+        eng.engram_gather_dequant(L, tabs.data, tabs.scale, rid, a, site=0)
+        eng.engram_gather_dequant(L, h_data, h_scale, rid, b, site=0)
+        torch.cuda.synchronize()
+        assert eng.engram_get_error() == 0
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{name} {dtype}"
+    log(f"{name}: host-resident gather equals the HBM gather on all {T} tokens")
+    del tabs, h_data, h_scale
+    _free()
+
+
+@pytest.mark.parametrize("host", [False, True])
+def test_prefetch_pipeline_equals_sequential(eng, host):
+    cfg = ei.get_config("prefill")
+    calls = [ei.make_batch(ei.get_config("prefill", seed=100 + i)) for i in range(4)]
+    T = calls[0].T
+    ref = Site(cfg, max_tokens=T)
+    tables = ref.tables
+    if host:
+        tabs = [_pinned_copy(t) for t in tables.data]
+        scs = [_pinned_copy(s) for s in tables.scale]
+    else:
+        tabs, scs = tables.data, tables.scale
+    pipe = eng.Engram(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+                      heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+                      table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes,
+                      tid2eid=ref.tid2eid, tables=tabs, scales=scs, weight=ref.weight,
+                      hidden=cfg.hidden, max_tokens=T, prefetch_slots=2)
+    # sequential reference
+    expect = []
+    for i, b in enumerate(calls):
+        x = ei.make_streams(cfg, T, DEV, step=i)
+        ref.site.forward(_d(b.tokens), _d(b.cu_seqlens), x)
+        expect.append(bf16_bits_np(x))
+    torch.cuda.synchronize()
+    # pipelined: the prefetch of call i+1 is enqueued before call i's projection
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    xs = [ei.make_streams(cfg, T, DEV, step=i) for i in range(len(calls))]
+    inputs = [(_d(b.tokens), _d(b.cu_seqlens)) for b in calls]
+    torch.cuda.synchronize()
+    pre = pipe.prefetch(*inputs[0], stream=side)
+    for i in range(len(calls)):
+        nxt = pipe.prefetch(*inputs[i + 1], stream=side) if i + 1 < len(calls) else None
+        pipe.apply(pre, 0, xs[i], stream=main)
+        pre = nxt
+    torch.cuda.synchronize()
+    assert eng.engram_get_error() == 0
+    for i in range(len(calls)):
+        assert np.array_equal(bf16_bits_np(xs[i]), expect[i]), f"call {i}"
+    log(f"prefetch pipeline ({'host' if host else 'HBM'} tables): {len(calls)} calls equal sequential")
+    del ref, pipe, tabs, scs
+    _free()
