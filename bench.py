@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--prefetch", action="store_true",
                     help="also time the pipelined loop: hash + gather of step i+1 on a prefetch "
                          "stream while step i projects and gates; value = pipelined rate")
+    ap.add_argument("--proj-splits", type=int, default=0,
+                    help="split-K factor of the projection (0: chosen from the call size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alt-paths", action="store_true",
                     help="skip the fused-path comparison after the timed steps (profiler runs)")
@@ -242,7 +244,7 @@ def main():
                       weight=weights[0] if one else weights, hidden=cfg.hidden, hc_mult=cfg.hc_mult,
                       max_tokens=T, path=args.path, num_sites=NS, table_split=cfg.table_split,
                       scale_block=cfg.scale_block, hash_floor=cfg.hash_floor,
-                      prefetch_slots=2 if args.prefetch else 0)
+                      prefetch_slots=2 if args.prefetch else 0, proj_splits=args.proj_splits)
     site_streams = [ei.make_streams(cfg, T, dev, step=s) for s in range(NS)]
     streams_host = None
     if not args.no_cpu_baseline:
@@ -285,9 +287,16 @@ def main():
                 eng.engram_gather_dequant(L, site.site_tables[si], site.site_scales[si], site.row_ids,
                                           site.rows, site=si, T=T)
                 mark()
-                eng.engram_project(L, site.rows, site.site_weights[si], site.v, T=T)
+                if site.proj_splits > 1:
+                    eng.engram_project_splitk(L, site.rows, site.site_weights[si], site.partials,
+                                              site.proj_splits, T=T)
+                else:
+                    eng.engram_project(L, site.rows, site.site_weights[si], site.v, T=T)
                 mark()
-            eng.engram_gate_add(L, site.v, site_streams[si], T=T)
+            if args.path != "fused" and site.proj_splits > 1:
+                eng.engram_gate_add_partials(L, site.partials, site.proj_splits, site_streams[si], T=T)
+            else:
+                eng.engram_gate_add(L, site.v, site_streams[si], T=T)
             mark()
 
     for _ in range(args.warmup):
@@ -365,7 +374,8 @@ def main():
                    "heads_per_order": cfg.heads, "hidden": cfg.hidden, "hc_mult": cfg.hc_mult,
                    "k_pad": site.info.k_pad, "path": args.path, "sites": NS,
                    "table_split": cfg.table_split, "scale_block": cfg.scale_block,
-                   "tables_in": "pinned host memory" if args.host_tables else "HBM"},
+                   "tables_in": "pinned host memory" if args.host_tables else "HBM",
+                   "proj_splits": site.proj_splits},
         "roofline": roofline,
         "kernels": kernels,
         "wall_s_timed": wall,

@@ -118,6 +118,8 @@ _sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _
 _sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
 _sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _i32, _P, _P])
 _sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
+_sig("engram_project_splitk", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _i32, _P])
+_sig("engram_gate_add_partials", [_P, _P, _i32, _i32, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
 _sig("engram_host_device_pointer", [_P, ctypes.POINTER(_P)])
@@ -425,6 +427,38 @@ def engram_gather_project(layout: Layout, tables: Sequence, scales: Sequence, ro
                                       T, _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
                                       _dev(v, torch.float32, "v"), _stream(stream)),
            "engram_gather_project")
+
+
+def engram_project_splitk(layout: Layout, rows, w, partials, splits: int, *, T: Optional[int] = None,
+                          stream=None):
+    """partials: float [splits][>=T][hidden] workspace (slice s at offset s*T*hidden)."""
+    import torch
+    if T is None:
+        T = rows.shape[0]
+    hidden = w.shape[0]
+    _need(rows.dim() == 2 and rows.shape[0] >= T, "rows too small")
+    _need(partials.numel() >= splits * T * hidden, "partials smaller than splits x T x hidden")
+    _check(_lib.engram_project_splitk(layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
+                                      _dev(w, torch.bfloat16, "w"), w.shape[1], hidden,
+                                      _dev(partials, torch.float32, "partials"), splits, T,
+                                      _stream(stream)), "engram_project_splitk")
+
+
+def engram_gate_add_partials(layout: Layout, partials, splits: int, streams, *, keep=None, v=None,
+                             T: Optional[int] = None, stream=None):
+    import torch
+    if T is None:
+        T = streams.shape[0]
+    hidden = streams.shape[2]
+    _need(streams.dim() == 3 and streams.shape[0] >= T, "streams must be [T][hc][hidden]")
+    _need(partials.numel() >= splits * T * hidden, "partials smaller than splits x T x hidden")
+    _need(v is None or (v.dim() == 2 and v.shape[0] >= T and v.shape[1] == hidden), "v must be [T][hidden]")
+    _need(keep is None or keep.numel() >= T, "keep too small")
+    _check(_lib.engram_gate_add_partials(layout.handle, _dev(partials, torch.float32, "partials"), splits,
+                                         hidden, streams.shape[1], _dev(keep, torch.uint8, "keep"),
+                                         _dev(streams, torch.bfloat16, "streams"),
+                                         _dev(v, torch.float32, "v"), T, _stream(stream)),
+           "engram_gate_add_partials")
 
 
 def engram_gate_add(layout: Layout, v, streams, *, keep=None, T: Optional[int] = None, stream=None):

@@ -263,6 +263,33 @@ extern "C" int engram_project(const engram_layout* L, const void* d_rows, int64_
   g.M = T;
   g.N = hidden;
   g.K = (int32_t)L->k_pad;
+  g.splits = 1;
+  g.c_split_stride = 0;
+  return hip_status(engram::launch_gemm_bf16_nt(g, stream));
+}
+
+extern "C" int engram_project_splitk(const engram_layout* L, const void* d_rows, int64_t rows_ld,
+                                     const void* d_w, int64_t w_ld, int32_t hidden,
+                                     float* d_partials, int32_t splits, int32_t T,
+                                     hipStream_t stream) {
+  if (!L || T < 0 || hidden < 1 || splits < 1) return ENGRAM_E_ARG;
+  if (L->k_pad % (64 * (int64_t)splits) != 0) return ENGRAM_E_ALIGN;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_rows || !d_w || !d_partials) return ENGRAM_E_ARG;
+  if (rows_ld < L->k_pad || w_ld < L->k_pad || rows_ld % 8 || w_ld % 8) return ENGRAM_E_ALIGN;
+  if (!aligned(d_rows, 16) || !aligned(d_w, 16) || !aligned(d_partials, 4)) return ENGRAM_E_ALIGN;
+  engram::GemmArgs g;
+  g.A = d_rows;
+  g.B = d_w;
+  g.C = d_partials;
+  g.lda = rows_ld;
+  g.ldb = w_ld;
+  g.ldc = hidden;
+  g.M = T;
+  g.N = hidden;
+  g.K = (int32_t)L->k_pad;
+  g.splits = splits;
+  g.c_split_stride = (int64_t)T * hidden;
   return hip_status(engram::launch_gemm_bf16_nt(g, stream));
 }
 
@@ -314,6 +341,35 @@ extern "C" int engram_gate_add(const engram_layout* L, const float* d_v, int32_t
   if (!aligned(d_v, 16) || !aligned(d_streams, 16)) return ENGRAM_E_ALIGN;
   engram::GateArgs a;
   a.v = d_v;
+  a.splits = 1;
+  a.split_stride = 0;
+  a.v_out = nullptr;
+  a.keep = d_keep;
+  a.streams = d_streams;
+  a.T = T;
+  a.hidden = hidden;
+  a.hc = hc_mult;
+  a.inv_sqrt_hidden = (float)(1.0 / sqrt((double)hidden));
+  return hip_status(engram::launch_gate_add(a, stream));
+}
+
+extern "C" int engram_gate_add_partials(const engram_layout* L, const float* d_partials,
+                                        int32_t splits, int32_t hidden, int32_t hc_mult,
+                                        const uint8_t* d_keep, void* d_streams, float* d_v,
+                                        int32_t T, hipStream_t stream) {
+  if (!L || T < 0 || splits < 1) return ENGRAM_E_ARG;
+  if (hc_mult != 4) return ENGRAM_E_UNSUPPORTED;
+  if (hidden < 8 || hidden % 8 != 0) return ENGRAM_E_ALIGN;
+  if (hidden > 8192) return ENGRAM_E_UNSUPPORTED;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_partials || !d_streams) return ENGRAM_E_ARG;
+  if (!aligned(d_partials, 16) || !aligned(d_streams, 16) || (d_v && !aligned(d_v, 16)))
+    return ENGRAM_E_ALIGN;
+  engram::GateArgs a;
+  a.v = d_partials;
+  a.splits = splits;
+  a.split_stride = (int64_t)T * hidden;
+  a.v_out = d_v;
   a.keep = d_keep;
   a.streams = d_streams;
   a.T = T;

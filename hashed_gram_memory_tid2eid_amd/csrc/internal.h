@@ -108,6 +108,8 @@ struct GemmArgs {
   float* C;        // f32 [M][ldc]
   int64_t lda, ldb, ldc;
   int32_t M, N, K;
+  int32_t splits;          // 1: C = A B^T; > 1: split-K partial slices of C
+  int64_t c_split_stride;  // elements between partial slices
 };
 hipError_t launch_gemm_bf16_nt(const GemmArgs& a, hipStream_t stream);
 
@@ -131,7 +133,10 @@ struct GatherGemmArgs {
 hipError_t launch_gemm_gather_fp8(const GatherGemmArgs& a, hipStream_t stream);
 
 struct GateArgs {
-  const float* v;         // [T][hidden]
+  const float* v;         // [T][hidden], or [splits][T][hidden] partial slices
+  int32_t splits;         // >= 1: v is the sum of the slices, in slice order
+  int64_t split_stride;   // elements between slices
+  float* v_out;           // optional: the summed v is written here
   const uint8_t* keep;    // [T] or NULL
   void* streams;          // bf16 [T][hc][hidden]
   int32_t T, hidden, hc;

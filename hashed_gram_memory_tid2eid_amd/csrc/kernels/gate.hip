@@ -10,7 +10,8 @@
 // stream -> wave reduction (xor shuffles) -> cross-wave sum in LDS in a fixed
 // order (deterministic) -> g = sigmoid(z) -> x + g v rounded once to bf16.
 // A token with keep = 0 returns before touching its streams: they stay
-// bit for bit.
+// bit for bit.  After a split-K projection, v arrives as partial slices that
+// are summed here in slice order (deterministic), optionally written out.
 
 namespace engram {
 
@@ -31,7 +32,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 template <int CPT>
 __global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
   const int t = blockIdx.x;
-  if (a.keep != nullptr && a.keep[t] == 0) return;  // uniform per workgroup
+  const bool kept = a.keep == nullptr || a.keep[t] != 0;
+  if (!kept && a.v_out == nullptr) return;  // uniform per workgroup
   const int tid = threadIdx.x;
   const int nchunks = a.hidden >> 3;
   const float* vrow = a.v + (int64_t)t * a.hidden;
@@ -44,8 +46,18 @@ __global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
   for (int c = 0; c < CPT; ++c) {
     const int ch = tid + c * kGateThreads;
     if (ch < nchunks) {
-      const g_f32x4 v0 = *reinterpret_cast<const g_f32x4*>(vrow + ch * 8);
-      const g_f32x4 v1 = *reinterpret_cast<const g_f32x4*>(vrow + ch * 8 + 4);
+      g_f32x4 v0 = *reinterpret_cast<const g_f32x4*>(vrow + ch * 8);
+      g_f32x4 v1 = *reinterpret_cast<const g_f32x4*>(vrow + ch * 8 + 4);
+      for (int sp = 1; sp < a.splits; ++sp) {  // split-K slices, summed in slice order
+        const float* pr = vrow + (int64_t)sp * a.split_stride + ch * 8;
+        v0 += *reinterpret_cast<const g_f32x4*>(pr);
+        v1 += *reinterpret_cast<const g_f32x4*>(pr + 4);
+      }
+      if (a.v_out != nullptr) {
+        float* vo = a.v_out + (int64_t)t * a.hidden + ch * 8;
+        *reinterpret_cast<g_f32x4*>(vo) = v0;
+        *reinterpret_cast<g_f32x4*>(vo + 4) = v1;
+      }
       v[c][0] = v0[0]; v[c][1] = v0[1]; v[c][2] = v0[2]; v[c][3] = v0[3];
       v[c][4] = v1[0]; v[c][5] = v1[1]; v[c][6] = v1[2]; v[c][7] = v1[3];
 #pragma unroll
@@ -66,6 +78,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
       }
     }
   }
+
+  if (!kept) return;  // v_out written; the streams of a dead token stay bit for bit
 
   __shared__ float part[kGateThreads / 64][kHc];
 #pragma unroll

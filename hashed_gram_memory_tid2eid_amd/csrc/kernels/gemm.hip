@@ -54,6 +54,8 @@ struct GemmKArgs {
   int32_t tiles_m, tiles_n;
   int32_t group_m;
   int32_t vec_store;  // C 16-byte aligned and ldc % 4 == 0: whole-tile stores may be 16-byte
+  int32_t k_chunk;          // split-K: k per split (blockIdx.y picks the split)
+  int64_t c_split_stride;   // split-K: elements between the splits' partial C slices
 };
 
 // physical 16-byte chunk of logical chunk c in a 128-byte LDS row: c ^ ((row >> 1) & 7).
@@ -78,6 +80,16 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
   constexpr int AI = BM / 8 / NWAVES, BI = BN / 8 / NWAVES;  // 1 KB direct loads per wave per stage
   static_assert(AI * 8 * NWAVES == BM && BI * 8 * NWAVES == BN, "tile must fill whole load rounds");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  // ---- split-K: split y multiplies k in [y k_chunk, (y+1) k_chunk) into its own
+  //      partial slice of C (the consumer sums the slices in split order)
+  if (gridDim.y > 1) {
+    const int sp = blockIdx.y;
+    a.A += (int64_t)sp * a.k_chunk;
+    a.B += (int64_t)sp * a.k_chunk;
+    a.C += (int64_t)sp * a.c_split_stride;
+    a.K = a.k_chunk;
+  }
 
   // ---- tile id: XCD-contiguous runs, then GROUP_M swizzle ------------------
   const int ntiles = a.tiles_m * a.tiles_n;
@@ -271,6 +283,9 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
   a.tiles_n = (g.N + BN - 1) / BN;
   a.group_m = 2;
   a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
+  const int splits = g.splits > 1 ? g.splits : 1;
+  a.k_chunk = g.K / splits;
+  a.c_split_stride = g.c_split_stride;
   const size_t lds_bytes = (size_t)kGemmStages * STAGE;
   static bool attr_set = false;
   if (!attr_set) {
@@ -280,14 +295,15 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
     attr_set = true;
   }
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, WMW, WNW>), dim3(grid), dim3(64 * WMW * WNW),
-                     lds_bytes, stream, a);
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, WMW, WNW>), dim3(grid, (unsigned)splits),
+                     dim3(64 * WMW * WNW), lds_bytes, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_nt(const GemmArgs& g, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (g.K % kGemmBK != 0 || g.K <= 0) return hipErrorInvalidValue;
+  if (g.splits > 1 && (g.K % (kGemmBK * g.splits) != 0)) return hipErrorInvalidValue;
   // Large M: 256 x 256 tiles, 8 waves (2 stages x 64 KB of LDS, one workgroup per CU).
   // Small M: 128 x 128 tiles, 4 waves, so that more CUs get work.
   if ((int64_t)g.M * g.N >= (int64_t)64 * 256 * 256)

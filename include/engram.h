@@ -290,6 +290,17 @@ int engram_project(const engram_layout* layout, const void* d_rows, int64_t rows
                    const void* d_w, int64_t w_ld, int32_t hidden, float* d_v, int32_t T,
                    hipStream_t stream);
 
+/* Split-K form of engram_project for few tokens (decode): K is cut into `splits`
+ * equal chunks (k_pad must be a multiple of 64 * splits) that run as separate
+ * workgroups, so a small token count still fills the chip; chunk s writes
+ *   d_partials[s][t][o] = sum over its k of rows[t][k] * W[o][k]
+ * (float [splits][T][hidden], caller-owned workspace).  engram_gate_add_partials
+ * sums the slices in slice order, so the result is deterministic.
+ * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN. */
+int engram_project_splitk(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
+                          const void* d_w, int64_t w_ld, int32_t hidden, float* d_partials,
+                          int32_t splits, int32_t T, hipStream_t stream);
+
 /* Steps 2 and the projection half of step 3 in one kernel, for e4m3fn tables:
  *   v[t][o] = sum_{k < k_pad} rows[t][k] * W[o][k]
  * with rows[t] exactly the bf16 rows engram_gather_dequant would write (row-wise
@@ -321,6 +332,14 @@ int engram_gather_project(const engram_layout* layout, const void* const* d_tabl
 int engram_gate_add(const engram_layout* layout, const float* d_v, int32_t hidden,
                     int32_t hc_mult, const uint8_t* d_keep, void* d_streams, int32_t T,
                     hipStream_t stream);
+
+/* engram_gate_add with v given as the split-K slices of engram_project_splitk:
+ * v[t][o] = sum_{s < splits} d_partials[s][t][o], summed in slice order; d_v
+ * (float [T][hidden], 16-byte aligned) receives that v when not NULL.  Otherwise
+ * as engram_gate_add. */
+int engram_gate_add_partials(const engram_layout* layout, const float* d_partials, int32_t splits,
+                             int32_t hidden, int32_t hc_mult, const uint8_t* d_keep,
+                             void* d_streams, float* d_v, int32_t T, hipStream_t stream);
 
 /* engram_project followed by engram_gate_add on the same stream; d_v is the
  * caller's fp32 [T][hidden] workspace.  There is no variant without rows: a

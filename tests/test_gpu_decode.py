@@ -171,3 +171,43 @@ def test_decode_step_graph_replays_equal_eager(eng):
     log(f"graph: {len(steps) - 1} replays equal eager")
     del g
     _free()
+
+
+@pytest.mark.parametrize("M,N,H,D,splits", [(256, 4096, 2, 512, 8), (256, 4096, 2, 512, 4),
+                                            (77, 264, 1, 128, 2), (512, 256, 2, 128, 2),
+                                            (1, 8, 1, 256, 4)])
+def test_projection_splitk_and_partial_gate(eng, M, N, H, D, splits):
+    """Split-K projection against torch's fp32 product of the same bf16 operands
+    (fp32 accumulation bound), and the gate over the partial slices against the
+    plain gate given the summed v (bit for bit)."""
+    L = eng.engram_layout_create(vocab_size=8, compressed_vocab=4, pad_token_id=7, heads_per_order=H,
+                                 rows=[100_000] * 3, row_dim=D, table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN,
+                                 row_pitch_bytes=D)
+    K = L.info.k_pad
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M * 31 + N + splits)
+    A = torch.randn((M, K), generator=g, device=DEV).to(torch.bfloat16)
+    B = (torch.randn((N, K), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    parts = torch.full((splits * M * N,), float("nan"), dtype=torch.float32, device=DEV)
+    eng.engram_project_splitk(L, A, B, parts, splits)
+    x = torch.randn((M, 4, N), generator=g, device=DEV).to(torch.bfloat16)
+    y = x.clone()
+    v = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    keep = (torch.rand(M, generator=g, device=DEV) > 0.2).to(torch.uint8)
+    eng.engram_gate_add_partials(L, parts, splits, y, keep=keep, v=v)
+    ref = A.float() @ B.float().T
+    torch.cuda.synchronize()
+    bound = 2 * K * 2.0 ** -24 * (A.float().abs() @ B.float().abs().T) + 1e-6
+    assert ((v - ref).abs() <= bound).all()
+    # the slices sum to v in slice order
+    p = parts.view(splits, M, N)
+    acc = p[0].clone()
+    for s in range(1, splits):
+        acc += p[s]
+    assert torch.equal(acc.view(torch.int32), v.view(torch.int32))
+    y2 = x.clone()
+    eng.engram_gate_add(L, v, y2, keep=keep)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    dead = keep == 0
+    assert torch.equal(y[dead].view(torch.int16), x[dead].view(torch.int16))
