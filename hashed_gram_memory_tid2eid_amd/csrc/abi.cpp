@@ -311,6 +311,8 @@ extern "C" int engram_gather_project(const engram_layout* L, const void* const* 
   const void* scale[3];
   const int rc = site_tables(L, d_tables, d_scales, g.table, scale, g.rows);
   if (rc != ENGRAM_OK) return rc;
+  for (int n = 0; n < 3; ++n)  // rows stream through direct-to-LDS loads: HBM tables only
+    if (in_host_memory(g.table[n]) || in_host_memory(scale[n])) return ENGRAM_E_UNSUPPORTED;
   for (int n = 0; n < 3; ++n) g.scale[n] = static_cast<const float*>(scale[n]);
   g.row_ids = d_row_ids + (int64_t)site * L->cols;
   g.rid_ld = L->all_cols;

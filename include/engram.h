@@ -313,8 +313,8 @@ int engram_project_splitk(const engram_layout* layout, const void* d_rows, int64
  *   read in 64-byte pieces up to seg_pitch; bytes past D are ignored).
  *   d_w, w_ld, hidden, d_v as for engram_project.
  * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN, ENGRAM_E_UNSUPPORTED (bf16 tables,
- * BLOCK32 scales).  Device error: ENGRAM_E_ROW_RANGE (that segment contributes
- * zero). */
+ * BLOCK32 scales, tables in host memory).  Device error: ENGRAM_E_ROW_RANGE (that
+ * segment contributes zero). */
 int engram_gather_project(const engram_layout* layout, const void* const* d_tables,
                           const void* const* d_scales, const int32_t* d_row_ids, int32_t site,
                           int32_t T, const void* d_w, int64_t w_ld, int32_t hidden, float* d_v,

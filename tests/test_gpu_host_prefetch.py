@@ -120,3 +120,18 @@ def test_prefetch_pipeline_equals_sequential(eng, host):
     log(f"prefetch pipeline ({'host' if host else 'HBM'} tables): {len(calls)} calls equal sequential")
     del ref, pipe, tabs, scs
     _free()
+
+
+def test_fused_path_refuses_host_tables(eng):
+    """The fused gather + projection streams rows by direct-to-LDS loads from HBM
+    tables; given tables in host memory it refuses instead of guessing."""
+    cfg = ei.get_config("tiny")
+    site = Site(cfg, max_tokens=64)
+    h_data = [_pinned_copy(t) for t in site.tables.data]
+    h_scale = [_pinned_copy(s) for s in site.tables.scale]
+    rid = torch.zeros((64, 3, cfg.heads), dtype=torch.int32, device=DEV)
+    v = torch.empty((64, cfg.hidden), dtype=torch.float32, device=DEV)
+    with pytest.raises(eng.EngramError) as ex:
+        eng.engram_gather_project(site.site.layout, h_data, h_scale, rid, site.site.weight, v)
+    assert ex.value.status == eng.ENGRAM_E_UNSUPPORTED
+    _free()
