@@ -4,7 +4,7 @@
 // [vLLM-V41] "vllm/models/deepseek_v41/nvidia/model", DeepseekV4Model.forward:
 // the gate of an image-span token is zeroed).  Included into engram_device.hip.
 //
-// One 256-thread workgroup per token.  Each thread holds CPT chunks of 8
+// One workgroup per token (256 or 512 threads).  Each thread holds CPT chunks of 8
 // elements of v (fp32) and of each of the hc = 4 streams (bf16) in registers,
 // so every byte is read once and written once: partial dot products per
 // stream -> wave reduction (xor shuffles) -> cross-wave sum in LDS in a fixed
@@ -18,7 +18,6 @@ namespace engram {
 typedef unsigned int g_u32x4 __attribute__((ext_vector_type(4)));
 typedef float g_f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGateThreads = 256;
 constexpr int kHc = 4;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -29,8 +28,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
-template <int CPT>
-__global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
+template <int CPT, int THREADS>
+__global__ __launch_bounds__(THREADS) void gate_add_kernel(GateArgs a) {
   const int t = blockIdx.x;
   const bool kept = a.keep == nullptr || a.keep[t] != 0;
   if (!kept && a.v_out == nullptr) return;  // uniform per workgroup
@@ -44,7 +43,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
   float dot[kHc] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int ch = tid + c * kGateThreads;
+    const int ch = tid + c * THREADS;
     if (ch < nchunks) {
       g_f32x4 v0 = *reinterpret_cast<const g_f32x4*>(vrow + ch * 8);
       g_f32x4 v1 = *reinterpret_cast<const g_f32x4*>(vrow + ch * 8 + 4);
@@ -81,7 +80,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
 
   if (!kept) return;  // v_out written; the streams of a dead token stay bit for bit
 
-  __shared__ float part[kGateThreads / 64][kHc];
+  __shared__ float part[THREADS / 64][kHc];
 #pragma unroll
   for (int s = 0; s < kHc; ++s) {
 #pragma unroll
@@ -97,14 +96,14 @@ __global__ __launch_bounds__(kGateThreads) void gate_add_kernel(GateArgs a) {
   for (int s = 0; s < kHc; ++s) {
     float z = part[0][s];
 #pragma unroll
-    for (int w = 1; w < kGateThreads / 64; ++w) z += part[w][s];
+    for (int w = 1; w < THREADS / 64; ++w) z += part[w][s];
     z *= a.inv_sqrt_hidden;
     g[s] = 1.0f / (1.0f + expf(-z));
   }
 
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int ch = tid + c * kGateThreads;
+    const int ch = tid + c * THREADS;
     if (ch >= nchunks) continue;
 #pragma unroll
     for (int s = 0; s < kHc; ++s) {
@@ -122,14 +121,15 @@ hipError_t launch_gate_add(const GateArgs& a, hipStream_t stream) {
   (void)hipGetLastError();  // drop a stale error another library left on this thread
   if (a.T == 0) return hipSuccess;
   const int nchunks = a.hidden / 8;
-  const int cpt = (nchunks + kGateThreads - 1) / kGateThreads;
-  const dim3 grid((unsigned)a.T), block(kGateThreads);
-  if (cpt <= 1)
-    hipLaunchKernelGGL(gate_add_kernel<1>, grid, block, 0, stream, a);
-  else if (cpt <= 2)
-    hipLaunchKernelGGL(gate_add_kernel<2>, grid, block, 0, stream, a);
-  else if (cpt <= 4)
-    hipLaunchKernelGGL(gate_add_kernel<4>, grid, block, 0, stream, a);
+  const dim3 grid((unsigned)a.T);
+  // one chunk of 8 elements per thread where the row allows it: 512 threads for
+  // hidden 4,096 keeps the register count low enough for 8 waves per SIMD
+  if (nchunks <= 256)
+    hipLaunchKernelGGL((gate_add_kernel<1, 256>), grid, dim3(256), 0, stream, a);
+  else if (nchunks <= 512)
+    hipLaunchKernelGGL((gate_add_kernel<1, 512>), grid, dim3(512), 0, stream, a);
+  else if (nchunks <= 1024)
+    hipLaunchKernelGGL((gate_add_kernel<2, 512>), grid, dim3(512), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
