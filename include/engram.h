@@ -12,6 +12,13 @@
  *                             engram_project + engram_gate_add are its two halves.
  *   engram_gather_project     steps 2 and the projection in one kernel for
  *                             e4m3fn tables (rows stay on chip).
+ *   engram_project_splitk +   the projection split over K for few tokens
+ *   engram_gate_add_partials  (decode), summed deterministically in the gate.
+ *   engram_store_*            the rolling store: reset, write, read (snapshot)
+ *                             and rollback to accepted lengths.
+ *   One layout may describe several Engram sites sharing one hash pass; the
+ *   gathers then take a site index.  Tables may live in HBM or in pinned host
+ *   memory (engram_host_device_pointer).
  *
  * Pages defining the operations (titles; sections named):
  *  [VeOmni#1370] GitHub PR "feat: support DeepSeek-V4.1-Flash in SeedOmni"
@@ -26,9 +33,10 @@
  *  - Device pointers ("d_" prefix) are caller-owned device memory on the
  *    current HIP device; the library never frees or keeps them.  Host pointers
  *    have no prefix.  Sizes are element counts unless the name says bytes.
- *  - Hot calls (compress_hash, gather_dequant, project, gate_add,
- *    gated_residual, store_*) allocate nothing, never synchronise, and only
- *    enqueue kernels on `stream`.
+ *  - Hot calls (compress_hash, gather_dequant, gather_project, project,
+ *    project_splitk, gate_add, gate_add_partials, gated_residual, store_*)
+ *    allocate nothing, never synchronise, and only enqueue kernels on `stream`;
+ *    none records a memset, so a caller may capture them in a HIP graph.
  *  - Faults that only the device can see (a token id outside the vocabulary,
  *    a row id outside its table, a bad slot, malformed cu_seqlens, a continuing
  *    sequence without a store) latch the first such status in a per-device
