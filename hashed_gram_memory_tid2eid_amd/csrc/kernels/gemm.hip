@@ -17,7 +17,8 @@
 // register staging) in stages of 64 k: one whole 128-byte line of every operand
 // row, so each line is fetched once and every cache request is a full line.  Two
 // stages (2 x 64 KB for a 256 x 256 tile) form a ring: stage kt+1 streams in
-// while stage kt multiplies; one barrier per stage.  A wave writes 1 KB of
+// while stage kt multiplies; one barrier per stage.  128 x 128 tiles (few tokens)
+// use a ring of 4 stages of 32 KB, so three stages stay in flight.  A wave writes 1 KB of
 // consecutive LDS per load, so the XOR swizzle of the 16-byte chunks
 // (chunk ^ ((row >> 1) & 7), rows of 128 B) is applied by choosing which global
 // chunk each lane fetches; with it the fragment reads are free of LDS bank
@@ -43,7 +44,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define ENGRAM_LDS_AS __attribute__((address_space(3)))
 
 constexpr int kGemmBK = 64;      // k per stage: one 128-byte line of every operand row
-constexpr int kGemmStages = 2;   // LDS ring depth
+// LDS ring depth: 2 stages of 64 KB for 256 x 256 tiles (all the LDS allows); 4 stages
+// of 32 KB for 128 x 128 tiles, whose few-token calls are bound by load latency
+constexpr int kSmallTileStages = 4;
 
 struct GemmKArgs {
   const __bf16* A;
@@ -70,7 +73,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int BM, int BN, int WM_WAVES, int WN_WAVES>
+template <int BM, int BN, int WM_WAVES, int WN_WAVES, int STAGES>
 __global__ __launch_bounds__(64 * WM_WAVES * WN_WAVES, 1)
 void gemm_bf16_nt_kernel(GemmKArgs a) {
   constexpr int BK = kGemmBK;
@@ -127,7 +130,7 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
     bp[i] = a.B + (int64_t)min(n0 + row, a.N - 1) * a.ldb + 8 * c;
   }
   auto issue = [&](int kt) {
-    char* st = smem + (kt & 1) * STAGE;
+    char* st = smem + (kt % STAGES) * STAGE;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(ap[i] + kt * BK),
@@ -155,7 +158,7 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
   }
   // fragments of k16 step ks (0..3) of stage kt
   auto load_frags = [&](int kt, int ks, bf16x8* fa, bf16x8* fb) {
-    const __bf16* base = reinterpret_cast<const __bf16*>(smem + (kt & 1) * STAGE);
+    const __bf16* base = reinterpret_cast<const __bf16*>(smem + (kt % STAGES) * STAGE);
     const int c = ks * 2 + lk;
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(base + brow[j] + 8 * (c ^ bswz[j]));
@@ -181,10 +184,13 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
   //      next stage's first step is read while the last step multiplies.  At most
   //      one step of fragments (TM + TN reads) is outstanding at any wait.
   const int nk = a.K / BK;
-  issue(0);
-  wait_vmcnt<0>();
+  constexpr int LOADS = AI + BI;  // direct loads per wave per stage
+  // prologue: every slot of the ring is free; wait for stage 0 only
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nk) issue(s);
+  if (nk >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>(); else wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  if (nk > 1) issue(1);
   bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   load_frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
@@ -207,13 +213,14 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
     mma(fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     // this wave is done reading stage kt once step 3 has landed; the barrier makes
-    // that true for every wave and publishes stage kt+1, then stage kt is refilled
-    // with kt+2 (the last iteration re-reads its own stage to keep the counts fixed)
+    // that true for every wave and publishes stage kt+1 (stages kt+2 .. kt+STAGES-1
+    // may still be in flight), then slot kt%STAGES is refilled with stage
+    // kt+STAGES (the last iteration re-reads its own stage to keep the counts fixed)
     wait_lgkmcnt0();
     if (kt + 1 < nk) {
-      wait_vmcnt<0>();
+      if (kt + STAGES - 1 < nk) wait_vmcnt<(STAGES - 2) * LOADS>(); else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      if (kt + 2 < nk) issue(kt + 2);
+      if (kt + STAGES < nk) issue(kt + STAGES);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_frags(kt + 1 < nk ? kt + 1 : kt, 0, fa0, fb0);
@@ -229,7 +236,7 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
   //      row segments of C instead of scattering 4-byte values.
   constexpr int SLAB = 32 * WN;                 // floats per staged slab
   constexpr int PITCH = WN + 4;                 // LDS row pitch (floats), breaks bank aliasing
-  static_assert(NWAVES * 32 * PITCH * 4 <= 2 * STAGE, "epilogue staging must fit in the ring");
+  static_assert(NWAVES * 32 * PITCH * 4 <= STAGES * STAGE, "epilogue staging must fit in the ring");
   (void)SLAB;
   __builtin_amdgcn_s_barrier();                 // every wave is done with the operand ring
   float* slab = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
@@ -265,7 +272,7 @@ void gemm_bf16_nt_kernel(GemmKArgs a) {
   }
 }
 
-template <int BM, int BN, int WMW, int WNW>
+template <int BM, int BN, int WMW, int WNW, int STAGES>
 static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
   (void)hipGetLastError();  // drop a stale error another library left on this thread
   constexpr int STAGE = (BM + BN) * kGemmBK * 2;
@@ -286,16 +293,16 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
   const int splits = g.splits > 1 ? g.splits : 1;
   a.k_chunk = g.K / splits;
   a.c_split_stride = g.c_split_stride;
-  const size_t lds_bytes = (size_t)kGemmStages * STAGE;
+  const size_t lds_bytes = (size_t)STAGES * STAGE;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_nt_kernel<BM, BN, WMW, WNW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_nt_kernel<BM, BN, WMW, WNW, STAGES>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
-  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, WMW, WNW>), dim3(grid, (unsigned)splits),
+  hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, WMW, WNW, STAGES>), dim3(grid, (unsigned)splits),
                      dim3(64 * WMW * WNW), lds_bytes, stream, a);
   return hipGetLastError();
 }
@@ -307,8 +314,8 @@ hipError_t launch_gemm_bf16_nt(const GemmArgs& g, hipStream_t stream) {
   // Large M: 256 x 256 tiles, 8 waves (2 stages x 64 KB of LDS, one workgroup per CU).
   // Small M: 128 x 128 tiles, 4 waves, so that more CUs get work.
   if ((int64_t)g.M * g.N >= (int64_t)64 * 256 * 256)
-    return launch_gemm_tile<256, 256, 2, 4>(g, stream);
-  return launch_gemm_tile<128, 128, 2, 2>(g, stream);
+    return launch_gemm_tile<256, 256, 2, 4, 2>(g, stream);
+  return launch_gemm_tile<128, 128, 2, 2, kSmallTileStages>(g, stream);
 }
 
 }  // namespace engram
