@@ -159,3 +159,42 @@ def test_fused_refuses_bf16_tables(eng):
     with pytest.raises(eng.EngramError) as ex:
         eng.engram_gather_project(L, t, s, rid, w, v)
     assert ex.value.status == eng.ENGRAM_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("split", ["order", "site"])
+def test_fused_second_site_equals_split(eng, split):
+    """Two sites sharing one hash pass: the fused kernel reads site 1's columns of
+    the shared row-id array (and, with one table per site, every segment from that
+    site's table) exactly like the two-call path."""
+    H, D, rows, T, N = 2, 128, 60_000, 700, 512
+    per_site = split == "site"
+    L = eng.engram_layout_create(
+        vocab_size=8, compressed_vocab=4, pad_token_id=7, heads_per_order=H,
+        rows=[rows, 0, 0] if per_site else [rows] * 3, row_dim=D,
+        table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN, row_pitch_bytes=D, hash_floor=1000, num_sites=2,
+        table_split=eng.ENGRAM_TABLE_PER_SITE if per_site else eng.ENGRAM_TABLES_PER_ORDER)
+    info = L.info
+    tabs, scales = _random_fp8_tables(rows, D, D, seed=77)
+    if per_site:
+        tabs, scales = tabs[:1], scales[:1]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(78)
+    rid = torch.empty((T, 2, 3, H), dtype=torch.int32, device=DEV)
+    for s in range(2):
+        for n in range(3):
+            for h in range(H):
+                lo = int(info.site_offsets[s][n][h])
+                p = int(info.site_primes[s][n][h])
+                rid[:, s, n, h] = torch.randint(lo, lo + p, (T,), generator=g, device=DEV, dtype=torch.int32)
+    w = (torch.randn((N, info.k_pad), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    e16 = torch.empty((T, info.k_pad), dtype=torch.bfloat16, device=DEV)
+    v_split = torch.empty((T, N), dtype=torch.float32, device=DEV)
+    v_fused = torch.empty_like(v_split)
+    for s in range(2):
+        eng.engram_gather_dequant(L, tabs, scales, rid, e16, site=s)
+        eng.engram_project(L, e16, w, v_split)
+        eng.engram_gather_project(L, tabs, scales, rid, w, v_fused, site=s)
+        torch.cuda.synchronize()
+        assert eng.engram_get_error() == 0
+        assert torch.equal(v_split.view(torch.int32), v_fused.view(torch.int32)), f"site {s}"
+    _free()

@@ -187,3 +187,48 @@ def test_v41_small_two_sites(eng):
 @pytest.mark.timeout(900)
 def test_v41_released_sizes(eng):
     _run(eng, "v41", f32_sample=1024, stream_sample=24)
+
+
+def test_two_sites_per_order_tables_against_oracle(eng):
+    """Two sites sharing one hash pass with three tables per order each: every
+    site's row ids exact against the oracle's per-site layouts, and each site's
+    gather reads its own tables (fp32 rows exact)."""
+    cfg = ei.get_config("tiny")
+    batch = ei.make_batch(cfg)
+    T = batch.T
+    floor_ = 1000
+    L = eng.engram_layout_create(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+                                 heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+                                 table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN,
+                                 row_pitch_bytes=cfg.row_pitch_bytes, hash_floor=floor_, num_sites=2)
+    tid_h = ei.make_tid2eid(cfg.vocab, cfg.vc)
+    tid = _d(tid_h)
+    eids = torch.empty(T, dtype=torch.int32, device=DEV)
+    rid = torch.empty((T, 2, 3, cfg.heads), dtype=torch.int32, device=DEV)
+    eng.engram_compress_hash(L, tid, _d(batch.tokens), _d(batch.cu_seqlens), eids, rid)
+    ols = oracle.site_layouts(2, cfg.heads, floor_, False)
+    refs = []
+    for ol in ols:
+        _, r = oracle.compress_hash(ol, vocab=cfg.vocab, vc=cfg.vc, pad_token_id=cfg.pad_token_id,
+                                    tid2eid=tid_h, tokens=batch.tokens, cu_seqlens=batch.cu_seqlens)
+        refs.append(r)
+    torch.cuda.synchronize()
+    assert np.array_equal(rid.cpu().numpy(), np.stack(refs, axis=1))
+    tabs = [ei.make_tables(cfg, DEV, site=s) for s in range(2)]
+    out = torch.empty((T, L.info.k_pad), dtype=torch.float32, device=DEV)
+    D = cfg.row_dim
+    for s in range(2):
+        eng.engram_gather_dequant(L, tabs[s].data, tabs[s].scale, rid, out, site=s)
+        torch.cuda.synchronize()
+        raw = np.zeros((T, 3 * cfg.heads, D), np.uint8)
+        sc = np.zeros((T, 3 * cfg.heads), np.float32)
+        for n in range(3):
+            for h in range(cfg.heads):
+                idx = torch.from_numpy(refs[s][:, n, h].astype(np.int64)).to(DEV)
+                raw[:, n * cfg.heads + h] = tabs[s].row_view(n).index_select(0, idx).cpu().numpy()
+                sc[:, n * cfg.heads + h] = tabs[s].scale[n].index_select(0, idx).cpu().numpy()
+        f_ref, _ = oracle.dequant_rows(raw.reshape(-1, D), sc.reshape(-1))
+        got = out.view(T, -1, L.info.seg_pitch).cpu().numpy()[:, :, :D]
+        assert np.array_equal(got.reshape(-1, D).view(np.uint32), f_ref.view(np.uint32)), f"site {s}"
+    assert eng.engram_get_error() == 0
+    _free()
