@@ -216,10 +216,12 @@ class Layout:
         self.desc = desc
         self.info = engram_layout_query(self)
 
-    def __del__(self):
+    # the destroy function is bound when the class is made: at interpreter exit the
+    # module's globals may already be gone when the last Layout is collected
+    def __del__(self, _destroy=_lib.engram_layout_destroy):
         h, self.handle = getattr(self, "handle", None), None
         if h:
-            _lib.engram_layout_destroy(h)
+            _destroy(h)
 
     @property
     def _as_parameter_(self):

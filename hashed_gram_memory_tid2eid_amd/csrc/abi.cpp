@@ -38,7 +38,7 @@ extern "C" int engram_tid2eid_check(const engram_layout* L, const int32_t* d_tid
   if (e == hipSuccess) e = engram::launch_map_check(a, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(h_res, d_res, sizeof h_res, hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  hipFree(d_res);
+  (void)hipFree(d_res);
   if (e != hipSuccess) return hip_status(e);
   if (h_res[0] != 0 || h_res[1] != a.vc - 1) return ENGRAM_E_MAP_RANGE;
   *pad_eid = h_res[2];
