@@ -467,6 +467,50 @@ def main():
             "reps": reps,
         }
         del v_alt
+    if args.path == "split" and not args.host_tables and not args.no_alt_paths:
+        # reuse in this batch and a control gather without it, outside the timed region:
+        # repeated n-grams look up the same rows, which the caches then serve; the
+        # control draws every row id uniformly from its column's buckets (seeded)
+        info = site.info
+        H = cfg.heads
+        rid = site.row_ids[:T].reshape(T, NS, 3, H)
+        unique = {}
+        for n in range(3):
+            col = rid[:, 0, n, :].reshape(-1)
+            unique[f"{n + 2}-gram"] = torch.unique(col).numel() / max(1, col.numel())
+        rid_u = torch.empty_like(rid)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        for si in range(NS):
+            for n in range(3):
+                for h in range(H):
+                    lo, p = int(info.site_offsets[si][n][h]), int(info.site_primes[si][n][h])
+                    rid_u[:, si, n, h] = torch.randint(lo, lo + p, (T,), generator=gen, device=dev,
+                                                       dtype=torch.int32)
+        reps = max(3, min(args.steps, 10))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        eng.engram_gather_dequant(L, site.site_tables[0], site.site_scales[0], rid_u, site.rows, site=0, T=T)
+        e[0].record()
+        for _ in range(reps):
+            eng.engram_gather_dequant(L, site.site_tables[0], site.site_scales[0], rid_u, site.rows,
+                                      site=0, T=T)
+        e[1].record()
+        for _ in range(reps):
+            eng.engram_gather_dequant(L, site.site_tables[0], site.site_scales[0], site.row_ids, site.rows,
+                                      site=0, T=T)
+        e[2].record()
+        torch.cuda.synchronize()
+        eng.check_device_error("gather controls")
+        u_ms, h_ms = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+        result["gather_controls"] = {
+            "unique_row_frac": unique,
+            "uniform_rows": {"ms": u_ms, "GB/s": gbs(gather_bytes, u_ms),
+                             "frac": gbs(gather_bytes, u_ms) / HBM_PEAK_GBS},
+            "hashed_rows_back_to_back": {"ms": h_ms, "GB/s": gbs(gather_bytes, h_ms),
+                                         "frac": gbs(gather_bytes, h_ms) / HBM_PEAK_GBS},
+            "reps": reps,
+        }
+        del rid_u
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
