@@ -163,3 +163,38 @@ def test_gather_split_past_2_31_chunks(eng):
     log(f"split gather: {n_s} sampled tokens (both launch edges) equal the oracle")
     del out, rid, tabs, scales
     _free()
+
+
+@pytest.mark.parametrize("S", [255, 3000])
+def test_many_short_sequences_against_the_oracle(eng, S):
+    """Sequences of 0..4 tokens with a slot store, mixed starts and dead spans, over
+    several workgroups (the store update runs as its own kernel after the hash)."""
+    cfg = ei.get_config("tiny")
+    rng = np.random.default_rng(91 + S)
+    lens = rng.integers(0, 5, size=S).astype(np.int32)
+    cu = np.zeros(S + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+    num_slots = S + 500
+    site = Site(cfg, max_tokens=T)
+    L = site.site.layout
+    batch = ei.Batch(tokens=ei.zipf_tokens(rng, T), cu_seqlens=cu,
+                     seq_start=(rng.random(S) < 0.5).astype(np.uint8),
+                     slots=rng.permutation(num_slots)[:S].astype(np.int32),
+                     dead=ei.make_dead_spans(T, 11, n_spans=T // 50, max_len=3))
+    store0 = rng.integers(0, cfg.vc, size=(num_slots, 3)).astype(np.int32)
+    store = torch.from_numpy(store0.copy()).to(DEV)
+    e = torch.empty(T, dtype=torch.int32, device=DEV)
+    r = torch.empty((T, 3, cfg.heads), dtype=torch.int32, device=DEV)
+    db = site.device_batch(batch)
+    eng.engram_compress_hash(L, site.tid2eid, db["tokens"], db["cu_seqlens"], e, r,
+                             seq_start=db["seq_start"], slots=db["slots"], store=store, dead=db["dead"])
+    torch.cuda.synchronize()
+    assert eng.engram_get_error() == 0
+    ref = store0.copy()
+    e_ref, r_ref = site.oracle_hash(batch, ref)
+    assert np.array_equal(e.cpu().numpy(), e_ref)
+    assert np.array_equal(r.cpu().numpy(), r_ref)
+    assert np.array_equal(store.cpu().numpy(), ref)
+    log(f"{S} sequences, {T} tokens: ids, row ids and store equal the oracle")
+    _free()
