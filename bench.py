@@ -351,6 +351,12 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
                     "traffic": measured_traffic(cfg), "bytes_per_launch": gather_bytes,
                     "avg_launch_ms": kern_ms["gather_dequant"]}
+        # the metric names the gather's HBM rate; the projection takes most of the step,
+        # so its own roofline goes beside it
+        roofline_projection = {"bound": "mfma", "kernel": "gemm_bf16_nt", "achieved": proj_tflops,
+                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": proj_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                               "flops_per_launch": proj_flops, "avg_launch_ms": kern_ms["project"]}
     kernels["gate_add"] = {"ms": kern_ms["gate_add"], "bound": "hbm", "GB/s": gate_gbs,
                            "frac": gate_gbs / HBM_PEAK_GBS}
     for n in kernels:
@@ -381,6 +387,8 @@ def main():
         "wall_s_timed": wall,
         "setup_s": setup_s,
     }
+    if args.path != "fused":
+        result["roofline_projection"] = roofline_projection
     if args.graph:
         # the same step captured once and replayed K times (launch overhead removed);
         # the decode step is launch-bound, so this is its production form
