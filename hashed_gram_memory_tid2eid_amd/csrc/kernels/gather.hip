@@ -12,7 +12,8 @@
 // it back transposed, so each of its two wave-wide 16-byte stores writes 1 KB
 // of consecutive output (whole cache lines; without the staging each store
 // instruction would leave 16-byte holes and the memory system would write
-// partial lines).  Each lane keeps UNROLL chunks in flight.
+// partial lines).  Each lane keeps UNROLL chunks in flight: two, or one for
+// small calls (decode steps), which then spread over twice as many workgroups.
 //
 // Dequant of a chunk: 16 e4m3fn bytes -> 16 fp32 (hardware conversion,
 // v_cvt_pk_f32_fp8), times the scale (one v_mul_f32 each: exactly the IEEE
@@ -35,6 +36,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 2;  // chunks in flight per lane (measured: 2 beats 4 and 8)
+// below this many workgroups at kGatherUnroll, a call runs with one chunk per lane
+constexpr uint64_t kGatherSmallBlocks = 512;
 
 // q = n / d for 0 <= n < 2^31 via a 64-bit multiply: m = ceil(2^s / d) with
 // s = 31 + ceil(log2 d) is exact on that range (round-up multiplier method).
@@ -82,7 +85,7 @@ __device__ __forceinline__ float e8m0_value(uint32_t b) {
   return __uint_as_float(b == 0 ? 0x00400000u : (b == 255 ? 0x7FC00000u : b << 23));
 }
 
-template <bool kBf16Table, bool kF32Out, bool kBlockScale>
+template <bool kBf16Table, bool kF32Out, bool kBlockScale, int UNROLL>
 __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // Per-wave LDS staging for the bf16 path: a lane converts 16 elements (32 B),
@@ -90,20 +93,20 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKA
   // of the two wave-wide 16-byte stores writes 1 KB of consecutive output.
   __shared__ u32x4 stage[kGatherThreads / 64][2][128];
   const bool staged = !kF32Out && a.linear_out;
-  // Grid-stride over blocks of kGatherThreads * kGatherUnroll chunks: one block per
+  // Grid-stride over blocks of kGatherThreads * UNROLL chunks: one block per
   // workgroup normally; a capped grid (tables in host memory) walks several.
-  const uint32_t per_block = kGatherThreads * kGatherUnroll;
+  const uint32_t per_block = kGatherThreads * UNROLL;
   for (uint32_t base = blockIdx.x * per_block; base < a.total; base += gridDim.x * per_block) {
     const uint32_t first = base + threadIdx.x;
 
-    u32x4 raw[kGatherUnroll][kBf16Table ? 2 : 1];
-    float scale[kGatherUnroll];
-    uint32_t tok[kGatherUnroll], seg[kGatherUnroll], chunk[kGatherUnroll];
-    bool live[kGatherUnroll], any[kGatherUnroll];
+    u32x4 raw[UNROLL][kBf16Table ? 2 : 1];
+    float scale[UNROLL];
+    uint32_t tok[UNROLL], seg[UNROLL], chunk[UNROLL];
+    bool live[UNROLL], any[UNROLL];
 
     // Issue every load first so that UNROLL row reads are in flight per lane.
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const uint32_t g = first + (uint32_t)u * kGatherThreads;
       live[u] = g < a.total;
       any[u] = false;
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(GatherKA
     }
 
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const uint32_t e0 = chunk[u] * 16;
       const uint32_t valid = e0 >= a.row_dim ? 0u : (a.row_dim - e0 >= 16 ? 16u : a.row_dim - e0);
       const int64_t obase = (int64_t)tok[u] * a.out_ld + (int64_t)seg[u] * a.seg_pitch + e0;
@@ -224,6 +227,32 @@ static FastDiv make_fastdiv(uint32_t d) {
   return f;
 }
 
+template <int UNROLL>
+static void launch_gather_variant(const GatherArgs& g, const GatherKArgs& a, uint64_t total,
+                                  hipStream_t stream) {
+  const uint32_t per_block = kGatherThreads * UNROLL;
+  uint64_t blocks = (total + per_block - 1) / per_block;
+  if (g.max_blocks > 0 && blocks > (uint64_t)g.max_blocks) blocks = (uint64_t)g.max_blocks;
+  const dim3 grid((unsigned)blocks);
+  const dim3 block(kGatherThreads);
+  if (g.bf16_table) {
+    if (g.f32_out)
+      hipLaunchKernelGGL((gather_dequant_kernel<true, true, false, UNROLL>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gather_dequant_kernel<true, false, false, UNROLL>), grid, block, 0, stream, a);
+  } else if (g.scale_block == 32) {
+    if (g.f32_out)
+      hipLaunchKernelGGL((gather_dequant_kernel<false, true, true, UNROLL>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gather_dequant_kernel<false, false, true, UNROLL>), grid, block, 0, stream, a);
+  } else {
+    if (g.f32_out)
+      hipLaunchKernelGGL((gather_dequant_kernel<false, true, false, UNROLL>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gather_dequant_kernel<false, false, false, UNROLL>), grid, block, 0, stream, a);
+  }
+}
+
 hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
   (void)hipGetLastError();  // drop a stale error another library left on this thread
   GatherKArgs a;
@@ -255,27 +284,11 @@ hipError_t launch_gather_dequant(const GatherArgs& g, hipStream_t stream) {
   a.total = (uint32_t)total;
   a.div_chunks = make_fastdiv(a.chunks);
   a.div_cols = make_fastdiv(a.cols);
-  const uint32_t per_block = kGatherThreads * kGatherUnroll;
-  uint64_t blocks = (total + per_block - 1) / per_block;
-  if (g.max_blocks > 0 && blocks > (uint64_t)g.max_blocks) blocks = (uint64_t)g.max_blocks;
-  const dim3 grid((unsigned)blocks);
-  const dim3 block(kGatherThreads);
-  if (g.bf16_table) {
-    if (g.f32_out)
-      hipLaunchKernelGGL((gather_dequant_kernel<true, true, false>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gather_dequant_kernel<true, false, false>), grid, block, 0, stream, a);
-  } else if (g.scale_block == 32) {
-    if (g.f32_out)
-      hipLaunchKernelGGL((gather_dequant_kernel<false, true, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gather_dequant_kernel<false, false, true>), grid, block, 0, stream, a);
-  } else {
-    if (g.f32_out)
-      hipLaunchKernelGGL((gather_dequant_kernel<false, true, false>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gather_dequant_kernel<false, false, false>), grid, block, 0, stream, a);
-  }
+  const uint64_t blocks2 = (total + kGatherThreads * kGatherUnroll - 1) / (kGatherThreads * kGatherUnroll);
+  if (g.max_blocks == 0 && blocks2 < kGatherSmallBlocks)
+    launch_gather_variant<1>(g, a, total, stream);
+  else
+    launch_gather_variant<kGatherUnroll>(g, a, total, stream);
   return hipGetLastError();
 }
 
