@@ -1,5 +1,7 @@
-// gemm.hip -- the wkv down-projection v = E W^T on the CDNA4 matrix cores.
-// Included into engram_device.hip.
+// gemm.hip -- the wkv down-projection v = E W^T on the CDNA4 matrix cores
+// ([VeOmni#1370] "feat: support DeepSeek-V4.1-Flash in SeedOmni", config commit:
+// the Engram connection projects the concatenated retrieved rows to the hidden
+// size before its gate).  Included into engram_device.hip.
 //
 // C[M][N] (fp32) = A[M][K] (bf16, row-major) * B[N][K]^T (bf16, row-major):
 // both operands are K-contiguous, the layout the gathered token rows and the

@@ -1,7 +1,9 @@
 // gemm_gather.hip -- fused gather + row-wise dequant + wkv projection:
 //   v[t][o] = sum_k W[o][k] * bf16(fp32(e4m3(table[row_ids[t][seg]][k_in_seg])) * scale)
-// without writing the gathered rows to HBM.  Included into engram_device.hip
-// after gemm.hip (shares its swizzle and wait helpers).
+// without writing the gathered rows to HBM ([VeOmni#1370] "feat: support
+// DeepSeek-V4.1-Flash in SeedOmni": the PR summary's row-wise FP8 dequant on
+// lookup and the config commit's wkv projection, done in one kernel).  Included
+// into engram_device.hip after gemm.hip (shares its swizzle and wait helpers).
 //
 // Same tile and wave layout as gemm_bf16_nt_kernel (256 x 256, 8 waves of
 // 128 x 64, v_mfma_f32_32x32x16_bf16, stages of 64 k), with the A operand taken

@@ -6,6 +6,12 @@ site engram_gather_dequant -> engram_gated_residual, on one stream, no host
 synchronisation, no allocation (path "split", the default).  Path "fused" (e4m3fn tables only) replaces the
 gather and the projection by engram_gather_project, which keeps the gathered
 rows on chip: no [T][k_pad] bf16 row buffer, at a lower projection rate.
+
+The order follows the pages' forward: one hash pass over the flattened batch
+before the layers ([vLLM-V41] "vllm/models/deepseek_v41/nvidia/model",
+DeepseekV4Model.forward), then each Engram site writes its gated memory into the
+residual streams ahead of its layer ([NeMo-V41]
+"nemo_automodel.components.models.deepseek_v41.model", the forward contract).
 """
 from __future__ import annotations
 
