@@ -197,6 +197,45 @@ def test_store_rollback_host_errors_need_no_device():
     assert rc == eng.ENGRAM_E_ARG
 
 
+def test_projection_and_gate_host_errors_need_no_device():
+    """The projection, split-K and gate calls check sizes, leading dimensions and
+    alignment on the host and return before any launch."""
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg)
+    lib = eng._lib
+    P = ctypes.c_void_p
+    K = L.info.k_pad
+    ok = P(256)
+    # leading dimensions below k_pad or not a multiple of 8 elements
+    assert lib.engram_project(L.handle, ok, K - 8, ok, K, cfg.hidden, ok, 4, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_project(L.handle, ok, K, ok, K + 4, cfg.hidden, ok, 4, None) == eng.ENGRAM_E_ALIGN
+    # operands not 16-byte aligned
+    assert lib.engram_project(L.handle, P(264), K, ok, K, cfg.hidden, ok, 4, None) == eng.ENGRAM_E_ALIGN
+    # negative token count, no hidden
+    assert lib.engram_project(L.handle, ok, K, ok, K, cfg.hidden, ok, -1, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_project(L.handle, ok, K, ok, K, 0, ok, 4, None) == eng.ENGRAM_E_ARG
+    # split-K: at least one split, and k_pad a multiple of 64 x splits (768 = 64 x 12)
+    assert lib.engram_project_splitk(L.handle, ok, K, ok, K, cfg.hidden, ok, 0, 4, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_project_splitk(L.handle, ok, K, ok, K, cfg.hidden, ok, 5, 4, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_project_splitk(L.handle, ok, K, ok, K, cfg.hidden, ok, 4, 0, None) == 0
+    # the gate: hc_mult 4 only, hidden a multiple of 8 up to 8,192, 16-byte aligned rows
+    assert lib.engram_gate_add_partials(L.handle, ok, 2, cfg.hidden, 2, None, ok, None, 4,
+                                        None) == eng.ENGRAM_E_UNSUPPORTED
+    assert lib.engram_gate_add_partials(L.handle, ok, 2, 8200, 4, None, ok, None, 4,
+                                        None) == eng.ENGRAM_E_UNSUPPORTED
+    assert lib.engram_gate_add_partials(L.handle, ok, 0, cfg.hidden, 4, None, ok, None, 4,
+                                        None) == eng.ENGRAM_E_ARG
+    assert lib.engram_gate_add_partials(L.handle, ok, 2, cfg.hidden, 4, None, ok, P(260), 4,
+                                        None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_gate_add(L.handle, P(260), cfg.hidden, 4, None, ok, 4, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_gate_add(L.handle, None, cfg.hidden, 4, None, ok, 4, None) == eng.ENGRAM_E_ARG
+    # the chained call checks the gate's shape before it launches the projection
+    assert lib.engram_gated_residual(L.handle, ok, K, ok, K, cfg.hidden, 3, None, ok, ok, 4,
+                                     None) == eng.ENGRAM_E_UNSUPPORTED
+    assert lib.engram_gated_residual(L.handle, ok, K, ok, K, cfg.hidden, 4, None, ok, P(260), 4,
+                                     None) == eng.ENGRAM_E_ALIGN
+
+
 def test_multi_site_layout_matches_oracle_and_pages(golden):
     """Two sites, 8 heads, floor 16,000,000, one table per site: the product's
     primes and offsets equal the oracle's, and each site's table size is the
