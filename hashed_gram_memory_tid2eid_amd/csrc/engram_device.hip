@@ -2,6 +2,8 @@
 // per-device status word and every kernel of the Engram hot path (gfx950).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "internal.h"
 
 namespace engram {
@@ -11,6 +13,21 @@ namespace engram {
 __device__ int g_device_status;
 
 __device__ __forceinline__ void latch_error(int status) { atomicCAS(&g_device_status, 0, status); }
+
+// Raises a kernel's dynamic-LDS limit on the current device, once per device
+// (bit d of `done` records device d; two threads that both see the bit clear both
+// set the same value, which is harmless).
+static hipError_t ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 hipError_t read_and_clear_device_error(hipStream_t stream, int* status) {
   hipError_t e = hipStreamSynchronize(stream);

@@ -296,13 +296,10 @@ static hipError_t launch_gemm_tile(const GemmArgs& g, hipStream_t stream) {
   a.k_chunk = g.K / splits;
   a.c_split_stride = g.c_split_stride;
   const size_t lds_bytes = (size_t)STAGES * STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_nt_kernel<BM, BN, WMW, WNW, STAGES>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&gemm_bf16_nt_kernel<BM, BN, WMW, WNW, STAGES>), (int)lds_bytes, lds_set);
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
   hipLaunchKernelGGL((gemm_bf16_nt_kernel<BM, BN, WMW, WNW, STAGES>), dim3(grid, (unsigned)splits),
                      dim3(64 * WMW * WNW), lds_bytes, stream, a);

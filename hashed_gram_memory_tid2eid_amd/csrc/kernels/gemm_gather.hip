@@ -363,13 +363,10 @@ hipError_t launch_gemm_gather_fp8(const GatherGemmArgs& g, hipStream_t stream) {
   a.tiles_n = (g.N + kGgBN - 1) / kGgBN;
   a.group_m = 2;
   a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_gather_fp8_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGgLDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e =
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_gather_fp8_kernel), kGgLDS, lds_set);
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
   hipLaunchKernelGGL(gemm_gather_fp8_kernel, dim3(grid), dim3(kGgThreads), kGgLDS, stream, a);
   return hipGetLastError();
