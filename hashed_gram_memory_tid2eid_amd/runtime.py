@@ -132,6 +132,7 @@ class Engram:
         self.pre_rows = [[torch.empty((max_tokens, info.k_pad), dtype=torch.bfloat16, device=dev)
                           for _ in range(num_sites)] for _ in range(prefetch_slots)]
         self.pre_free = [None] * prefetch_slots
+        self.pre_pending = [set() for _ in range(prefetch_slots)]  # sites not yet applied
         self._next_slot = 0
 
     # single-site views
@@ -212,6 +213,10 @@ class Engram:
         if T > self.max_tokens:
             raise ValueError(f"{T} tokens > max_tokens {self.max_tokens}")
         slot = self._next_slot
+        if self.pre_pending[slot]:
+            raise RuntimeError(f"prefetch slot {slot} still holds a call whose sites "
+                               f"{sorted(self.pre_pending[slot])} are not applied; apply it first "
+                               f"or construct with more prefetch_slots")
         self._next_slot = (slot + 1) % len(self.pre_rows)
         if self.pre_free[slot] is not None:
             stream.wait_event(self.pre_free[slot])
@@ -223,19 +228,24 @@ class Engram:
         ready = torch.cuda.Event()
         ready.record(stream)
         self.pre_free[slot] = None
+        self.pre_pending[slot] = set(range(self.num_sites))
         return Prefetched(slot=slot, T=T, ready=ready)
 
     def apply(self, pre: "Prefetched", site: int, streams, *, keep=None, stream=None):
         """Projection and gate of one site of a prefetched call, on ``stream``
         (default: the current stream), after the prefetch has landed."""
         import torch
+        if site not in self.pre_pending[pre.slot]:
+            raise RuntimeError(f"site {site} of prefetch slot {pre.slot} is already applied "
+                               f"(or the slot was refilled)")
         st = stream if stream is not None else torch.cuda.current_stream()
         st.wait_event(pre.ready)
         engram_gated_residual(self.layout, self.pre_rows[pre.slot][site], self.site_weights[site],
                               streams, self.v, keep=keep, T=pre.T, stream=st)
         done = torch.cuda.Event()
         done.record(st)
-        self.pre_free[pre.slot] = done
+        self.pre_free[pre.slot] = done  # the last site's apply is the slot's last reader
+        self.pre_pending[pre.slot].discard(site)
         return streams
 
 

@@ -135,3 +135,35 @@ def test_fused_path_refuses_host_tables(eng):
         eng.engram_gather_project(site.site.layout, h_data, h_scale, rid, site.site.weight, v)
     assert ex.value.status == eng.ENGRAM_E_UNSUPPORTED
     _free()
+
+
+def test_prefetch_refuses_to_overwrite_an_unapplied_slot(eng):
+    """With two slots, a third prefetch before the first call is applied would
+    overwrite rows an apply still has to read: it raises instead.  Applying the
+    first call frees its slot; applying a site twice raises too."""
+    cfg = ei.get_config("tiny")
+    batch = ei.make_batch(cfg)
+    ref = Site(cfg, max_tokens=batch.T)
+    pipe = eng.Engram(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+                      heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+                      table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes,
+                      tid2eid=ref.tid2eid, tables=ref.tables.data, scales=ref.tables.scale,
+                      weight=ref.weight, hidden=cfg.hidden, max_tokens=batch.T, prefetch_slots=2)
+    tok, cu = _d(batch.tokens), _d(batch.cu_seqlens)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    p0 = pipe.prefetch(tok, cu, stream=side)
+    p1 = pipe.prefetch(tok, cu, stream=side)
+    with pytest.raises(RuntimeError):
+        pipe.prefetch(tok, cu, stream=side)
+    x = ei.make_streams(cfg, batch.T, DEV)
+    pipe.apply(p0, 0, x)
+    with pytest.raises(RuntimeError):
+        pipe.apply(p0, 0, x)
+    p2 = pipe.prefetch(tok, cu, stream=side)  # slot 0 is free again
+    pipe.apply(p1, 0, x)
+    pipe.apply(p2, 0, x)
+    torch.cuda.synchronize()
+    assert eng.engram_get_error() == 0
+    del ref, pipe
+    _free()
