@@ -352,10 +352,14 @@ def main():
                                      "frac": gather_gbs / HBM_PEAK_GBS}
         kernels["project"] = {"ms": kern_ms["project"], "bound": "mfma", "TFLOP/s": proj_tflops,
                               "frac": proj_tflops / BF16_PEAK_TFLOPS}
+        traffic = measured_traffic(cfg)
         roofline = {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
-                    "traffic": measured_traffic(cfg), "bytes_per_launch": gather_bytes,
+                    "traffic": traffic, "bytes_per_launch": gather_bytes,
                     "avg_launch_ms": kern_ms["gather_dequant"]}
+        if traffic is not None:
+            # the HBM rate the counters imply for this run's launch time
+            kernels["gather_dequant"]["hbm_GB/s_measured_bytes"] = gbs(traffic, kern_ms["gather_dequant"])
         # the metric names the gather's HBM rate; the projection takes most of the step,
         # so its own roofline goes beside it
         roofline_projection = {"bound": "mfma", "kernel": "gemm_bf16_nt", "achieved": proj_tflops,
