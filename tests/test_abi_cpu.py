@@ -289,3 +289,13 @@ def test_multi_site_fit_is_largest_floor():
     def fits(fl):
         return all(int(l.primes.sum()) <= rows for l in oracle.site_layouts(2, 2, fl, True))
     assert fits(f) and not fits(f + 1)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it exits with a message, before it
+    touches a device."""
+    import subprocess
+    import sys
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert out.returncode == 2 and "one GPU" in out.stderr

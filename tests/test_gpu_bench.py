@@ -1,0 +1,43 @@
+"""bench.py keeps its output contract: one JSON line with the metric, the
+whole-job value, the roofline of the gather and of the projection, the per-kernel
+breakdown and the oracle's CPU rate.  Runs the tiny workload in a child process
+(a few seconds)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line_contract():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    out = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--config", "tiny",
+                          "--steps", "3", "--warmup", "1", "--cpu-budget", "1"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert out.returncode == 0, out.stderr[-2000:]
+    lines = [ln for ln in out.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, out.stdout
+    d = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
+    assert d["value"] == pytest.approx(d["config"]["tokens_per_step"] / (d["ms_per_step"] * 1e-3), rel=1e-6)
+    assert "workload" in d["config"]
+    r = d["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in r, k
+    assert r["bound"] == "hbm" and r["frac"] == pytest.approx(r["achieved"] / r["peak"])
+    assert d["roofline_projection"]["bound"] == "mfma"
+    c = d["cpu_baseline"]
+    for k in ("value", "unit", "cores", "kind", "sample"):
+        assert k in c, k
+    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0
+
