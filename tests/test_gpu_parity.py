@@ -359,6 +359,46 @@ def test_prefill_parity(eng):
     _free()
 
 
+def test_prefill_with_image_spans(eng):
+    """The prefill workload with image spans (runs of dead positions, up to 64 long):
+    compressed ids and row ids exact on every token, the streams of dead tokens
+    untouched bit for bit, and sampled streams (including the three positions after
+    each span, whose lookback the span blocks) within tolerance of the oracle."""
+    cfg = ei.get_config("prefill")
+    b0 = ei.make_batch(cfg)
+    T = b0.T
+    dead = ei.make_dead_spans(T, 21, n_spans=48, max_len=64)
+    batch = ei.Batch(tokens=b0.tokens, cu_seqlens=b0.cu_seqlens, seq_start=b0.seq_start,
+                     slots=b0.slots, dead=dead)
+    site = Site(cfg, max_tokens=T)
+    db = site.device_batch(batch)
+    streams = ei.make_streams(cfg, T, DEV)
+    x_all = bf16_bits_np(streams)
+    site.site.forward(db["tokens"], db["cu_seqlens"], streams, seq_start=db["seq_start"],
+                      dead=db["dead"], keep=db["keep"])
+    torch.cuda.synchronize()
+    _no_device_error(eng, "prefill with image spans")
+    e_ref, r_ref = site.oracle_hash(batch)
+    assert np.array_equal(site.site.eids[:T].cpu().numpy(), e_ref)
+    assert np.array_equal(site.site.row_ids[:T].cpu().numpy(), r_ref)
+    y = bf16_bits_np(streams)
+    keep = (dead == 0).astype(np.uint8)
+    assert np.array_equal(y[keep == 0], x_all[keep == 0]), "a dead token's streams changed"
+    after = [p for p in range(1, T) if dead[p - 1] and not dead[p]]
+    near = {p + j for p in after for j in range(3) if p + j < T}
+    idx = np.array(sorted(set(sample_tokens(batch, 96, seed=cfg.seed).tolist()) | near), dtype=np.int64)
+    _, b16 = site.oracle_dequant(r_ref[idx])
+    E = b16.reshape(len(idx), -1)
+    W = site.weight_bits()
+    v_ref = oracle.project(E, W)
+    y_ref, _ = oracle.gate_add(x_all[idx], v_ref, keep=keep[idx])
+    worst = assert_streams_close(y[idx], y_ref, "prefill with image spans")
+    log(f"prefill with {int(dead.sum())} dead positions in {len(after)} spans: ids exact, dead streams "
+        f"untouched, {len(idx)} sampled streams within tolerance (worst {worst:.2e})")
+    del site
+    _free()
+
+
 def test_long_prefill_parity(eng):
     _large_run(eng, "long", f32_sample=4096, stream_sample=96)
     _free()
