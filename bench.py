@@ -212,10 +212,11 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     cfg = ei.get_config(args.config)
-    if args.path == "fused" and (cfg.table_dtype != "fp8" or cfg.scale_block or args.host_tables):
-        print("bench.py: the fused path reads e4m3fn tables with one fp32 scale per row from HBM; "
-              f"workload {cfg.name}{' with host tables' if args.host_tables else ''} needs --path split",
-              file=sys.stderr)
+    if args.path == "fused" and (cfg.table_dtype != "fp8" or (cfg.scale_block and cfg.row_dim > 256)
+                                 or args.host_tables):
+        print("bench.py: the fused path reads e4m3fn tables from HBM (one fp32 scale per row, or e8m0 "
+              f"block scales on rows of at most 256 elements); workload {cfg.name}"
+              f"{' with host tables' if args.host_tables else ''} needs --path split", file=sys.stderr)
         sys.exit(2)
     t_setup = time.perf_counter()
     tid2eid = torch.from_numpy(ei.make_tid2eid(cfg.vocab, cfg.vc)).to(dev)

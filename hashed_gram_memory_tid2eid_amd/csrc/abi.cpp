@@ -300,7 +300,9 @@ extern "C" int engram_gather_project(const engram_layout* L, const void* const* 
   if (!L || T < 0 || hidden < 1 || !d_tables || !d_scales) return ENGRAM_E_ARG;
   if (site < 0 || site >= L->num_sites) return ENGRAM_E_ARG;
   if (L->desc.table_dtype != ENGRAM_DTYPE_FP8_E4M3FN) return ENGRAM_E_UNSUPPORTED;
-  if (L->scale_block != 0) return ENGRAM_E_UNSUPPORTED;
+  // (1, 32) block scales: a converting thread keeps a row's e8m0 bytes in registers,
+  // at most 8 of them (rows of up to 256 elements, the released layout)
+  if (L->scale_block != 0 && L->desc.row_dim > 8 * 32) return ENGRAM_E_UNSUPPORTED;
   if (T == 0) return ENGRAM_OK;
   if (!d_row_ids || !d_w || !d_v) return ENGRAM_E_ARG;
   const int64_t pitch = L->desc.row_pitch_bytes;
@@ -313,7 +315,12 @@ extern "C" int engram_gather_project(const engram_layout* L, const void* const* 
   if (rc != ENGRAM_OK) return rc;
   for (int n = 0; n < 3; ++n)  // rows stream through direct-to-LDS loads: HBM tables only
     if (in_host_memory(g.table[n]) || in_host_memory(scale[n])) return ENGRAM_E_UNSUPPORTED;
-  for (int n = 0; n < 3; ++n) g.scale[n] = static_cast<const float*>(scale[n]);
+  for (int n = 0; n < 3; ++n) {
+    // a row's 8 e8m0 bytes are read with one 8-byte load
+    if (L->scale_block != 0 && L->desc.row_dim == 8 * 32 && !aligned(scale[n], 8)) return ENGRAM_E_ALIGN;
+    g.scale[n] = scale[n];
+  }
+  g.scale_block = L->scale_block;
   g.row_ids = d_row_ids + (int64_t)site * L->cols;
   g.rid_ld = L->all_cols;
   g.per_site_table = L->per_site_table;

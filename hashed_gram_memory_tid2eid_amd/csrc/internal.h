@@ -117,7 +117,8 @@ hipError_t launch_gemm_bf16_nt(const GemmArgs& a, hipStream_t stream);
 // A is the dequantised concatenation of the rows that row_ids[t] names.
 struct GatherGemmArgs {
   const uint8_t* table[3];
-  const float* scale[3];
+  const void* scale[3];    // float [rows] or uint8 e8m0 [rows][D/32]
+  int32_t scale_block;     // 0 or 32
   int64_t rows[3];
   const int32_t* row_ids;  // the site's first column; tokens rid_ld ints apart
   int32_t rid_ld;

@@ -20,7 +20,9 @@
 // A stage never straddles two segments (seg_pitch is a multiple of 64), so a
 // stage reads one table row per token; a thread converts the same four tile rows
 // in every stage and keeps their scales in registers, refreshed when the
-// segment changes.
+// segment changes: one fp32 scale per row, or, for (1, 32)-blocked tables, the
+// row's e8m0 bytes (at most 8: rows of up to 256 elements, the released layout)
+// from which each stage picks its block's exponent.
 
 namespace engram {
 
@@ -28,9 +30,10 @@ struct GatherGemmKArgs {
   const uint8_t* t0;
   const uint8_t* t1;
   const uint8_t* t2;
-  const float* s0;
-  const float* s1;
-  const float* s2;
+  const void* s0;           // float [rows], or uint8 e8m0 [rows][nblk]
+  const void* s1;
+  const void* s2;
+  int32_t nblk;             // e8m0 bytes per row (block scales)
   int32_t r0, r1, r2;       // rows per table
   const int32_t* row_ids;   // the site's first column; tokens rid_ld ints apart
   int32_t rid_ld;
@@ -59,13 +62,15 @@ __device__ __forceinline__ int gg_order(const GatherGemmKArgs& a, int seg) {
 __device__ __forceinline__ const uint8_t* gg_table(const GatherGemmKArgs& a, int n) {
   return n == 0 ? a.t0 : (n == 1 ? a.t1 : a.t2);
 }
-__device__ __forceinline__ const float* gg_scale(const GatherGemmKArgs& a, int n) {
+__device__ __forceinline__ const void* gg_scale(const GatherGemmKArgs& a, int n) {
   return n == 0 ? a.s0 : (n == 1 ? a.s1 : a.s2);
 }
+constexpr int kGgMaxBlocks = 8;  // e8m0 bytes a converting thread keeps per row
 __device__ __forceinline__ int gg_rows(const GatherGemmKArgs& a, int n) {
   return n == 0 ? a.r0 : (n == 1 ? a.r1 : a.r2);
 }
 
+template <bool kBlockScale>
 __global__ __launch_bounds__(kGgThreads, 1) void gemm_gather_fp8_kernel(GatherGemmKArgs a) {
   constexpr int BK = kGgBK;
   constexpr int WM = kGgBM / kGgWM, WN = kGgBN / kGgWN, TM = WM / 32, TN = WN / 32;
@@ -149,20 +154,34 @@ __global__ __launch_bounds__(kGgThreads, 1) void gemm_gather_fp8_kernel(GatherGe
   const int cpiece = tid & 7;
   int conv_seg = -1;
   float cscale[4];  // per phase row; 0 for rows past M and bad row ids (they convert to zeros)
+  uint32_t cblk[4][kBlockScale ? 2 : 1];  // block scales: the row's e8m0 bytes, little-endian
   auto set_conv_segment = [&](int seg) {
     const int n = gg_order(a, seg);
-    const float* sc = gg_scale(a, n);
     const int rows = gg_rows(a, n);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m = m0 + 64 * q + (tid >> 3);
       cscale[q] = 0.f;
+      if (kBlockScale) cblk[q][0] = cblk[q][kBlockScale ? 1 : 0] = 0u;
       if (m < a.M) {
         const int r = a.row_ids[(int64_t)m * a.rid_ld + seg];
-        if (r < 0 || r >= rows)
+        if (r < 0 || r >= rows) {
           latch_error(ENGRAM_E_ROW_RANGE);
-        else
-          cscale[q] = sc[r];
+        } else if (kBlockScale) {
+          const uint8_t* sb = static_cast<const uint8_t*>(gg_scale(a, n)) + (int64_t)r * a.nblk;
+          if (a.nblk == kGgMaxBlocks) {  // 8-byte aligned: one load
+            typedef unsigned int u32x2s __attribute__((ext_vector_type(2)));
+            const u32x2s w = *reinterpret_cast<const u32x2s*>(sb);
+            cblk[q][0] = w[0];
+            cblk[q][kBlockScale ? 1 : 0] = w[1];
+          } else {
+            for (int b = 0; b < a.nblk; ++b)
+              cblk[q][b >> 2] |= (uint32_t)sb[b] << (8 * (b & 3));
+          }
+          cscale[q] = 1.f;  // marks a valid row
+        } else {
+          cscale[q] = static_cast<const float*>(gg_scale(a, n))[r];
+        }
       }
     }
     conv_seg = seg;
@@ -177,7 +196,11 @@ __global__ __launch_bounds__(kGgThreads, 1) void gemm_gather_fp8_kernel(GatherGe
     typedef float f32x2g __attribute__((ext_vector_type(2)));
     typedef unsigned int u32x4g __attribute__((ext_vector_type(4)));
     const u32x2g w = *reinterpret_cast<const u32x2g*>(src);
-    const float s = cscale[q];
+    float s = cscale[q];
+    if (kBlockScale && s != 0.f) {  // the exponent of this piece's 32-element block
+      const int blk = (e0 >> 5) & (kGgMaxBlocks - 1);  // padding pieces are zeroed below
+      s = e8m0_value((cblk[q][blk >> 2] >> (8 * (blk & 3))) & 0xFFu);
+    }
     float f[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -341,6 +364,7 @@ hipError_t launch_gemm_gather_fp8(const GatherGemmArgs& g, hipStream_t stream) {
   a.s0 = g.scale[0];
   a.s1 = g.scale[1];
   a.s2 = g.scale[2];
+  a.nblk = g.scale_block ? g.row_dim / g.scale_block : 0;
   a.r0 = (int32_t)g.rows[0];
   a.r1 = (int32_t)g.rows[1];
   a.r2 = (int32_t)g.rows[2];
@@ -363,12 +387,22 @@ hipError_t launch_gemm_gather_fp8(const GatherGemmArgs& g, hipStream_t stream) {
   a.tiles_n = (g.N + kGgBN - 1) / kGgBN;
   a.group_m = 2;
   a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
-  static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_gather_fp8_kernel), kGgLDS, lds_set);
-  if (e != hipSuccess) return e;
+  if (g.scale_block != 0 && (g.scale_block != 32 || a.nblk < 1 || a.nblk > kGgMaxBlocks))
+    return hipErrorInvalidValue;  // the entry point refuses these first
   const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
-  hipLaunchKernelGGL(gemm_gather_fp8_kernel, dim3(grid), dim3(kGgThreads), kGgLDS, stream, a);
+  if (g.scale_block) {
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_gather_fp8_kernel<true>),
+                                            kGgLDS, lds_set);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_gather_fp8_kernel<true>, dim3(grid), dim3(kGgThreads), kGgLDS, stream, a);
+  } else {
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_gather_fp8_kernel<false>),
+                                            kGgLDS, lds_set);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_gather_fp8_kernel<false>, dim3(grid), dim3(kGgThreads), kGgLDS, stream, a);
+  }
   return hipGetLastError();
 }
 

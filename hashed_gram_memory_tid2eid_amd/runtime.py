@@ -3,7 +3,7 @@ device buffers.
 
 ``Engram.forward`` = engram_compress_hash (every site in one pass) -> for each
 site engram_gather_dequant -> engram_gated_residual, on one stream, no host
-synchronisation, no allocation (path "split", the default).  Path "fused" (e4m3fn tables only) replaces the
+synchronisation, no allocation (path "split", the default).  Path "fused" (e4m3fn tables) replaces the
 gather and the projection by engram_gather_project, which keeps the gathered
 rows on chip: no [T][k_pad] bf16 row buffer, at a lower projection rate.
 
@@ -78,8 +78,9 @@ class Engram:
         import torch
         if path not in ("split", "fused"):
             raise ValueError(f"unknown path {path!r}")
-        if path == "fused" and (table_dtype != "fp8" or scale_block):
-            raise ValueError("the fused path reads e4m3fn tables with a per-row fp32 scale only")
+        if path == "fused" and (table_dtype != "fp8" or (scale_block and row_dim > 256)):
+            raise ValueError("the fused path reads e4m3fn tables with a per-row fp32 scale, or "
+                             "(1, 32) e8m0 block scales on rows of at most 256 elements")
         if table_split not in ("order", "site"):
             raise ValueError(f"unknown table split {table_split!r}")
         self.path = path

@@ -320,9 +320,12 @@ int engram_project_splitk(const engram_layout* layout, const void* d_rows, int64
  *   layout's row_pitch_bytes must be >= seg_pitch and a multiple of 16 (a row is
  *   read in 64-byte pieces up to seg_pitch; bytes past D are ignored).
  *   d_w, w_ld, hidden, d_v as for engram_project.
+ *   Scales: one fp32 per row, or BLOCK32 e8m0 bytes for rows of at most 256
+ *   elements (the released layout's width); with 256-element rows each scale
+ *   array must be 8-byte aligned.
  * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN, ENGRAM_E_UNSUPPORTED (bf16 tables,
- * BLOCK32 scales, tables in host memory).  Device error: ENGRAM_E_ROW_RANGE (that
- * segment contributes zero). */
+ * BLOCK32 scales on rows wider than 256, tables in host memory).  Device error:
+ * ENGRAM_E_ROW_RANGE (that segment contributes zero). */
 int engram_gather_project(const engram_layout* layout, const void* const* d_tables,
                           const void* const* d_scales, const int32_t* d_row_ids, int32_t site,
                           int32_t T, const void* d_w, int64_t w_ld, int32_t hidden, float* d_v,

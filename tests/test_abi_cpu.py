@@ -171,6 +171,17 @@ def test_gather_project_host_errors_need_no_device():
     rc = lib.engram_gather_project(L.handle, some, None, P(256), 0, 4, P(256), L.info.k_pad,
                                    cfg.hidden, P(256), None)
     assert rc == eng.ENGRAM_E_ARG
+    # e8m0 block scales: rows of at most 256 elements (a thread keeps a row's 8 exponent
+    # bytes in registers), and for 256-element rows 8-byte aligned scale arrays
+    Lwide = _layout(cfg, row_dim=320, row_pitch_bytes=384, scale_layout=eng.ENGRAM_SCALE_BLOCK32_E8M0)
+    rc = lib.engram_gather_project(Lwide.handle, some, some, P(256), 0, 4, P(256), Lwide.info.k_pad,
+                                   cfg.hidden, P(256), None)
+    assert rc == eng.ENGRAM_E_UNSUPPORTED
+    L256 = _layout(cfg, row_dim=256, row_pitch_bytes=256, scale_layout=eng.ENGRAM_SCALE_BLOCK32_E8M0)
+    odd = (P * 3)(P(260), P(260), P(260))
+    rc = lib.engram_gather_project(L256.handle, some, odd, P(256), 0, 4, P(256), L256.info.k_pad,
+                                   cfg.hidden, P(256), None)
+    assert rc == eng.ENGRAM_E_ALIGN
     # empty call is a no-op
     assert lib.engram_gather_project(L.handle, some, some, None, 0, 0, None, L.info.k_pad,
                                      cfg.hidden, None, None) == 0

@@ -198,3 +198,92 @@ def test_fused_second_site_equals_split(eng, split):
         assert eng.engram_get_error() == 0
         assert torch.equal(v_split.view(torch.int32), v_fused.view(torch.int32)), f"site {s}"
     _free()
+
+
+def _random_e8m0_tables(rows, pitch, D, seed, n_tables=3):
+    """Random e4m3fn bytes (no NaN codes) with NaN bytes in the row padding, and
+    (1, 32) e8m0 block scales: mostly exponents near 2^-7, some rows at the
+    smallest codes (0 = 2^-127, 1 = 2^-126) and some up to 2^3."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    tabs, scales = [], []
+    for _ in range(n_tables):
+        t = torch.randint(0, 256, (rows, pitch), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+        t[t == 0x7F] = 0x7E
+        t[t == 0xFF] = 0xFE
+        if pitch > D:
+            t[:, D:] = 0xFF
+        tabs.append(t.reshape(-1))
+        s = torch.randint(110, 131, (rows, D // 32), generator=g, device=DEV, dtype=torch.int32)
+        s[::97] = 0
+        s[1::89] = 1
+        scales.append(s.to(torch.uint8).reshape(-1))
+    return tabs, scales
+
+
+@pytest.mark.parametrize("M,N,H,D,pitch", [
+    (1, 8, 1, 32, 64),
+    (77, 200, 1, 96, 128),
+    (300, 512, 2, 128, 128),
+    (700, 512, 8, 256, 256),
+    (4097, 1024, 8, 256, 256),
+])
+def test_fused_block_scales_equal_split_bitwise(eng, M, N, H, D, pitch):
+    """(1, 32) e8m0 block-scaled tables: the fused kernel picks each 32-element
+    block's exponent from the row's scale bytes and equals gather + projection bit
+    for bit (rows of up to 256 elements, the released layout's width)."""
+    rows = 40_000
+    L = eng.engram_layout_create(vocab_size=8, compressed_vocab=4, pad_token_id=7, heads_per_order=H,
+                                 rows=[rows] * 3, row_dim=D, table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN,
+                                 row_pitch_bytes=pitch, scale_layout=eng.ENGRAM_SCALE_BLOCK32_E8M0)
+    info = L.info
+    tabs, scales = _random_e8m0_tables(rows, pitch, D, seed=M * 11 + D)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M + 17 * N)
+    rid = torch.randint(0, rows, (M, 3, H), generator=g, device=DEV, dtype=torch.int32)
+    w = (torch.randn((N, info.k_pad), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    e16 = torch.empty((M, info.k_pad), dtype=torch.bfloat16, device=DEV)
+    v_split = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    v_fused = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    eng.engram_gather_dequant(L, tabs, scales, rid, e16)
+    eng.engram_project(L, e16, w, v_split)
+    eng.engram_gather_project(L, tabs, scales, rid, w, v_fused)
+    torch.cuda.synchronize()
+    assert eng.engram_get_error() == 0
+    assert torch.equal(v_split.view(torch.int32), v_fused.view(torch.int32)), \
+        f"fused differs from split on {int((v_split != v_fused).sum())} outputs"
+    del tabs, scales
+    _free()
+
+
+def test_fused_released_layout_two_sites_equals_split(eng):
+    """The v41_small workload (two sites sharing one hash pass, one table per site,
+    3 x 8 heads of 256 elements, e8m0 block scales) through Engram(path="fused") and
+    the split path on the same inputs: every stream bit for bit."""
+    cfg = ei.get_config("v41_small")
+    batch = ei.make_batch(cfg)
+    T = batch.T
+    tid = torch.from_numpy(ei.make_tid2eid(cfg.vocab, cfg.vc)).to(DEV)
+    tables = [ei.make_tables(cfg, DEV, site=s) for s in range(cfg.n_sites)]
+    weights = [ei.make_weight(cfg, DEV, site=s) for s in range(cfg.n_sites)]
+    outs = {}
+    for path in ("split", "fused"):
+        e = eng.Engram(vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+                       heads_per_order=cfg.heads, rows=[cfg.rows], row_dim=cfg.row_dim,
+                       table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes, tid2eid=tid,
+                       tables=[t.data for t in tables], scales=[t.scale for t in tables], weight=weights,
+                       hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=T, hash_floor=cfg.hash_floor,
+                       num_sites=cfg.n_sites, table_split=cfg.table_split, scale_block=cfg.scale_block,
+                       path=path)
+        streams = [ei.make_streams(cfg, T, DEV, step=s) for s in range(cfg.n_sites)]
+        e.forward(torch.from_numpy(batch.tokens).to(DEV), torch.from_numpy(batch.cu_seqlens).to(DEV),
+                  streams)
+        torch.cuda.synchronize()
+        assert eng.engram_get_error() == 0
+        outs[path] = [bf16_bits_np(x) for x in streams]
+        del e
+    for s in range(cfg.n_sites):
+        assert np.array_equal(outs["split"][s], outs["fused"][s]), f"site {s}"
+    log(f"v41_small: fused and split paths give the same streams on all {T} tokens of both sites")
+    del tables, weights
+    _free()
