@@ -293,13 +293,9 @@ def main():
                 eng.engram_gather_dequant(L, site.site_tables[si], site.site_scales[si], site.row_ids,
                                           site.rows, site=si, T=T)
                 mark()
-                if site.proj_splits > 1:
-                    eng.engram_project_splitk(L, site.rows, site.site_weights[si], site.partials,
-                                              site.proj_splits, T=T)
-                else:
-                    eng.engram_project(L, site.rows, site.site_weights[si], site.v, T=T)
+                site.project(si, site.rows, T)
                 mark()
-            if args.path != "fused" and site.proj_splits > 1:
+            if args.path != "fused" and site.projection_kind(si, T) == "splitk":
                 eng.engram_gate_add_partials(L, site.partials, site.proj_splits, site_streams[si], T=T)
             else:
                 eng.engram_gate_add(L, site.v, site_streams[si], T=T)
@@ -363,7 +359,10 @@ def main():
             kernels["gather_dequant"]["hbm_GB/s_measured_bytes"] = gbs(traffic, kern_ms["gather_dequant"])
         # the metric names the gather's HBM rate; the projection takes most of the step,
         # so its own roofline goes beside it
-        roofline_projection = {"bound": "mfma", "kernel": "gemm_bf16_nt", "achieved": proj_tflops,
+        pkind = site.projection_kind(0, T)
+        roofline_projection = {"bound": "mfma",
+                               "kernel": "gemm_bf16_nt_packed" if pkind == "packed" else "gemm_bf16_nt",
+                               "achieved": proj_tflops,
                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": proj_tflops / BF16_PEAK_TFLOPS, "traffic": None,
                                "flops_per_launch": proj_flops, "avg_launch_ms": kern_ms["project"]}
@@ -391,7 +390,8 @@ def main():
                    "k_pad": site.info.k_pad, "path": args.path, "sites": NS,
                    "table_split": cfg.table_split, "scale_block": cfg.scale_block,
                    "tables_in": "pinned host memory" if args.host_tables else "HBM",
-                   "proj_splits": site.proj_splits},
+                   "proj_splits": site.proj_splits,
+                   "projection": site.projection_kind(0, T) if args.path != "fused" else "fused"},
         "roofline": roofline,
         "kernels": kernels,
         "wall_s_timed": wall,
@@ -472,11 +472,24 @@ def main():
         e[1].record()
         for _ in range(reps):
             eng.engram_gather_dequant(L, site.tables, site.scales, site.row_ids, site.rows, T=T)
-            eng.engram_project(L, site.rows, site.weight, site.v, T=T)
+            site.project(0, site.rows, T)
         e[2].record()
         torch.cuda.synchronize()
         eng.check_device_error("fused comparison")
         f_ms, s_ms = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+        if site.projection_kind(0, T) == "packed":
+            # the projection from the unpacked weight (two operands through LDS) on the same rows
+            v_plain = torch.empty_like(site.v)
+            eng.engram_project(L, site.rows, site.weight, v_plain, T=T)
+            e[0].record()
+            for _ in range(reps):
+                eng.engram_project(L, site.rows, site.weight, v_plain, T=T)
+            e[1].record()
+            torch.cuda.synchronize()
+            result["alt_paths_projection"] = {
+                "gemm_bf16_nt_unpacked_ms": e[0].elapsed_time(e[1]) / reps,
+                "bitwise_equal_v": bool(torch.equal(v_plain.view(torch.int32), site.v.view(torch.int32))),
+                "reps": reps}
         result["alt_paths"] = {
             "gather_project_fused": {"ms": f_ms, "TFLOP/s": proj_flops / (f_ms * 1e-3) / 1e12,
                                      "bitwise_equal_v": bool(torch.equal(v_alt.view(torch.int32),

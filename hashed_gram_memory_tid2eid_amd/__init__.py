@@ -118,6 +118,9 @@ _sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _
 _sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
 _sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _i32, _P, _P])
 _sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
+_sig("engram_packed_weight_bytes", [_P, _i32, ctypes.POINTER(_i64)])
+_sig("engram_pack_weight", [_P, _P, _i64, _i32, _P, _P])
+_sig("engram_project_packed", [_P, _P, _i64, _P, _i32, _P, _i32, _P])
 _sig("engram_project_splitk", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _i32, _P])
 _sig("engram_gate_add_partials", [_P, _P, _i32, _i32, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
@@ -412,6 +415,38 @@ def engram_project(layout: Layout, rows, w, v, *, T: Optional[int] = None, strea
     _check(_lib.engram_project(layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
                                _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
                                _dev(v, torch.float32, "v"), T, _stream(stream)), "engram_project")
+
+
+def engram_packed_weight_bytes(layout: Layout, hidden: int) -> int:
+    n = _i64(0)
+    _check(_lib.engram_packed_weight_bytes(layout.handle, int(hidden), ctypes.byref(n)),
+           "engram_packed_weight_bytes")
+    return int(n.value)
+
+
+def engram_pack_weight(layout: Layout, w, packed, stream=None):
+    """packed: a device tensor of at least engram_packed_weight_bytes(layout, hidden) bytes."""
+    import torch
+    _need(w.dim() == 2, "w must be [hidden][w_ld]")
+    need = engram_packed_weight_bytes(layout, w.shape[0])
+    _need(packed.numel() * packed.element_size() >= need, f"packed smaller than {need} bytes")
+    _check(_lib.engram_pack_weight(layout.handle, _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
+                                   _dev(packed, None, "packed"), _stream(stream)), "engram_pack_weight")
+
+
+def engram_project_packed(layout: Layout, rows, packed, hidden: int, v, *, T: Optional[int] = None,
+                          stream=None):
+    import torch
+    if T is None:
+        T = rows.shape[0]
+    _need(rows.dim() == 2 and rows.shape[0] >= T, "rows too small")
+    _need(v.dim() == 2 and v.shape[0] >= T and v.shape[1] == hidden, "v must be [T][hidden]")
+    need = engram_packed_weight_bytes(layout, hidden)
+    _need(packed.numel() * packed.element_size() >= need, f"packed smaller than {need} bytes")
+    _check(_lib.engram_project_packed(layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
+                                      _dev(packed, None, "packed"), int(hidden),
+                                      _dev(v, torch.float32, "v"), T, _stream(stream)),
+           "engram_project_packed")
 
 
 def engram_gather_project(layout: Layout, tables: Sequence, scales: Sequence, row_ids, w, v, *,

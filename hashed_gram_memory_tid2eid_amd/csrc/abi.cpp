@@ -268,6 +268,50 @@ extern "C" int engram_project(const engram_layout* L, const void* d_rows, int64_
   return hip_status(engram::launch_gemm_bf16_nt(g, stream));
 }
 
+extern "C" int engram_packed_weight_bytes(const engram_layout* L, int32_t hidden, int64_t* bytes) {
+  if (!L || hidden < 1 || !bytes) return ENGRAM_E_ARG;
+  *bytes = (int64_t)((hidden + 31) / 32) * 32 * L->k_pad * 2;
+  return ENGRAM_OK;
+}
+
+extern "C" int engram_pack_weight(const engram_layout* L, const void* d_w, int64_t w_ld,
+                                  int32_t hidden, void* d_packed, hipStream_t stream) {
+  if (!L || hidden < 1 || !d_w || !d_packed) return ENGRAM_E_ARG;
+  if (w_ld < L->k_pad || w_ld % 8) return ENGRAM_E_ALIGN;
+  if (!aligned(d_w, 16) || !aligned(d_packed, 16)) return ENGRAM_E_ALIGN;
+  engram::PackWeightArgs g;
+  g.W = d_w;
+  g.ldw = w_ld;
+  g.N = hidden;
+  g.K = (int32_t)L->k_pad;
+  g.out = d_packed;
+  return hip_status(engram::launch_pack_weight(g, stream));
+}
+
+extern "C" int engram_project_packed(const engram_layout* L, const void* d_rows, int64_t rows_ld,
+                                     const void* d_packed, int32_t hidden, float* d_v, int32_t T,
+                                     hipStream_t stream) {
+  if (!L || T < 0 || hidden < 1) return ENGRAM_E_ARG;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_rows || !d_packed || !d_v) return ENGRAM_E_ARG;
+  if (rows_ld < L->k_pad || rows_ld % 8) return ENGRAM_E_ALIGN;
+  if (!aligned(d_rows, 16) || !aligned(d_packed, 16) || !aligned(d_v, 4)) return ENGRAM_E_ALIGN;
+  // the kernel addresses one 256-row tile of rows and 8 column tiles of the packed
+  // weight with 32-bit byte offsets
+  if ((int64_t)256 * rows_ld * 2 > INT32_MAX || (int64_t)8 * L->k_pad * 64 > INT32_MAX)
+    return ENGRAM_E_UNSUPPORTED;
+  engram::GemmPackedArgs g;
+  g.A = d_rows;
+  g.Bp = d_packed;
+  g.C = d_v;
+  g.lda = rows_ld;
+  g.ldc = hidden;
+  g.M = T;
+  g.N = hidden;
+  g.K = (int32_t)L->k_pad;
+  return hip_status(engram::launch_gemm_bf16_nt_packed(g, stream));
+}
+
 extern "C" int engram_project_splitk(const engram_layout* L, const void* d_rows, int64_t rows_ld,
                                      const void* d_w, int64_t w_ld, int32_t hidden,
                                      float* d_partials, int32_t splits, int32_t T,

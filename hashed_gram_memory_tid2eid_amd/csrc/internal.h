@@ -113,6 +113,25 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_bf16_nt(const GemmArgs& a, hipStream_t stream);
 
+// The projection weight in matrix-core fragment order (see kernels/gemm_packed.hip):
+// out[N32][K16][64][8] bf16, N32 = ceil(N / 32), K16 = K / 16, rows past N zero.
+struct PackWeightArgs {
+  const void* W;   // bf16 [N][ldw]
+  int64_t ldw;
+  int32_t N, K;    // K multiple of 16
+  void* out;
+};
+hipError_t launch_pack_weight(const PackWeightArgs& a, hipStream_t stream);
+
+struct GemmPackedArgs {
+  const void* A;   // bf16 [M][lda]
+  const void* Bp;  // packed weight of [N][K]
+  float* C;        // f32 [M][ldc]
+  int64_t lda, ldc;
+  int32_t M, N, K;
+};
+hipError_t launch_gemm_bf16_nt_packed(const GemmPackedArgs& a, hipStream_t stream);
+
 // Fused gather + dequant + projection for e4m3fn tables: C = A B^T where row t of
 // A is the dequantised concatenation of the rows that row_ids[t] names.
 struct GatherGemmArgs {

@@ -1,0 +1,314 @@
+// gemm_packed.hip -- the wkv down-projection v = E W^T with W held in matrix-core
+// fragment order ([VeOmni#1370] "feat: support DeepSeek-V4.1-Flash in SeedOmni",
+// config commit: the Engram connection projects the concatenated retrieved rows to
+// the hidden size before its gate).  Included into engram_device.hip after gemm.hip.
+//
+// The weight is static, so it is rearranged once (pack_weight_kernel) into
+//   Wp[N/32][K/16][64 lanes][8 bf16]:
+// the 16 bytes lane l needs as the B operand of v_mfma_f32_32x32x16_bf16 for column
+// tile j and k16 step s (column 32 j + l % 32, k 16 s + 8 (l / 32) .. +8) sit at
+// chunk (j K/16 + s) 64 + l.  A wave then fetches a whole B fragment with one
+// 16-byte-per-lane load of 1 KB of consecutive bytes (8 full cache lines) straight
+// into registers, and B takes no LDS at all: no direct-load writes and no
+// fragment reads.  The LDS keeps only the gathered rows (operand A), in a deeper
+// ring than the two-operand kernel can afford.
+//
+// Tile: 256 x 256 per workgroup, 8 waves as 2 (M) x 4 (N), 128 x 64 per wave (4 x 2
+// tiles of 32 x 32, two waves per SIMD), the same products accumulated in the same
+// k16 order as gemm_bf16_nt_kernel, so C is bit-identical to it.
+// A: direct global->LDS loads of one 128-byte line per row per 64-k stage, in a ring
+// of A_STAGES stages of 32 KB, XOR-swizzled as in gemm.hip.
+// B: a ring of four k16 steps in registers; the fragments of step s of stage kt+1 are
+// requested right after step s of stage kt has been multiplied, one stage ahead.
+//
+// Every iteration issues the same loads (the last stages re-read clamped, in-bounds
+// addresses into slots nothing reads again), so the vector-memory counter waits
+// below are fixed numbers: per iteration, in issue order, B steps 0..2 (2 loads
+// each), the stage wait, A (4 loads), B step 3 (2 loads).
+
+namespace engram {
+
+constexpr int kPackedAStages = 4;  // 4 x 32 KB of A in LDS
+// dword 3 of a buffer resource on gfx9-family parts: 32-bit data format, no swizzle
+constexpr int kBufferRsrcFlags = 0x00020000;
+
+struct GemmPackedKArgs {
+  const __bf16* A;     // bf16 [M][lda]
+  const bf16x8* Bp;    // packed weight, [N32][K16][64] chunks of 8 bf16
+  float* C;            // f32 [M][ldc]
+  int64_t lda, ldc;
+  int32_t M, N, K;     // K multiple of 64
+  int32_t n32;         // ceil(N / 32)
+  int32_t tiles_m, tiles_n, group_m;
+  int32_t vec_store;
+};
+
+__global__ __launch_bounds__(256)
+void pack_weight_kernel(const __bf16* __restrict__ W, int64_t ldw, int32_t N, int32_t K,
+                        int64_t total_chunks, bf16x8* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= total_chunks) return;
+  const int k16 = K >> 4;
+  const int lane = (int)(c & 63);
+  const int64_t t = c >> 6;
+  const int s = (int)(t % k16);
+  const int j = (int)(t / k16);
+  const int n = j * 32 + (lane & 31);
+  const int k = s * 16 + 8 * (lane >> 5);
+  bf16x8 v = {};
+  if (n < N) v = *reinterpret_cast<const bf16x8*>(W + (int64_t)n * ldw + k);
+  out[c] = v;
+}
+
+template <int A_STAGES>
+__global__ __launch_bounds__(512, 1)
+void gemm_bf16_nt_packed_kernel(GemmPackedKArgs a) {
+  constexpr int BM = 256, BN = 256, WN_WAVES = 4, NWAVES = 8;
+  constexpr int BK = kGemmBK;
+  constexpr int WM = 128, WN = 64, TM = 4, TN = 2;
+  constexpr int STAGE = BM * BK * 2;           // 32 KB of A per stage
+  constexpr int AI = BM / 8 / NWAVES;          // 1 KB direct loads per wave per stage
+  constexpr int BL = TN;                       // B loads per k16 step
+  constexpr int PER_ITER = 4 * BL + AI;        // vector-memory loads per iteration
+  static_assert(AI * 8 * NWAVES == BM, "A tile must fill whole load rounds");
+  static_assert(A_STAGES >= 2, "ring needs two stages");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  // ---- tile id: XCD-contiguous runs, then GROUP_M swizzle (as gemm.hip) -------
+  const int ntiles = a.tiles_m * a.tiles_n;
+  int bid = blockIdx.x;
+  if ((ntiles & 7) == 0) {
+    const int per_xcd = ntiles >> 3;
+    bid = (bid & 7) * per_xcd + (bid >> 3);
+  }
+  const int group = a.group_m * a.tiles_n;
+  const int gid = bid / group;
+  const int first_m = gid * a.group_m;
+  const int gm = min(a.tiles_m - first_m, a.group_m);
+  const int in_group = bid - gid * group;
+  const int m0 = (first_m + in_group % gm) * BM;
+  const int n0 = (in_group / gm) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN_WAVES, wn = wave % WN_WAVES;
+  const int nk = a.K / BK;
+  const int k16 = a.K >> 4;
+
+  // Both operands are read through buffer resources (MUBUF): the compiler counts
+  // direct-to-LDS buffer loads and register buffer loads on one in-order vector
+  // memory counter, so its waits for the B registers stay exact (mixing global
+  // direct-to-LDS loads with register loads makes it wait for everything).  Each
+  // resource starts at this tile's first row (column tile) so byte offsets fit
+  // 32 bits; its record count covers exactly the rows (tiles) the tile may read.
+  const int rows_here = min(a.M - m0, BM);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.A + (int64_t)m0 * a.lda), (short)0, (int)((int64_t)rows_here * a.lda * 2), kBufferRsrcFlags);
+  const int jt0 = n0 / 32;
+  const int tiles_here = min(a.n32 - jt0, BN / 32);
+  const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.Bp + (int64_t)jt0 * k16 * 64), (short)0, tiles_here * k16 * 1024, kBufferRsrcFlags);
+
+  // ---- A: direct loads into LDS (wave w, load i fills LDS bytes
+  //      [(NWAVES i + w) KB, +1 KB) of the stage; 8 lanes fetch one whole line).
+  //      Rows past M read row M-1 (never stored).
+  int aoff[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int P = 64 * (i * NWAVES + wave) + lane, row = P >> 3, c = (P & 7) ^ gemm_swz(row);
+    aoff[i] = (min(row, rows_here - 1) * (int)a.lda + 8 * c) * 2;
+  }
+  auto issue_a = [&](int kt) {
+    char* st = smem + (kt % A_STAGES) * STAGE;
+    const int ks = min(kt, nk - 1);  // past the end: an in-bounds stage into a slot no one reads
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (ENGRAM_LDS_AS void*)(st + (i * NWAVES + wave) * 1024), 16,
+                                               aoff[i] + ks * BK * 2, 0, 0, 0);
+  };
+
+  // ---- B: packed fragments; column tiles past N read the last tile (never stored)
+  int boff[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int jt = min(wn * TN + j, tiles_here - 1);
+    boff[j] = (jt * k16 * 64 + lane) * 16;
+  }
+  bf16x8 bfr[4][TN];
+  auto issue_b = [&](int kt, int ks) {
+    const int s = min(kt, nk - 1) * 4 + ks;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bfr[ks][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(brsrc, boff[j] + s * 1024, 0, 0));
+  };
+
+  // ---- A fragment rows and swizzles inside a stage ---------------------------
+  const int lrow = lane & 31, lk = lane >> 5;
+  int arow[TM], aswz[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * WM + i * 32 + lrow;
+    arow[i] = r * BK;
+    aswz[i] = gemm_swz(r);
+  }
+  auto load_a = [&](int kt, int ks, bf16x8* fa) {
+    const __bf16* base = reinterpret_cast<const __bf16*>(smem + (kt % A_STAGES) * STAGE);
+    const int c = ks * 2 + lk;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + arow[i] + 8 * (c ^ aswz[i]));
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- prologue: B of stage 0, then A stages 0 .. A_STAGES-1; wait for A stage 0
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) issue_b(0, ks);
+#pragma unroll
+  for (int s = 0; s < A_STAGES; ++s) issue_a(s);
+  wait_vmcnt<(A_STAGES - 1) * AI>();
+  __builtin_amdgcn_s_barrier();
+
+  // Loads issued after A stage kt+1 when iteration kt waits for it: in steady state
+  // (A_STAGES-2) whole iterations plus B step 3 of the iteration that issued it and
+  // B steps 0..2 of this one; in the first A_STAGES-1 iterations the stage came from
+  // the prologue and fewer loads follow it, fewest at kt = 0.
+  constexpr int WAIT_SS = (A_STAGES - 2) * PER_ITER + 4 * BL;
+  constexpr int WAIT_EARLY = (A_STAGES - 2) * AI + 3 * BL;
+  static_assert(WAIT_SS <= 63 && WAIT_EARLY <= WAIT_SS, "vmcnt field holds 6 bits");
+
+  bf16x8 fa0[TM], fa1[TM];
+  load_a(0, 0, fa0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kt, 1, fa1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, bfr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt + 1, 0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kt, 2, fa0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, bfr[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt + 1, 1);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kt, 3, fa1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, bfr[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt + 1, 2);
+    // this wave has read all of A stage kt once step 3 has landed; the barrier makes
+    // that true for every wave and publishes A stage kt+1, then slot kt % A_STAGES
+    // is refilled with stage kt + A_STAGES
+    wait_lgkmcnt0();
+    if (kt + 1 < A_STAGES) wait_vmcnt<WAIT_EARLY>(); else wait_vmcnt<WAIT_SS>();
+    __builtin_amdgcn_s_barrier();
+    issue_a(kt + A_STAGES);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kt + 1 < nk ? kt + 1 : kt, 0, fa0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, bfr[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt + 1, 3);
+  }
+
+  // ---- epilogue (as gemm.hip): stage one 32-row slab per wave in LDS, write
+  //      whole row segments of C with 16-byte stores.  The clamped loads of the
+  //      last iterations may still be landing in the ring: drain them first.
+  constexpr int PITCH = WN + 4;
+  static_assert(NWAVES * 32 * PITCH * 4 <= A_STAGES * STAGE, "epilogue staging must fit in the ring");
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  float* slab = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
+  const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N) && a.vec_store;
+  constexpr int LANES_PER_ROW = WN / 4;
+  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        slab[r * PITCH + j * 32 + (lane & 31)] = acc[i][j][v];
+      }
+    }
+    const int gm0 = m0 + wm * WM + i * 32;
+    const int gn = n0 + wn * WN + (lane % LANES_PER_ROW) * 4;
+#pragma unroll
+    for (int q = 0; q < 32 / ROWS_PER_PASS; ++q) {
+      const int r = q * ROWS_PER_PASS + lane / LANES_PER_ROW;
+      const f32x4 val = *reinterpret_cast<const f32x4*>(slab + r * PITCH + (lane % LANES_PER_ROW) * 4);
+      const int m = gm0 + r;
+      float* dst = a.C + (int64_t)m * a.ldc + gn;
+      if (full) {
+        *reinterpret_cast<f32x4*>(dst) = val;
+      } else if (m < a.M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gn + e < a.N) dst[e] = val[e];
+      }
+    }
+  }
+}
+
+hipError_t launch_pack_weight(const PackWeightArgs& g, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (g.N <= 0 || g.K <= 0 || g.K % 16 != 0) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)((g.N + 31) / 32) * (g.K / 16) * 64;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const __bf16*>(g.W), g.ldw, g.N, g.K, total,
+                     reinterpret_cast<bf16x8*>(g.out));
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_nt_packed(const GemmPackedArgs& g, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (g.K % kGemmBK != 0 || g.K <= 0) return hipErrorInvalidValue;
+  GemmPackedKArgs a;
+  a.A = reinterpret_cast<const __bf16*>(g.A);
+  a.Bp = reinterpret_cast<const bf16x8*>(g.Bp);
+  a.C = g.C;
+  a.lda = g.lda;
+  a.ldc = g.ldc;
+  a.M = g.M;
+  a.N = g.N;
+  a.K = g.K;
+  a.n32 = (g.N + 31) / 32;
+  a.tiles_m = (g.M + 255) / 256;
+  a.tiles_n = (g.N + 255) / 256;
+  a.group_m = 2;
+  a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
+  constexpr int A_STAGES = kPackedAStages;
+  const size_t lds_bytes = (size_t)A_STAGES * 256 * kGemmBK * 2;
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&gemm_bf16_nt_packed_kernel<A_STAGES>), (int)lds_bytes, lds_set);
+  if (e != hipSuccess) return e;
+  // per-tile byte offsets are 32-bit: one tile's rows of A and 8 column tiles of B
+  if ((int64_t)256 * g.lda * 2 > 0x7FFFFFFF || (int64_t)8 * (g.K / 16) * 1024 > 0x7FFFFFFF)
+    return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_bf16_nt_packed_kernel<A_STAGES>, dim3((unsigned)grid), dim3(512), lds_bytes,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace engram

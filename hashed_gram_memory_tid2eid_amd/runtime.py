@@ -2,8 +2,9 @@
 device buffers.
 
 ``Engram.forward`` = engram_compress_hash (every site in one pass) -> for each
-site engram_gather_dequant -> engram_gated_residual, on one stream, no host
-synchronisation, no allocation (path "split", the default).  Path "fused" (e4m3fn tables) replaces the
+site engram_gather_dequant -> projection (engram_project_packed for many tokens,
+engram_project_splitk for few, else engram_project) -> engram_gate_add, on one
+stream, no host synchronisation, no allocation (path "split", the default).  Path "fused" (e4m3fn tables) replaces the
 gather and the projection by engram_gather_project, which keeps the gathered
 rows on chip: no [T][k_pad] bf16 row buffer, at a lower projection rate.
 
@@ -21,7 +22,11 @@ from . import (ENGRAM_DTYPE_BF16, ENGRAM_DTYPE_FP8_E4M3FN, ENGRAM_SCALE_BLOCK32_
                ENGRAM_SCALE_ROW_F32, ENGRAM_TABLE_PER_SITE, ENGRAM_TABLES_PER_ORDER, Layout,
                engram_compress_hash, engram_gate_add_partials, engram_project_splitk,
                engram_gate_add, engram_gather_dequant, engram_gather_project,
-               engram_gated_residual, engram_layout_create, engram_tid2eid_check)
+               engram_layout_create, engram_pack_weight, engram_packed_weight_bytes,
+               engram_project, engram_project_packed, engram_tid2eid_check)
+
+# calls with at least this many outputs (tokens x hidden) take the 256 x 256 tiles
+BIG_PROJECTION = 64 * 256 * 256
 
 
 def pad_weight(w, layout: Layout):
@@ -48,7 +53,7 @@ def choose_proj_splits(tokens: int, hidden: int, k_pad: int) -> int:
     per split, and k_pad a multiple of 64 x splits.  (Decode, 256 tokens x 4,096
     outputs: 64 tiles -> 4 splits, measured 24 us for the projection against
     42 us unsplit; 8 splits measured no faster.)"""
-    if tokens * hidden >= 64 * 256 * 256:  # the 256 x 256 path: many tiles already
+    if tokens * hidden >= BIG_PROJECTION:  # the 256 x 256 path: many tiles already
         return 1
     tiles = -(-tokens // 128) * -(-hidden // 128)
     best = 1
@@ -110,6 +115,13 @@ class Engram:
         self.hidden = hidden
         self.hc_mult = hc_mult
         self.max_tokens = max_tokens
+        # many-token calls project from the weight in fragment order (packed once here)
+        self.site_packed = [None] * num_sites
+        if path == "split" and max_tokens * hidden >= BIG_PROJECTION:
+            nbytes = engram_packed_weight_bytes(self.layout, hidden)
+            for s, w in enumerate(self.site_weights):
+                self.site_packed[s] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+                engram_pack_weight(self.layout, w, self.site_packed[s], stream)
         self.eids = torch.empty(max_tokens, dtype=torch.int32, device=dev)
         rid_shape = ((max_tokens, 3, info.heads) if num_sites == 1
                      else (max_tokens, num_sites, 3, info.heads))
@@ -170,14 +182,36 @@ class Engram:
             return streams
         engram_gather_dequant(self.layout, self.site_tables[site], self.site_scales[site],
                               self.row_ids, self.rows, site=site, T=T, stream=stream)
-        if self.proj_splits > 1:
-            engram_project_splitk(self.layout, self.rows, self.site_weights[site], self.partials,
+        return self.project_gate(site, self.rows, streams, T, keep=keep, stream=stream)
+
+    def projection_kind(self, site: int, T: int) -> str:
+        """Which projection a T-token call of `site` runs: "packed" (256 x 256 tiles
+        from the packed weight), "splitk" (few tokens) or "plain"."""
+        if self.site_packed[site] is not None and T * self.hidden >= BIG_PROJECTION:
+            return "packed"
+        return "splitk" if self.proj_splits > 1 else "plain"
+
+    def project(self, site: int, rows, T: int, *, stream=None):
+        """v (or the split-K partial slices of v) of `rows` for `site`."""
+        kind = self.projection_kind(site, T)
+        if kind == "packed":
+            engram_project_packed(self.layout, rows, self.site_packed[site], self.hidden, self.v, T=T,
+                                  stream=stream)
+        elif kind == "splitk":
+            engram_project_splitk(self.layout, rows, self.site_weights[site], self.partials,
                                   self.proj_splits, T=T, stream=stream)
+        else:
+            engram_project(self.layout, rows, self.site_weights[site], self.v, T=T, stream=stream)
+        return kind
+
+    def project_gate(self, site: int, rows, streams, T: int, *, keep=None, stream=None):
+        """Projection and gated residual of `site` from gathered `rows`.  There is no
+        variant without rows: a site with no looked-up rows is a caller error."""
+        if self.project(site, rows, T, stream=stream) == "splitk":
             engram_gate_add_partials(self.layout, self.partials, self.proj_splits, streams, keep=keep,
                                      v=self.v, T=T, stream=stream)
-            return streams
-        engram_gated_residual(self.layout, self.rows, self.site_weights[site], streams, self.v,
-                              keep=keep, T=T, stream=stream)
+        else:
+            engram_gate_add(self.layout, self.v, streams, keep=keep, T=T, stream=stream)
         return streams
 
     def forward(self, tokens, cu_seqlens, streams, *, seq_start=None, slots=None, store=None,
@@ -241,8 +275,7 @@ class Engram:
                                f"(or the slot was refilled)")
         st = stream if stream is not None else torch.cuda.current_stream()
         st.wait_event(pre.ready)
-        engram_gated_residual(self.layout, self.pre_rows[pre.slot][site], self.site_weights[site],
-                              streams, self.v, keep=keep, T=pre.T, stream=st)
+        self.project_gate(site, self.pre_rows[pre.slot][site], streams, pre.T, keep=keep, stream=st)
         done = torch.cuda.Event()
         done.record(st)
         self.pre_free[pre.slot] = done  # the last site's apply is the slot's last reader

@@ -298,6 +298,30 @@ int engram_project(const engram_layout* layout, const void* d_rows, int64_t rows
                    const void* d_w, int64_t w_ld, int32_t hidden, float* d_v, int32_t T,
                    hipStream_t stream);
 
+/* The projection weight rearranged once into matrix-core fragment order, so that
+ * engram_project_packed reads it with whole-line loads straight into registers
+ * and keeps only the rows in on-chip memory (same wkv projection as
+ * engram_project, [VeOmni#1370] config commit).
+ * engram_packed_weight_bytes: size of the packed form of a [hidden][k_pad] weight,
+ *   ceil(hidden / 32) * 32 * k_pad * 2 bytes.
+ * engram_pack_weight: d_w bf16 [hidden][w_ld] as for engram_project (columns
+ *   k_pad.. ignored) -> d_packed (caller-owned, that many bytes, 16-byte aligned):
+ *   for column tile j = o / 32, k16 step s = k / 16 and lane l = o % 32 + 32 ((k % 16) / 8),
+ *   element W[o][k] sits at bf16 index ((j (k_pad / 16) + s) 64 + l) 8 + k % 8;
+ *   rows past hidden are zero.  Enqueued on `stream`; d_w may be freed once it ran.
+ * engram_project_packed: v = rows W^T as engram_project, from the packed weight,
+ *   bit-identical to engram_project (the same products summed in the same order).
+ *   Meant for many tokens (it tiles 256 x 256); d_rows, rows_ld, d_v, T as for
+ *   engram_project.
+ * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN; ENGRAM_E_UNSUPPORTED when 256 rows of
+ * rows_ld elements or k_pad * 64 bytes pass 2^31 - 1 (32-bit per-tile offsets). */
+int engram_packed_weight_bytes(const engram_layout* layout, int32_t hidden, int64_t* bytes);
+int engram_pack_weight(const engram_layout* layout, const void* d_w, int64_t w_ld, int32_t hidden,
+                       void* d_packed, hipStream_t stream);
+int engram_project_packed(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
+                          const void* d_packed, int32_t hidden, float* d_v, int32_t T,
+                          hipStream_t stream);
+
 /* Split-K form of engram_project for few tokens (decode): K is cut into `splits`
  * equal chunks (k_pad must be a multiple of 64 * splits) that run as separate
  * workgroups, so a small token count still fills the chip; chunk s writes

@@ -247,6 +247,43 @@ def test_projection_and_gate_host_errors_need_no_device():
                                      None) == eng.ENGRAM_E_ALIGN
 
 
+def test_packed_projection_host_errors_need_no_device():
+    """The packed-weight size, the pack and the packed projection check their
+    arguments on the host and return before any launch."""
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg)
+    lib = eng._lib
+    P = ctypes.c_void_p
+    K = L.info.k_pad
+    ok = P(256)
+    # size: ceil(hidden / 32) * 32 rows of k_pad bf16
+    assert eng.engram_packed_weight_bytes(L, 256) == 256 * K * 2
+    assert eng.engram_packed_weight_bytes(L, 264) == 288 * K * 2
+    assert eng.engram_packed_weight_bytes(L, 1) == 32 * K * 2
+    n = ctypes.c_int64(0)
+    assert lib.engram_packed_weight_bytes(L.handle, 0, ctypes.byref(n)) == eng.ENGRAM_E_ARG
+    assert lib.engram_packed_weight_bytes(L.handle, 8, None) == eng.ENGRAM_E_ARG
+    # pack: leading dimension >= k_pad and a multiple of 8, 16-byte aligned pointers
+    assert lib.engram_pack_weight(L.handle, ok, K - 8, cfg.hidden, ok, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_pack_weight(L.handle, ok, K + 4, cfg.hidden, ok, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_pack_weight(L.handle, P(264), K, cfg.hidden, ok, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_pack_weight(L.handle, ok, K, cfg.hidden, P(8), None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_pack_weight(L.handle, ok, K, 0, ok, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_pack_weight(L.handle, None, K, cfg.hidden, ok, None) == eng.ENGRAM_E_ARG
+    # packed projection
+    assert lib.engram_project_packed(L.handle, ok, K - 8, ok, cfg.hidden, ok, 4, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_project_packed(L.handle, P(264), K, ok, cfg.hidden, ok, 4, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_project_packed(L.handle, ok, K, ok, cfg.hidden, P(258), 4, None) == eng.ENGRAM_E_ALIGN
+    assert lib.engram_project_packed(L.handle, ok, K, ok, cfg.hidden, ok, -1, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_project_packed(L.handle, ok, K, ok, 0, ok, 4, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_project_packed(L.handle, None, K, ok, cfg.hidden, ok, 4, None) == eng.ENGRAM_E_ARG
+    # 256 rows of this leading dimension do not fit 32-bit byte offsets
+    assert lib.engram_project_packed(L.handle, ok, 1 << 22, ok, cfg.hidden, ok, 4,
+                                     None) == eng.ENGRAM_E_UNSUPPORTED
+    # no tokens: nothing to do
+    assert lib.engram_project_packed(L.handle, ok, K, ok, cfg.hidden, ok, 0, None) == 0
+
+
 def test_multi_site_layout_matches_oracle_and_pages(golden):
     """Two sites, 8 heads, floor 16,000,000, one table per site: the product's
     primes and offsets equal the oracle's, and each site's table size is the
