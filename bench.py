@@ -68,14 +68,14 @@ def algorithmic_per_token(cfg):
     }
 
 
-def measured_traffic(cfg):
-    """HBM bytes per gather launch from the committed profiler counters
-    (profiles/gather_dequant_<workload>_traffic.txt), or None when there is no
+def measured_traffic(cfg, profile="gather_dequant_{tag}_traffic.txt", source="gather.hip"):
+    """HBM bytes per launch of a kernel from the committed profiler counters
+    (profiles/<profile>, by default the gather's), or None when there is no
     measurement for this workload or the kernel source changed since it was taken."""
     import hashlib
     tag = {"full": "full_fp8"}.get(cfg.name, cfg.name)
-    path = os.path.join(ROOT, "profiles", f"gather_dequant_{tag}_traffic.txt")
-    src = os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "csrc", "kernels", "gather.hip")
+    path = os.path.join(ROOT, "profiles", profile.format(tag=tag))
+    src = os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "csrc", "kernels", source)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -360,11 +360,13 @@ def main():
         # the metric names the gather's HBM rate; the projection takes most of the step,
         # so its own roofline goes beside it
         pkind = site.projection_kind(0, T)
+        proj_traffic = (measured_traffic(cfg, "gemm_bf16_nt_packed_{tag}_counters.txt", "gemm_packed.hip")
+                        if pkind == "packed" else None)
         roofline_projection = {"bound": "mfma",
                                "kernel": "gemm_bf16_nt_packed" if pkind == "packed" else "gemm_bf16_nt",
                                "achieved": proj_tflops,
                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": proj_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                               "frac": proj_tflops / BF16_PEAK_TFLOPS, "traffic": proj_traffic,
                                "flops_per_launch": proj_flops, "avg_launch_ms": kern_ms["project"]}
     kernels["gate_add"] = {"ms": kern_ms["gate_add"], "bound": "hbm", "GB/s": gate_gbs,
                            "frac": gate_gbs / HBM_PEAK_GBS}
