@@ -15,9 +15,12 @@
 //
 // Tile: 256 x 256 per workgroup, 8 waves as 2 (M) x 4 (N), 128 x 64 per wave (4 x 2
 // tiles of 32 x 32, two waves per SIMD), the same products accumulated in the same
-// k16 order as gemm_bf16_nt_kernel, so C is bit-identical to it.
-// A: direct global->LDS loads of one 128-byte line per row per 64-k stage, in a ring
-// of A_STAGES stages of 32 KB, XOR-swizzled as in gemm.hip.
+// k16 order as gemm_bf16_nt_kernel, so C is bit-identical to it.  Calls with a short
+// K take 128 x 256 tiles of 4 waves (1 x 4, the same 128 x 64 per wave) instead, two
+// workgroups per CU: one workgroup's prologue and epilogue then overlap the other's
+// main loop, and each stage barrier holds only one wave per SIMD.
+// A: direct loads into LDS of one 128-byte line per row per 64-k stage, in a ring
+// of A_STAGES stages, XOR-swizzled as in gemm.hip.
 // B: a ring of four k16 steps in registers; the fragments of step s of stage kt+1 are
 // requested right after step s of stage kt has been multiplied, one stage ahead.
 //
@@ -28,7 +31,10 @@
 
 namespace engram {
 
-constexpr int kPackedAStages = 4;  // 4 x 32 KB of A in LDS
+constexpr int kPackedAStages = 4;  // A ring: 4 stages of 64 k (32 KB each at 256 rows, 16 KB at 128)
+// calls with k_pad up to this take 128 x 256 tiles (measured: faster at k_pad 3,072 and
+// 6,144, even at 9,792, slower at 19,584 than 256 x 256)
+constexpr int kPackedShortK = 8192;
 // dword 3 of a buffer resource on gfx9-family parts: 32-bit data format, no swizzle
 constexpr int kBufferRsrcFlags = 0x00020000;
 
@@ -60,13 +66,12 @@ void pack_weight_kernel(const __bf16* __restrict__ W, int64_t ldw, int32_t N, in
   out[c] = v;
 }
 
-template <int A_STAGES>
-__global__ __launch_bounds__(512, 1)
-void gemm_bf16_nt_packed_kernel(GemmPackedKArgs a) {
-  constexpr int BM = 256, BN = 256, WN_WAVES = 4, NWAVES = 8;
+template <int A_STAGES, int BM, int WM_WAVES>
+__device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
+  constexpr int BN = 256, WN_WAVES = 4, NWAVES = WM_WAVES * WN_WAVES;
   constexpr int BK = kGemmBK;
-  constexpr int WM = 128, WN = 64, TM = 4, TN = 2;
-  constexpr int STAGE = BM * BK * 2;           // 32 KB of A per stage
+  constexpr int WM = BM / WM_WAVES, WN = BN / WN_WAVES, TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = BM * BK * 2;           // bytes of A per stage
   constexpr int AI = BM / 8 / NWAVES;          // 1 KB direct loads per wave per stage
   constexpr int BL = TN;                       // B loads per k16 step
   constexpr int PER_ITER = 4 * BL + AI;        // vector-memory loads per iteration
@@ -265,6 +270,15 @@ void gemm_bf16_nt_packed_kernel(GemmPackedKArgs a) {
   }
 }
 
+// 256 x 256 tiles, one workgroup of 8 waves per CU (calls with a long K)
+__global__ __launch_bounds__(512, 1) void gemm_bf16_nt_packed_kernel(GemmPackedKArgs a) {
+  packed_gemm_tile<kPackedAStages, 256, 2>(a);
+}
+// 128 x 256 tiles, two workgroups of 4 waves per CU (short K)
+__global__ __launch_bounds__(256, 2) void gemm_bf16_nt_packed128_kernel(GemmPackedKArgs a) {
+  packed_gemm_tile<kPackedAStages, 128, 1>(a);
+}
+
 hipError_t launch_pack_weight(const PackWeightArgs& g, hipStream_t stream) {
   (void)hipGetLastError();
   if (g.N <= 0 || g.K <= 0 || g.K % 16 != 0) return hipErrorInvalidValue;
@@ -291,23 +305,31 @@ hipError_t launch_gemm_bf16_nt_packed(const GemmPackedArgs& g, hipStream_t strea
   a.N = g.N;
   a.K = g.K;
   a.n32 = (g.N + 31) / 32;
-  a.tiles_m = (g.M + 255) / 256;
   a.tiles_n = (g.N + 255) / 256;
-  a.group_m = 2;
   a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
-  constexpr int A_STAGES = kPackedAStages;
-  const size_t lds_bytes = (size_t)A_STAGES * 256 * kGemmBK * 2;
-  static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = ensure_dynamic_lds(
-      reinterpret_cast<const void*>(&gemm_bf16_nt_packed_kernel<A_STAGES>), (int)lds_bytes, lds_set);
+  // short K: two 128-row workgroups per CU (tile groups of 4 row blocks, the same rows
+  // per XCD as 2 of 256); long K: one 256-row workgroup per CU
+  const bool short_k = g.K <= kPackedShortK;
+  const int bm = short_k ? 128 : 256;
+  a.tiles_m = (g.M + bm - 1) / bm;
+  a.group_m = short_k ? 4 : 2;
+  const size_t lds_bytes = (size_t)kPackedAStages * bm * kGemmBK * 2;
+  static std::atomic<uint64_t> lds_set256{0}, lds_set128{0};
+  const hipError_t e =
+      short_k ? ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_bf16_nt_packed128_kernel), (int)lds_bytes,
+                                   lds_set128)
+              : ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_bf16_nt_packed_kernel), (int)lds_bytes,
+                                   lds_set256);
   if (e != hipSuccess) return e;
   // per-tile byte offsets are 32-bit: one tile's rows of A and 8 column tiles of B
   if ((int64_t)256 * g.lda * 2 > 0x7FFFFFFF || (int64_t)8 * (g.K / 16) * 1024 > 0x7FFFFFFF)
     return hipErrorInvalidValue;
   const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_bf16_nt_packed_kernel<A_STAGES>, dim3((unsigned)grid), dim3(512), lds_bytes,
-                     stream, a);
+  if (short_k)
+    hipLaunchKernelGGL(gemm_bf16_nt_packed128_kernel, dim3((unsigned)grid), dim3(256), lds_bytes, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_bf16_nt_packed_kernel, dim3((unsigned)grid), dim3(512), lds_bytes, stream, a);
   return hipGetLastError();
 }
 

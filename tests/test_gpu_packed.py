@@ -77,10 +77,12 @@ def test_packed_bytes_follow_the_index_formula(eng):
 
 @pytest.mark.parametrize("M,N,cols,D", [(1, 8, 3, 64), (77, 200, 3, 100), (300, 512, 6, 128),
                                         (1000, 264, 3, 192), (4097, 4096, 3, 512),
-                                        (513, 300, 6, 1000), (256, 256, 3, 64)])
+                                        (513, 300, 6, 1000), (256, 256, 3, 64),
+                                        (700, 520, 3, 3000), (255, 40, 3, 2731)])
 def test_packed_projection_equals_unpacked(eng, M, N, cols, D):
     """Ragged M and N (row and column tile tails, a 264-wide weight whose last
-    256-column block holds one 32-column tile) and K from 192 to 6,144."""
+    256-column block holds one 32-column tile) and K from 192 to 6,144 (128 x 256
+    tiles), and 9,024 and 8,256 (256 x 256 tiles, k_pad past 8,192)."""
     L = _layout(eng, cols, D)
     K = L.info.k_pad
     A, B = _operands(L, M, N, seed=M * 1000 + N)
