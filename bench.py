@@ -186,6 +186,11 @@ def main():
     ap.add_argument("--prefetch", action="store_true",
                     help="also time the pipelined loop: hash + gather of step i+1 on a prefetch "
                          "stream while step i projects and gates; value = pipelined rate")
+    ap.add_argument("--order", default="lookahead", choices=["lookahead", "sequential"],
+                    help="lookahead (split path, prefill-style workloads): per step the next "
+                         "call's hash, then per site this call's projection, the next call's "
+                         "gather, this call's gate; sequential: hash, gather, projection, gate. "
+                         "The other order is timed after the main line.")
     ap.add_argument("--proj-splits", type=int, default=0,
                     help="split-K factor of the projection (0: chosen from the call size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -230,6 +235,10 @@ def main():
     site_tables = [ei.make_tables(cfg, dev, site=s) for s in range(NS)]
     weights = [ei.make_weight(cfg, dev, site=s) for s in range(NS)]
     one = NS == 1
+    # the look-ahead order applies to the split path's many-token calls (not decode steps,
+    # graph captures or the two-stream prefetch loop, which keep their own order)
+    lookahead_ok = (args.order == "lookahead" and args.path == "split" and not cfg.decode_steps
+                    and not args.graph and not args.prefetch)
     if args.host_tables:
         # tables move to pinned host memory; the device copies are dropped
         for t in site_tables:
@@ -250,7 +259,8 @@ def main():
                       weight=weights[0] if one else weights, hidden=cfg.hidden, hc_mult=cfg.hc_mult,
                       max_tokens=T, path=args.path, num_sites=NS, table_split=cfg.table_split,
                       scale_block=cfg.scale_block, hash_floor=cfg.hash_floor,
-                      prefetch_slots=2 if args.prefetch else 0, proj_splits=args.proj_splits)
+                      prefetch_slots=2 if args.prefetch else 0, proj_splits=args.proj_splits,
+                      lookahead=lookahead_ok)
     site_streams = [ei.make_streams(cfg, T, dev, step=s) for s in range(NS)]
     streams_host = None
     if not args.no_cpu_baseline:
@@ -266,13 +276,40 @@ def main():
     setup_s = time.perf_counter() - t_setup
     print(f"# setup {setup_s:.1f}s: {cfg.name}, T={T}, k_pad={site.info.k_pad}", file=sys.stderr, flush=True)
 
-    # kernel sequence of one step: the hash, then per site gather (+) project, gate
+    # kernel sequence of one step: the hash, then per site gather (+) project, gate;
+    # in the look-ahead order the hash is the next call's, and per site the projection
+    # (this call's rows, gathered one step earlier) comes before the next call's gather
     if args.path == "fused":
         seq = ["compress_hash"] + ["gather_project", "gate_add"] * NS
     else:
         seq = ["compress_hash"] + ["gather_dequant", "project", "gate_add"] * NS
+    seq_la = ["compress_hash"] + ["project", "gather_dequant", "gate_add"] * NS
 
-    def step(ev=None):
+    def step_lookahead(ev=None):
+        k = 0
+
+        def mark():
+            nonlocal k
+            if ev:
+                ev[k].record()
+            k += 1
+        mark()
+        eng.engram_compress_hash(L, tid2eid, tok, cu, site.eids, site.row_ids, seq_start=ss,
+                                 slots=sl, store=store)
+        mark()
+        for si in range(NS):
+            kind = site.project(si, site.site_rows[si], T)
+            mark()
+            eng.engram_gather_dequant(L, site.site_tables[si], site.site_scales[si], site.row_ids,
+                                      site.site_rows[si], site=si, T=T)
+            mark()
+            if kind == "splitk":
+                eng.engram_gate_add_partials(L, site.partials, site.proj_splits, site_streams[si], T=T)
+            else:
+                eng.engram_gate_add(L, site.v, site_streams[si], T=T)
+            mark()
+
+    def step_sequential(ev=None):
         k = 0
 
         def mark():
@@ -301,29 +338,39 @@ def main():
                 eng.engram_gate_add(L, site.v, site_streams[si], T=T)
             mark()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    eng.check_device_error("warmup")
+    def timed(step_fn, sq):
+        """Warm-up steps, then K timed steps with an event between kernels: total ms,
+        ms per launch of each kernel, host wall seconds."""
+        for _ in range(args.warmup):
+            step_fn()
+        torch.cuda.synchronize()
+        eng.check_device_error("warmup")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(sq) + 1)] for _ in range(args.steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        start.record()
+        for i in range(args.steps):
+            step_fn(evs[i])
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        eng.check_device_error("timed steps")
+        # average time per launch of each kernel (a step launches the per-site kernels NS times)
+        kms = {}
+        for n in dict.fromkeys(sq):
+            js = [j for j, m in enumerate(sq) if m == n]
+            kms[n] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs for j in js]))
+        return start.elapsed_time(stop), kms, wall
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    eng.check_device_error("timed steps")
-    total_ms = start.elapsed_time(stop)
+    if lookahead_ok:
+        # the first call's lookup, so that every timed step projects rows gathered a step earlier
+        site.gather_ahead(tok, cu, seq_start=ss, slots=sl, store=store)
+        step, order_seq = step_lookahead, seq_la
+    else:
+        step, order_seq = step_sequential, seq
+    total_ms, kern_ms, wall = timed(step, order_seq)
     ms_per_step = total_ms / args.steps
-    # average time per launch of each kernel (a step launches the per-site kernels NS times)
-    kern_ms = {}
-    for n in dict.fromkeys(seq):
-        js = [j for j, m in enumerate(seq) if m == n]
-        kern_ms[n] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs for j in js]))
 
     per = algorithmic_per_token(cfg)
     def gbs(b, ms):
@@ -393,6 +440,7 @@ def main():
                    "table_split": cfg.table_split, "scale_block": cfg.scale_block,
                    "tables_in": "pinned host memory" if args.host_tables else "HBM",
                    "proj_splits": site.proj_splits,
+                   "step_order": "lookahead" if lookahead_ok else "sequential",
                    "projection": site.projection_kind(0, T) if args.path != "fused" else "fused"},
         "roofline": roofline,
         "kernels": kernels,
@@ -401,6 +449,14 @@ def main():
     }
     if args.path != "fused":
         result["roofline_projection"] = roofline_projection
+    if lookahead_ok:
+        # the same K steps in the sequential order (hash, gather, projection, gate of one
+        # call), on the same inputs, after the main line
+        o_ms, o_kern, _ = timed(step_sequential, seq)
+        result["sequential_order"] = {
+            "value": T * args.steps / (o_ms * 1e-3), "ms_per_step": o_ms / args.steps,
+            "kernels_ms": o_kern,
+            "gather_frac": gbs(gather_bytes, o_kern["gather_dequant"]) / HBM_PEAK_GBS}
     if args.graph:
         # the same step captured once and replayed K times (launch overhead removed);
         # the decode step is launch-bound, so this is its production form

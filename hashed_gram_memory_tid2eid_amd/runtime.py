@@ -79,7 +79,7 @@ class Engram:
                  weight, hidden: int, hc_mult: int = 4, max_tokens: int, hash_floor: int = 0,
                  path: str = "split", num_sites: int = 1, table_split: str = "order",
                  scale_block: int = 0, prefetch_slots: int = 0, proj_splits: int = 0,
-                 stream=None):
+                 lookahead: bool = False, stream=None):
         import torch
         if path not in ("split", "fused"):
             raise ValueError(f"unknown path {path!r}")
@@ -128,6 +128,14 @@ class Engram:
         self.row_ids = torch.empty(rid_shape, dtype=torch.int32, device=dev)
         self.rows = (torch.empty((max_tokens, info.k_pad), dtype=torch.bfloat16, device=dev)
                      if path == "split" else None)
+        # look-ahead order (run_ahead): each site's rows wait in a buffer of their own
+        # from one call to the next; one site can use the shared buffer
+        if lookahead and path != "split":
+            raise ValueError("the look-ahead order gathers rows, which the split path alone keeps")
+        self.lookahead = lookahead
+        self.site_rows = ([self.rows] + [torch.empty_like(self.rows) for _ in range(num_sites - 1)]
+                          if lookahead else None)
+        self.pending_T = None  # tokens of the call whose rows wait for run_ahead
         self.v = torch.empty((max_tokens, hidden), dtype=torch.float32, device=dev)
         # split-K projection for few tokens: the partial slices live in a workspace
         # sized once here; 0 = choose from the call size
@@ -233,6 +241,64 @@ class Engram:
         for s in range(self.num_sites):
             self.site_forward(s, per_site[s], T, keep=keep, stream=stream)
         return streams
+
+    # ---- look-ahead order: the next call's lookup between projection and gate -------
+    def gather_ahead(self, tokens, cu_seqlens, *, seq_start=None, slots=None, store=None,
+                     dead=None, stream=None):
+        """Hash and every site's gather of a call, into the look-ahead buffers, with
+        no projection: the first call of a look-ahead sequence."""
+        self._check_lookahead(tokens)
+        self.hash(tokens, cu_seqlens, seq_start=seq_start, slots=slots, store=store, dead=dead,
+                  stream=stream)
+        T = tokens.numel()
+        for s in range(self.num_sites):
+            engram_gather_dequant(self.layout, self.site_tables[s], self.site_scales[s], self.row_ids,
+                                  self.site_rows[s], site=s, T=T, stream=stream)
+        self.pending_T = T
+
+    def run_ahead(self, streams, *, keep=None, next_tokens=None, next_cu_seqlens=None,
+                  next_seq_start=None, next_slots=None, next_store=None, next_dead=None,
+                  stream=None):
+        """Adds the Engram memory of the call gathered last into ``streams`` (as
+        ``forward`` would have), and, when ``next_tokens`` is given, hashes and gathers
+        the next call in between, on the same stream: the next call's hash, then per
+        site the projection of this call, the gather of the next and the gate of this
+        one.  A site's projection has read its rows before the next gather overwrites
+        them, and the gate's stream writes drain while the next projection runs,
+        instead of under the next gather.  The lookup depends on token ids alone, so it
+        can run a call ahead, as the pages' lookup runs ahead of the backbone.  Every
+        call still runs each kernel once; outputs equal sequential ``forward`` calls bit
+        for bit."""
+        if self.pending_T is None:
+            raise RuntimeError("no gathered call is waiting: call gather_ahead first")
+        T = self.pending_T
+        per_site = [streams] if self.num_sites == 1 else list(streams)
+        if len(per_site) != self.num_sites or any(x.shape[0] != T for x in per_site):
+            raise ValueError("streams must hold one row per token of the waiting call (one tensor per site)")
+        T_next = None
+        if next_tokens is not None:
+            self._check_lookahead(next_tokens)
+            T_next = next_tokens.numel()
+            self.hash(next_tokens, next_cu_seqlens, seq_start=next_seq_start, slots=next_slots,
+                      store=next_store, dead=next_dead, stream=stream)
+        for s in range(self.num_sites):
+            kind = self.project(s, self.site_rows[s], T, stream=stream)
+            if T_next is not None:
+                engram_gather_dequant(self.layout, self.site_tables[s], self.site_scales[s],
+                                      self.row_ids, self.site_rows[s], site=s, T=T_next, stream=stream)
+            if kind == "splitk":
+                engram_gate_add_partials(self.layout, self.partials, self.proj_splits, per_site[s],
+                                         keep=keep, v=self.v, T=T, stream=stream)
+            else:
+                engram_gate_add(self.layout, self.v, per_site[s], keep=keep, T=T, stream=stream)
+        self.pending_T = T_next
+        return streams
+
+    def _check_lookahead(self, tokens):
+        if not self.lookahead:
+            raise ValueError("construct with lookahead=True for the look-ahead order")
+        if tokens.numel() > self.max_tokens:
+            raise ValueError(f"{tokens.numel()} tokens > max_tokens {self.max_tokens}")
 
     # ---- prefetch: gather ahead on a stream of its own ------------------------------
     def prefetch(self, tokens, cu_seqlens, *, stream, seq_start=None, slots=None, store=None,
