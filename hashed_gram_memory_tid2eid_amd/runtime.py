@@ -233,6 +233,8 @@ class Engram:
             raise ValueError(f"{T} tokens > max_tokens {self.max_tokens}")
         if dead is not None and keep is None:
             raise ValueError("a dead mask needs the matching keep mask")
+        if self.pending_T is not None:
+            raise RuntimeError("a gathered call waits for run_ahead; forward would overwrite its rows")
         per_site = [streams] if self.num_sites == 1 else list(streams)
         if len(per_site) != self.num_sites or any(x.shape[0] != T for x in per_site):
             raise ValueError("streams must hold one row per token (one tensor per site)")

@@ -134,5 +134,11 @@ def test_lookahead_needs_a_gathered_call(eng):
     c = _calls(cfg, 1, T)[0]
     with pytest.raises(ValueError):
         plain.gather_ahead(c["tokens"], c["cu"])
+    # a waiting call's rows are not overwritten by a plain forward
+    site.gather_ahead(c["tokens"], c["cu"])
+    with pytest.raises(RuntimeError):
+        site.forward(c["tokens"], c["cu"], x)
+    site.run_ahead(x)
+    site.forward(c["tokens"], c["cu"], x)
     del site, plain
     _free()
