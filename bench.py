@@ -204,8 +204,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(tables are replicated per GPU, tokens split across them); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
