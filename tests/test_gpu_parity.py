@@ -351,6 +351,28 @@ def _large_run(eng, name, f32_sample, stream_sample, tables=None):
         assert torch.equal(v_f.view(torch.int32), site.site.v[:T].view(torch.int32))
         log(f"{name}: fused gather+projection equals the split path on all {T} tokens")
         del v_f
+        # the look-ahead order the benchmark times (next call's hash, projection, next
+        # call's gather, gate), on the same tables: streams equal the sequential pass above
+        # bit for bit, for the call gathered ahead and for the one gathered in between
+        la = eng.Engram(
+            vocab_size=cfg.vocab, compressed_vocab=cfg.vc, pad_token_id=cfg.pad_token_id,
+            heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+            table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes,
+            tid2eid=site.tid2eid, tables=site.tables.data, scales=site.tables.scale,
+            weight=site.weight, hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=T, lookahead=True)
+        la.gather_ahead(db["tokens"], db["cu_seqlens"], seq_start=db["seq_start"])
+        for nxt in (True, False):
+            x = ei.make_streams(cfg, T, DEV)
+            kw = dict(next_tokens=db["tokens"], next_cu_seqlens=db["cu_seqlens"],
+                      next_seq_start=db["seq_start"]) if nxt else {}
+            la.run_ahead(x, **kw)
+            torch.cuda.synchronize()
+            _no_device_error(eng, f"{name} look-ahead")
+            assert torch.equal(x.view(torch.int16), streams.view(torch.int16))
+            del x
+        log(f"{name}: look-ahead order equals the sequential pass on all {T} tokens "
+            f"({la.projection_kind(0, T)} projection)")
+        del la
     return site
 
 
