@@ -1,6 +1,7 @@
 """bench.py keeps its output contract: one JSON line with the metric, the
 whole-job value, the roofline of the gather and of the projection, the per-kernel
-breakdown and the oracle's CPU rate.  Runs the tiny workload in a child process
+breakdown, the sequential step order timed beside the look-ahead one, and the
+oracle's CPU rate.  Runs the tiny workload in a child process
 (a few seconds)."""
 import json
 import os
@@ -36,6 +37,13 @@ def test_bench_json_line_contract():
         assert k in r, k
     assert r["bound"] == "hbm" and r["frac"] == pytest.approx(r["achieved"] / r["peak"])
     assert d["roofline_projection"]["bound"] == "mfma"
+    # the tiny workload is a many-token split-path call: the look-ahead order is timed,
+    # and the sequential order beside it
+    assert d["config"]["step_order"] == "lookahead"
+    so = d["sequential_order"]
+    assert so["value"] > 0 and so["ms_per_step"] > 0
+    assert so["value"] == pytest.approx(d["config"]["tokens_per_step"] / (so["ms_per_step"] * 1e-3), rel=1e-6)
+    assert set(so["kernels_ms"]) == set(d["kernels"])
     c = d["cpu_baseline"]
     for k in ("value", "unit", "cores", "kind", "sample"):
         assert k in c, k
