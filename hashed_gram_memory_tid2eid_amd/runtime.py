@@ -250,6 +250,8 @@ class Engram:
         """Hash and every site's gather of a call, into the look-ahead buffers, with
         no projection: the first call of a look-ahead sequence."""
         self._check_lookahead(tokens)
+        if self.pending_T is not None:
+            raise RuntimeError("a gathered call already waits for run_ahead; its rows would be overwritten")
         self.hash(tokens, cu_seqlens, seq_start=seq_start, slots=slots, store=store, dead=dead,
                   stream=stream)
         T = tokens.numel()
@@ -267,10 +269,11 @@ class Engram:
         site the projection of this call, the gather of the next and the gate of this
         one.  A site's projection has read its rows before the next gather overwrites
         them, and the gate's stream writes drain while the next projection runs,
-        instead of under the next gather.  The lookup depends on token ids alone, so it
-        can run a call ahead, as the pages' lookup runs ahead of the backbone.  Every
-        call still runs each kernel once; outputs equal sequential ``forward`` calls bit
-        for bit."""
+        instead of under the next gather.  The lookup depends on token ids (and the
+        image mask) alone, so it can run a call ahead ([VeOmni#1370] "feat: support
+        DeepSeek-V4.1-Flash in SeedOmni", n-gram memory lookup commit: the lookup is
+        its own graph node ahead of the backbone).  Every call still runs each kernel
+        once; outputs equal sequential ``forward`` calls bit for bit."""
         if self.pending_T is None:
             raise RuntimeError("no gathered call is waiting: call gather_ahead first")
         T = self.pending_T

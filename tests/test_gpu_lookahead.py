@@ -138,6 +138,8 @@ def test_lookahead_needs_a_gathered_call(eng):
     site.gather_ahead(c["tokens"], c["cu"])
     with pytest.raises(RuntimeError):
         site.forward(c["tokens"], c["cu"], x)
+    with pytest.raises(RuntimeError):
+        site.gather_ahead(c["tokens"], c["cu"])
     site.run_ahead(x)
     site.forward(c["tokens"], c["cu"], x)
     del site, plain
