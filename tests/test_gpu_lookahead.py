@@ -4,7 +4,8 @@ gather placed between this call's projection and gate, on one stream.
 Bar: every output (streams, and v of the last call) equals sequential
 Engram.forward calls bit for bit -- the same kernels run on the same inputs, only
 in another order -- for one site with the plain, packed and split-K projections
-(with a dead span in one call), and for two sites with per-site row buffers.
+(with a dead span in one call), for two sites with per-site row buffers, and for
+decode steps that continue their stored history (the store equal too).
 """
 import gc
 
@@ -143,4 +144,47 @@ def test_lookahead_needs_a_gathered_call(eng):
     site.run_ahead(x)
     site.forward(c["tokens"], c["cu"], x)
     del site, plain
+    _free()
+
+
+def test_lookahead_decode_steps_with_store(eng):
+    """Decode steps (256 slots, one new token each, continuing their stored
+    history) in the look-ahead order: every step's streams and the store after the
+    last step equal sequential forward calls bit for bit (the split-K projection)."""
+    cfg = ei.get_config("decode")
+    steps = ei.make_decode_steps(cfg, 6)
+    T = steps[0].T
+    dev_steps = [dict(tokens=torch.from_numpy(b.tokens).to(DEV), cu=torch.from_numpy(b.cu_seqlens).to(DEV),
+                      ss=torch.from_numpy(b.seq_start).to(DEV), sl=torch.from_numpy(b.slots).to(DEV))
+                 for b in steps]
+    store0 = torch.from_numpy(ei.make_store_init(cfg)).to(DEV)
+    seq_site = _engram(eng, cfg, T, False)
+    store_seq = store0.clone()
+    seq_out = [ei.make_streams(cfg, T, DEV, step=k) for k in range(len(steps))]
+    for c, x in zip(dev_steps, seq_out):
+        seq_site.forward(c["tokens"], c["cu"], x, seq_start=c["ss"], slots=c["sl"], store=store_seq)
+    torch.cuda.synchronize()
+    kind = seq_site.projection_kind(0, T)
+    del seq_site
+    _free()
+    la_site = _engram(eng, cfg, T, True)
+    store_la = store0.clone()
+    la_out = [ei.make_streams(cfg, T, DEV, step=k) for k in range(len(steps))]
+    c0 = dev_steps[0]
+    la_site.gather_ahead(c0["tokens"], c0["cu"], seq_start=c0["ss"], slots=c0["sl"], store=store_la)
+    for k in range(len(steps)):
+        nxt = dev_steps[k + 1] if k + 1 < len(steps) else None
+        if nxt is None:
+            la_site.run_ahead(la_out[k])
+        else:
+            la_site.run_ahead(la_out[k], next_tokens=nxt["tokens"], next_cu_seqlens=nxt["cu"],
+                              next_seq_start=nxt["ss"], next_slots=nxt["sl"], next_store=store_la)
+    torch.cuda.synchronize()
+    assert eng.engram_get_error() == 0
+    for x, y in zip(seq_out, la_out):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(store_seq, store_la)
+    assert kind == "splitk"
+    log(f"look-ahead order, {len(steps)} decode steps with the store ({kind} projection): bit-identical")
+    del la_site
     _free()
