@@ -213,6 +213,9 @@ def main():
     import torch
 
     import engram_inputs as ei
+    import runpy
+    # only when nothing is built (a fresh checkout): the package needs the library
+    runpy.run_path(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "build_lib.py"))["ensure_built"]()
     import hashed_gram_memory_tid2eid_amd as eng
 
     dev = "cuda:0"

@@ -62,5 +62,11 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def ensure_built() -> str:
+    """Builds the library when it is missing (a fresh checkout); otherwise leaves the
+    built one in place."""
+    return LIB if os.path.exists(LIB) else build()
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
