@@ -347,3 +347,23 @@ def test_bench_refuses_more_than_one_gpu():
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert out.returncode == 2 and "one GPU" in out.stderr
+
+
+def test_projection_split_choice():
+    """The runtime's split-K choice for a call (host logic, no device): no split once
+    the 256 x 256 tiles have many tiles; for few tokens the largest of 2, 4, 8 that keeps
+    at most one workgroup of 128 x 128 tiles per CU, four k-stages per split and k_pad a
+    multiple of 64 x splits."""
+    from hashed_gram_memory_tid2eid_amd.runtime import BIG_PROJECTION, choose_proj_splits
+    assert BIG_PROJECTION == 64 * 256 * 256
+    # the full and prefill workloads: many tokens, no split
+    assert choose_proj_splits(65536, 4096, 19584) == 1
+    assert choose_proj_splits(16384, 4096, 3072) == 1
+    # decode: 256 tokens x 4,096 outputs = 64 tiles -> 4 splits (8 would need 512 CUs)
+    assert choose_proj_splits(256, 4096, 3072) == 4
+    # tiny: 512 x 256 = 8 tiles; 4 splits would leave 192 k per split (< 4 stages)
+    assert choose_proj_splits(512, 256, 768) == 2
+    # k_pad not a multiple of 64 x 2: no split
+    assert choose_proj_splits(64, 256, 320) == 1
+    # a single token: 32 tiles of 128 columns -> 8 splits when k_pad allows
+    assert choose_proj_splits(1, 4096, 4096) == 8
