@@ -367,3 +367,31 @@ def test_projection_split_choice():
     assert choose_proj_splits(64, 256, 320) == 1
     # a single token: 32 tiles of 128 columns -> 8 splits when k_pad allows
     assert choose_proj_splits(1, 4096, 4096) == 8
+
+
+def test_bench_traffic_is_keyed_to_the_kernel_source(tmp_path):
+    """bench.py reports counter-measured traffic only while the kernel source hashes
+    to the value recorded with the counters; an edited kernel gives null."""
+    import importlib.util
+    import shutil
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    full = ei.get_config("full")
+    proj = ("gemm_bf16_nt_packed_{tag}_counters.txt", "gemm_packed.hip")
+    assert bench.measured_traffic(full) > bench.algorithmic_per_token(full)["gather_bytes"] * 65536
+    assert bench.measured_traffic(full, *proj) > 0
+    assert bench.measured_traffic(ei.get_config("tiny")) is None  # no counters for it
+    # the same files under another root, with one comment added to each kernel source
+    shutil.copytree(os.path.join(ROOT, "profiles"), tmp_path / "profiles")
+    kdir = tmp_path / "hashed_gram_memory_tid2eid_amd" / "csrc" / "kernels"
+    kdir.mkdir(parents=True)
+    for name in ("gather.hip", "gemm_packed.hip"):
+        src = open(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "csrc", "kernels", name)).read()
+        (kdir / name).write_text(src)
+    bench.ROOT = str(tmp_path)
+    assert bench.measured_traffic(full) is not None and bench.measured_traffic(full, *proj) is not None
+    for name in ("gather.hip", "gemm_packed.hip"):
+        (kdir / name).write_text((kdir / name).read_text() + "// edited\n")
+    assert bench.measured_traffic(full) is None
+    assert bench.measured_traffic(full, *proj) is None
