@@ -395,3 +395,25 @@ def test_bench_traffic_is_keyed_to_the_kernel_source(tmp_path):
         (kdir / name).write_text((kdir / name).read_text() + "// edited\n")
     assert bench.measured_traffic(full) is None
     assert bench.measured_traffic(full, *proj) is None
+
+
+def test_readme_c_example_compiles_against_the_header(tmp_path):
+    """The C example of the README compiles as C11 against include/engram.h (the ABI
+    is plain C), and every engram_* function it calls is one the library exports."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    text = open(os.path.join(ROOT, "README.md")).read()
+    m = re.search(r"```c\n(.*?)```", text, re.S)
+    assert m, "the README holds a C example"
+    src = tmp_path / "example.c"
+    src.write_text(m.group(1))
+    obj = tmp_path / "example.o"
+    out = subprocess.run([gcc, "-std=c11", "-c", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                          "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src),
+                          "-o", str(obj)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    nm = subprocess.run(["nm", str(obj)], capture_output=True, text=True, check=True).stdout
+    called = {ln.split()[-1] for ln in nm.splitlines() if ln.strip().startswith("U engram_")}
+    assert called and called <= set(declared_functions())
