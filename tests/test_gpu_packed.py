@@ -162,3 +162,37 @@ def test_runtime_picks_packed_for_many_tokens(eng):
     assert torch.equal(v_packed.view(torch.int32), big.v.view(torch.int32))
     del small, big, rows, v_packed
     _free()
+
+
+def test_gated_residual_equals_its_halves_and_the_packed_pair(eng):
+    """engram_gated_residual (projection + gate in one call) leaves the same streams as
+    engram_project then engram_gate_add, and as engram_project_packed then
+    engram_gate_add, bit for bit (rows with a keep mask, prefill-like shape)."""
+    L = _layout(eng, 6, 512)
+    K = L.info.k_pad
+    M, N = 3000, 1024
+    A, B = _operands(L, M, N, seed=5)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(6)
+    x0 = torch.randn((M, 4, N), generator=g, device=DEV).to(torch.bfloat16)
+    keep = (torch.rand(M, generator=g, device=DEV) > 0.1).to(torch.uint8)
+    packed = torch.empty(eng.engram_packed_weight_bytes(L, N), dtype=torch.uint8, device=DEV)
+    eng.engram_pack_weight(L, B, packed)
+    v = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    x1 = x0.clone()
+    eng.engram_gated_residual(L, A, B, x1, v, keep=keep)
+    x2 = x0.clone()
+    eng.engram_project(L, A, B, v)
+    eng.engram_gate_add(L, v, x2, keep=keep)
+    x3 = x0.clone()
+    eng.engram_project_packed(L, A, packed, N, v)
+    eng.engram_gate_add(L, v, x3, keep=keep)
+    torch.cuda.synchronize()
+    assert eng.engram_get_error() == 0
+    assert torch.equal(x1.view(torch.int16), x2.view(torch.int16))
+    assert torch.equal(x1.view(torch.int16), x3.view(torch.int16))
+    dropped = keep == 0
+    assert torch.equal(x1[dropped].view(torch.int16), x0[dropped].view(torch.int16))
+    assert not torch.equal(x1[~dropped].view(torch.int16), x0[~dropped].view(torch.int16))
+    del A, B, packed, v, x0, x1, x2, x3
+    _free()
