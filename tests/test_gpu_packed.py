@@ -196,3 +196,32 @@ def test_gated_residual_equals_its_halves_and_the_packed_pair(eng):
     assert not torch.equal(x1[~dropped].view(torch.int16), x0[~dropped].view(torch.int16))
     del A, B, packed, v, x0, x1, x2, x3
     _free()
+
+
+def test_packed_projection_random_shapes(eng):
+    """24 seeded random shapes (tokens 1..2,000, hidden a multiple of 8 up to 1,200;
+    1 or 2 heads with rows of 1..1,100 elements, and every fourth case 2 heads with rows
+    of 1,400..3,000, so k_pad past 8,192 and both tile heights): bit-identical to
+    engram_project each time."""
+    import numpy as np
+    rng = np.random.default_rng(20261202)
+    for case in range(24):
+        M = int(rng.integers(1, 2001))
+        N = 8 * int(rng.integers(1, 151))
+        if case % 4 == 0:  # k_pad past 8,192: the 256-row tiles
+            cols, D = 6, int(rng.integers(1400, 3001))
+        else:
+            cols, D = 3 * int(rng.integers(1, 3)), int(rng.integers(1, 1101))
+        L = _layout(eng, cols, D)
+        A, B = _operands(L, M, N, seed=case)
+        packed = torch.empty(eng.engram_packed_weight_bytes(L, N), dtype=torch.uint8, device=DEV)
+        eng.engram_pack_weight(L, B, packed)
+        v0 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        v1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        eng.engram_project(L, A, B, v0)
+        eng.engram_project_packed(L, A, packed, N, v1)
+        torch.cuda.synchronize()
+        assert torch.equal(v0.view(torch.int32), v1.view(torch.int32)), (case, M, N, cols, D, L.info.k_pad)
+        del A, B, packed, v0, v1
+    assert eng.engram_get_error() == 0
+    _free()
