@@ -71,8 +71,7 @@ def algorithmic_per_token(cfg):
 def measured_traffic(cfg, profile="gather_dequant_{tag}_traffic.txt", source="gather.hip"):
     """HBM bytes per launch of a kernel from the committed profiler counters
     (profiles/<profile>, by default the gather's), or None when there is no
-    measurement for this workload or the kernel source changed since it was taken."""
-    import hashlib
+    measurement for this workload or the kernel's code changed since it was taken."""
     tag = {"full": "full_fp8"}.get(cfg.name, cfg.name)
     path = os.path.join(ROOT, "profiles", profile.format(tag=tag))
     src = os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "csrc", "kernels", source)
@@ -84,19 +83,27 @@ def measured_traffic(cfg, profile="gather_dequant_{tag}_traffic.txt", source="ga
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    if kv.get("kernel_source_sha256_16") != sha:
+    with open(src) as f:
+        sha = kernel_code_hash(f.read())
+    if kv.get("kernel_code_sha256_16") != sha:
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+def kernel_code_hash(text: str) -> str:
+    """First 16 hex digits of a SHA-256 over a kernel source with its comments removed
+    and its whitespace collapsed: an edit of the code changes it, an edit of a comment
+    does not."""
+    import hashlib
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
 def cpu_baseline(cfg, batch, site_tables, weights, streams_host_bits, budget_s: float):
     """The oracle as it stands, single-threaded on a host core, on a bounded token
     sample of the same workload (rows read from the device tables by torch)."""
-    import numpy as np
-    import torch
-
     import engram_inputs as ei
     import oracle
 
@@ -109,6 +116,40 @@ def cpu_baseline(cfg, batch, site_tables, weights, streams_host_bits, budget_s: 
     else:
         layouts = [oracle.fit_layout([cfg.rows] * 3, cfg.heads)]
     store = ei.make_store_init(cfg) if batch.slots is not None else None
+    # the oracle runs on this thread: pin the calling thread (Linux applies an affinity
+    # set for pid 0 to the caller alone) to one host core for the timed part, and restore
+    # its mask afterwards
+    old_mask = os.sched_getaffinity(0)
+    core = min(old_mask)
+    os.sched_setaffinity(0, {core})
+    try:
+        res = _cpu_baseline_pinned(cfg, batch, site_tables, weights, streams_host_bits, budget_s,
+                                   layouts, tid2eid, store)
+    finally:
+        os.sched_setaffinity(0, old_mask)
+    res["sample"] += f"; pinned to host core {core} of {len(old_mask)} in this process's mask"
+    return res
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (else the machine type)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def _cpu_baseline_pinned(cfg, batch, site_tables, weights, streams_host_bits, budget_s, layouts,
+                         tid2eid, store):
+    import numpy as np
+    import torch
+
+    import oracle
+
     t0 = time.perf_counter()
     site_rows = []
     for si, L in enumerate(layouts):
@@ -164,10 +205,12 @@ def cpu_baseline(cfg, batch, site_tables, weights, streams_host_bits, budget_s: 
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "sample": (f"{done} of {batch.T} tokens of the same batch (seeded), full path per token "
                    f"and site ({cfg.n_sites}): compress+hash (whole batch {t_hash_all:.3f}s, charged "
                    f"pro rata), dequant, fp64 projection, gate; {total:.1f}s of single-thread C on "
-                   f"{platform.processor() or platform.machine()}, {os.cpu_count()} host threads visible"),
+                   f"{cpu_model()}, {os.cpu_count()} host CPUs"),
     }
 
 
@@ -214,7 +257,7 @@ def main():
 
     import engram_inputs as ei
     import runpy
-    # only when nothing is built (a fresh checkout): the package needs the library
+    # builds only when the library is missing or was built from other sources
     runpy.run_path(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "build_lib.py"))["ensure_built"]()
     import hashed_gram_memory_tid2eid_amd as eng
 

@@ -128,6 +128,12 @@ _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
 _sig("engram_host_device_pointer", [_P, ctypes.POINTER(_P)])
 _sig("engram_get_error", [_P])
 _sig("engram_last_hip_error", [], ctypes.c_char_p)
+_sig("engram_build_id", [], ctypes.c_char_p)
+
+
+def engram_build_id() -> str:
+    """'engram-src-sha256:<16 hex>' of the sources the loaded library was built from."""
+    return _lib.engram_build_id().decode()
 
 
 def engram_strerror(status: int) -> str:

@@ -4,10 +4,17 @@ Usage: ``python hashed_gram_memory_tid2eid_amd/build_lib.py`` (run by path: impo
 the package loads the library this script builds).  Compiles the single
 device translation unit and the host sources to objects under ``_build/`` and
 links ``hashed_gram_memory_tid2eid_amd/libengram.so``.  Always recompiles.
+
+The library carries a hash of what it was built from (every source under
+``csrc/`` and ``include/`` plus the compiler flags), readable with
+``engram_build_id()``.  ``ensure_built()`` rebuilds whenever that hash differs
+from the sources in the tree, so a stale library is never loaded.
 """
 from __future__ import annotations
 
+import hashlib
 import os
+import re
 import subprocess
 import sys
 
@@ -28,17 +35,48 @@ COMMON = [
 ]
 
 SOURCES = ["engram_device.hip", "abi.cpp", "layout.cpp"]
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_ID_PREFIX = "engram-src-sha256:"
+
+
+def source_hash() -> str:
+    """First 16 hex digits of a SHA-256 over every source file under csrc/ and
+    include/ (relative path and bytes, in sorted order) and the compiler flags."""
+    h = hashlib.sha256()
+    for top in (CSRC, INCLUDE):
+        for root, dirs, files in os.walk(top):
+            dirs.sort()
+            for f in sorted(files):
+                if f.endswith((".hip", ".cpp", ".h", ".hpp", ".inc")):
+                    path = os.path.join(root, f)
+                    h.update(os.path.relpath(path, ROOT).encode())
+                    with open(path, "rb") as fh:
+                        h.update(fh.read())
+    h.update(" ".join(COMMON).encode())
+    return h.hexdigest()[:16]
+
+
+def built_hash(lib: str = LIB):
+    """The source hash recorded in a built library, or None (missing, or built
+    before the hash existed)."""
+    if not os.path.exists(lib):
+        return None
+    with open(lib, "rb") as f:
+        m = re.search(re.escape(BUILD_ID_PREFIX.encode()) + rb"([0-9a-f]{16})", f.read())
+    return m.group(1).decode() if m else None
 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    sha = source_hash()
     procs = []
     objs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
-        cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        defs = [f'-DENGRAM_BUILD_ID="{BUILD_ID_PREFIX}{sha}"'] if src == "abi.cpp" else []
+        cmd = [HIPCC, *COMMON, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -63,9 +101,12 @@ def build(verbose: bool = False) -> str:
 
 
 def ensure_built() -> str:
-    """Builds the library when it is missing (a fresh checkout); otherwise leaves the
-    built one in place."""
-    return LIB if os.path.exists(LIB) else build()
+    """Builds the library when it is missing or was built from other sources than
+    the tree holds now (compared by the embedded source hash); otherwise leaves
+    the built one in place."""
+    if built_hash() == source_hash():
+        return LIB
+    return build()
 
 
 if __name__ == "__main__":

@@ -454,6 +454,11 @@ extern "C" int engram_get_error(hipStream_t stream) {
 
 extern "C" const char* engram_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
+#ifndef ENGRAM_BUILD_ID
+#define ENGRAM_BUILD_ID "engram-src-sha256:unknown"
+#endif
+extern "C" const char* engram_build_id(void) { return ENGRAM_BUILD_ID; }
+
 extern "C" int engram_host_device_pointer(const void* host, void** dev) {
   if (!host || !dev) return ENGRAM_E_ARG;
   *dev = nullptr;

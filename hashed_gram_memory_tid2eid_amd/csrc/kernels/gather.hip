@@ -1,6 +1,6 @@
 // gather.hip -- row gather + row-wise dequant ([VeOmni#1370] "feat: support
-// DeepSeek-V4.1-Flash in SeedOmni", PR summary: native FP8 row-wise
-// dequantization on lookup).  Included into engram_device.hip.
+// DeepSeek-V4.1-Flash in SeedOmni", PR summary: the FP8 rows are
+// dequantised with their row scale when they are looked up).  Included into engram_device.hip.
 //
 // The output of one call is T token rows of k_pad elements, each the 3*H
 // segments (order-major, then head) of seg_pitch elements; a segment holds the
@@ -19,7 +19,8 @@
 // v_cvt_pk_f32_fp8), times the scale (one v_mul_f32 each: exactly the IEEE
 // product), then round-to-nearest-even to bf16 (v_cvt_pk_bf16_f32) or kept as
 // fp32.  The scale is the row's fp32 scale, or, for (1, 32)-blocked tables
-// ([VeOmni#1370] per-row-scale commit: one exponent per row per 32 columns),
+// ([VeOmni#1370] per-row-scale commit: each row carries an exponent for every block of 32
+// columns),
 // the e8m0 byte b of the chunk's block as the float 2^(b-127) (b = 0 is the
 // subnormal 2^-127, b = 255 NaN); a 16-element chunk never straddles a block.
 // BF16 tables are copied (or widened to fp32).

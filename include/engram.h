@@ -179,8 +179,8 @@ int engram_tid2eid_check(const engram_layout* layout, const int32_t* d_tid2eid,
 /* The store is caller-owned device memory int32 [num_slots][3]: per slot the
  * last three window ids of its sequence, oldest first ([VeOmni#1370] n-gram
  * incremental decode cache commit: the whole cache is a fixed-width tail of
- * max_ngram_size - 1 ids; [vLLM-V41] DeepseekV4Model.__init__: a slot-keyed
- * rolling store of compressed ids for chunked prefill and decode).  A slot
+ * max_ngram_size - 1 ids; [vLLM-V41] DeepseekV4Model.__init__: compressed ids
+ * are kept per KV-cache slot so chunked prefill and decode can look back).  A slot
  * holding pad ids behaves exactly like a sequence start. */
 
 /* d_slots[n] (NULL = all slots, n ignored) <- (pad, pad, pad). */
@@ -224,8 +224,9 @@ int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid,
  *           compress to pad, the id a blocked lookback already reads);
  *   window (w0..w3) = (e_t, e_{t-1}, e_{t-2}, e_{t-3}) where a lookback stops
  *           (reads PAD from there on) at a dead position or before a sequence
- *           that starts here ([VeOmni#1370] n-gram memory lookup commit: an
- *           n-gram never spans an image span or reaches past position 0); a
+ *           that starts here ([VeOmni#1370] n-gram memory lookup commit: no
+ *           n-gram crosses an image span or reaches before the first
+ *           position); a
  *           dead token's own window is all PAD; positions before a continuing
  *           sequence are read from its store slot;
  *   key_n = sum_{j<n} w_j * V_c^j (exact in 64 bits), n = 2, 3, 4;
@@ -260,7 +261,8 @@ int engram_compress_hash(const engram_layout* layout, const int32_t* d_tid2eid,
  *   out[t][(n*H + h)*seg_pitch + d] = fp32(q * scale) rounded to out_dtype,
  *   q = e4m3fn value of table[row][d], row = row_ids[t][site][n][h], scale =
  *   the row's fp32 scale or the e8m0 exponent of its block d / 32 ([VeOmni#1370]
- *   PR summary: native FP8 row-wise dequantization on lookup; per-row-scale
+ *   PR summary: FP8 rows are dequantised with their row scale at lookup time;
+ *   per-row-scale
  *   commit: (1, 32) blocks).  BF16 tables carry no scale and are copied (or
  *   widened to fp32).  Elements d in [D, seg_pitch) of every segment are
  *   written as zero.
@@ -394,6 +396,10 @@ int engram_get_error(hipStream_t stream);
 /* Name of the last HIP runtime error behind an ENGRAM_E_HIP status returned on
  * this thread ("hipSuccess" if none); a static string. */
 const char* engram_last_hip_error(void);
+
+/* Identity of the build: "engram-src-sha256:" followed by 16 hex digits of a
+ * SHA-256 over the library's sources and compiler flags; a static string. */
+const char* engram_build_id(void);
 
 /* ---- host-resident tables -------------------------------------------------- */
 /* Tables too large for HBM may live in pinned host memory (hipHostMalloc); the

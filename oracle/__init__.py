@@ -56,9 +56,14 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        # ORACLE_LIB names another build of the same source (the sanitizer test runs
+        # the pins against an AddressSanitizer / UBSan build this way)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64, i32, u64 = ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
         L.oracle_draw_primes.argtypes = [i32, i32, i32, u64, P]

@@ -20,40 +20,60 @@
 /* Layout: prime draw, floor fit, row-count guard                           */
 /* ------------------------------------------------------------------------ */
 
-static int is_prime_u64(uint64_t n) {
-  if (n < 2) return 0;
-  for (uint64_t d = 2; d * d <= n; ++d)
-    if (n % d == 0) return 0;
-  return 1;
+/* Primality of every integer in [lo, lo + len), by a segmented sieve of
+ * Eratosthenes: the base primes up to sqrt(lo + len - 1) come from a plain sieve,
+ * and each strikes out its multiples inside the window.  out[i] = 1 iff lo + i
+ * is prime.  Returns ORC_E_ARG if a buffer cannot be allocated. */
+static int sieve_window(uint64_t lo, uint64_t len, uint8_t *out) {
+  const uint64_t hi = lo + len - 1;
+  uint64_t r = 1;
+  while ((r + 1) * (r + 1) <= hi) ++r;
+  uint8_t *base = (uint8_t *)malloc((size_t)r + 1);
+  if (!base) return ORC_E_ARG;
+  memset(base, 1, (size_t)r + 1);
+  base[0] = 0;
+  if (r >= 1) base[1] = 0;
+  for (uint64_t p = 2; p * p <= r; ++p)
+    if (base[p])
+      for (uint64_t m = p * p; m <= r; m += p) base[m] = 0;
+  memset(out, 1, (size_t)len);
+  for (uint64_t i = 0; i < len && lo + i < 2; ++i) out[i] = 0; /* 0 and 1 are not prime */
+  for (uint64_t p = 2; p <= r; ++p) {
+    if (!base[p]) continue;
+    uint64_t m = (lo + p - 1) / p * p; /* first multiple of p at or above lo */
+    if (m < p * p) m = p * p;          /* p itself stays prime */
+    for (; m <= hi; m += p) out[m - lo] = 0;
+  }
+  free(base);
+  return ORC_OK;
 }
 
-static int already_drawn(const uint64_t *drawn, int count, uint64_t v) {
-  for (int i = 0; i < count; ++i)
-    if (drawn[i] == v) return 1;
-  return 0;
-}
-
-/* [VeOmni#1370] "n-gram memory lookup" commit and the validate_bucket_layout
- * review thread: for each layer, each order, each head, walk upward from the
- * floor to the next prime that has not been drawn yet.  The walk restarts at
- * the floor for every order, so later orders skip the primes earlier orders
- * (and earlier layers) took. */
+/* [VeOmni#1370] n-gram memory lookup commit and the validate_bucket_layout
+ * review thread: layer after layer, order after order (2 .. max_ngram), head
+ * after head, each bucket takes the smallest prime at or above the floor that
+ * no earlier bucket took.  So the buckets receive the consecutive primes from
+ * the floor upward, in (layer, order, head) order; they are read off a sieved
+ * window above the floor, widened until it holds enough primes. */
 int oracle_draw_primes(int n_layers, int max_ngram, int n_heads, uint64_t floor_,
                        uint64_t *primes_out) {
   if (n_layers < 1 || max_ngram < 2 || n_heads < 1 || floor_ < 1 || !primes_out)
     return ORC_E_ARG;
-  int count = 0;
-  for (int layer = 0; layer < n_layers; ++layer) {
-    for (int order = 2; order <= max_ngram; ++order) {
-      uint64_t cur = floor_ - 1;
-      for (int h = 0; h < n_heads; ++h) {
-        cur += 1;
-        while (!is_prime_u64(cur) || already_drawn(primes_out, count, cur)) cur += 1;
-        primes_out[count++] = cur;
-      }
+  const int need = n_layers * (max_ngram - 1) * n_heads;
+  uint64_t len = 4096;
+  for (;;) {
+    uint8_t *flag = (uint8_t *)malloc((size_t)len);
+    if (!flag) return ORC_E_ARG;
+    if (sieve_window(floor_, len, flag) != ORC_OK) {
+      free(flag);
+      return ORC_E_ARG;
     }
+    int count = 0;
+    for (uint64_t i = 0; i < len && count < need; ++i)
+      if (flag[i]) primes_out[count++] = floor_ + i;
+    free(flag);
+    if (count == need) return ORC_OK;
+    len *= 2;
   }
-  return ORC_OK;
 }
 
 static void offsets_from_primes(const uint64_t *primes, int n_heads, uint64_t *offsets) {
@@ -137,24 +157,24 @@ int oracle_fit_layout(const uint64_t rows[3], int n_heads, uint64_t *floor_out,
 /* Compress + rolling n-gram hash                                           */
 /* ------------------------------------------------------------------------ */
 
-/* Token by token, in sequence order, carrying a three-id tail exactly as the
- * "n-gram incremental decode cache" commit describes: an n-gram ending at a
- * position reaches back max_ngram_size-1 = 3 ids and no further, so the tail is
- * the entire state.
+/* Token by token, in sequence order, carrying a three-id tail as the n-gram
+ * incremental decode cache commit describes: the longest n-gram (order 4) at a
+ * position looks back over at most the 3 ids before it, so those 3 ids are all
+ * the state a sequence needs.
  *
  *  - compress: e = tid2eid[token]; a dead position (image span) compresses to
- *    the pad id ([VeOmni#1370] pack_ngram_inputs commit: pad is what a blocked
- *    lookback compresses to).  PAD = tid2eid[pad_token_id].
+ *    the pad id ([VeOmni#1370] pack_ngram_inputs commit: a dead position takes
+ *    the same pad id that a cut-off lookback reads).  PAD = tid2eid[pad_token_id].
  *  - a sequence that starts here has an all-PAD history (lookback never reaches
  *    past position 0; packed samples restart); a continuing sequence reads the
  *    slot's stored tail ([vLLM-V41] NgramHashState, a slot-keyed rolling store).
  *  - the window of position t is (w0,w1,w2,w3) = (e_t, tail[2], tail[1],
- *    tail[0]); a dead position's own window is all PAD (an n-gram never spans an
+ *    tail[0]); a dead position's own window is all PAD (no n-gram crosses an
  *    image span).
  *  - after t: tail = dead ? (PAD,PAD,PAD) : (tail[1], tail[2], e_t), so nothing
  *    before a dead position is ever read again.
- *  - hash (reading of "every hash multiplier derives from the compressed vocab
- *    size"): key_n = sum_{j<n} w_j * vc^j as an exact integer; the row of head h
+ *  - hash (reading of the pages' statement that the hash multipliers are
+ *    functions of the compressed vocabulary size): key_n = sum_{j<n} w_j * vc^j as an exact integer; the row of head h
  *    is offsets[n][h] + key_n mod primes[n][h].
  */
 int oracle_compress_hash(int64_t vocab, int64_t vc, int64_t pad_token_id, int n_heads,
@@ -323,8 +343,8 @@ int oracle_dequant_rows(const uint8_t *rows, const float *scales, int64_t n, int
 
 /* OCP MX E8M0 scale byte: an unsigned exponent with bias 127, value
  * 2^(b - 127); 0xFF is NaN; there is no zero and no sign.  [VeOmni#1370]
- * per-row-scale commit: the released tables carry one such exponent per row
- * per 32 columns. */
+ * per-row-scale commit: in the released tables every row has such an exponent
+ * for each block of 32 columns. */
 double oracle_e8m0_decode(uint8_t b) {
   if (b == 0xFF) return NAN;
   return ldexp(1.0, (int)b - 127);

@@ -9,8 +9,8 @@ if ROOT not in sys.path:
 
 
 def pytest_sessionstart(session):
-    # a fresh checkout has no built library: build it once (hipcc for gfx950), as the
-    # package refuses to import without it
+    # builds the library (hipcc for gfx950) when it is missing or was built from other
+    # sources than the tree holds: the package refuses to import without it
     import runpy
     runpy.run_path(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "build_lib.py"))["ensure_built"]()
 

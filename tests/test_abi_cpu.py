@@ -370,8 +370,9 @@ def test_projection_split_choice():
 
 
 def test_bench_traffic_is_keyed_to_the_kernel_source(tmp_path):
-    """bench.py reports counter-measured traffic only while the kernel source hashes
-    to the value recorded with the counters; an edited kernel gives null."""
+    """bench.py reports counter-measured traffic only while the kernel's code (its source
+    without comments) hashes to the value recorded with the counters; an edited kernel
+    gives null."""
     import importlib.util
     import shutil
     spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
@@ -391,8 +392,12 @@ def test_bench_traffic_is_keyed_to_the_kernel_source(tmp_path):
         (kdir / name).write_text(src)
     bench.ROOT = str(tmp_path)
     assert bench.measured_traffic(full) is not None and bench.measured_traffic(full, *proj) is not None
+    # a comment edit leaves the kernel as it was measured; a code edit does not
     for name in ("gather.hip", "gemm_packed.hip"):
-        (kdir / name).write_text((kdir / name).read_text() + "// edited\n")
+        (kdir / name).write_text((kdir / name).read_text() + "// edited\n/* edited */\n")
+    assert bench.measured_traffic(full) is not None and bench.measured_traffic(full, *proj) is not None
+    for name in ("gather.hip", "gemm_packed.hip"):
+        (kdir / name).write_text((kdir / name).read_text() + "static int edited;\n")
     assert bench.measured_traffic(full) is None
     assert bench.measured_traffic(full, *proj) is None
 
@@ -417,3 +422,15 @@ def test_readme_c_example_compiles_against_the_header(tmp_path):
     nm = subprocess.run(["nm", str(obj)], capture_output=True, text=True, check=True).stdout
     called = {ln.split()[-1] for ln in nm.splitlines() if ln.strip().startswith("U engram_")}
     assert called and called <= set(declared_functions())
+
+
+def test_loaded_library_is_built_from_the_tree():
+    """The loaded library records the hash of the sources it was built from, and it
+    equals the hash of csrc/ and include/ as they stand (the build step rebuilds a
+    library whose hash differs, so no stale binary is loaded)."""
+    import runpy
+    bl = runpy.run_path(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "build_lib.py"))
+    sha = bl["source_hash"]()
+    assert eng.engram_build_id() == bl["BUILD_ID_PREFIX"] + sha
+    assert bl["built_hash"](eng.LIB_PATH) == sha
+    assert bl["built_hash"](os.path.join(ROOT, "README.md")) is None

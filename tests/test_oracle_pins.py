@@ -78,6 +78,23 @@ def test_prime_draw_vs_sieve(args):
     assert np.array_equal(oracle.draw_primes(*args), draw_by_sieve(is_p, layers, mx, heads, fl))
 
 
+def test_prime_draw_vs_trial_division():
+    """The draw as a walk: every bucket, in (layer, order, head) order, takes the
+    next integer at or above the floor that trial division finds prime and no
+    earlier bucket took."""
+    def is_prime(n):
+        return n >= 2 and all(n % d for d in range(2, math.isqrt(n) + 1))
+
+    for layers, mx, heads, fl in [(1, 4, 2, 64), (2, 4, 3, 1), (3, 4, 2, 1000)]:
+        taken, got, cur = set(), [], fl
+        for _ in range(layers * (mx - 1) * heads):
+            while not is_prime(cur) or cur in taken:
+                cur += 1
+            taken.add(cur)
+            got.append(cur)
+        assert [int(x) for x in oracle.draw_primes(layers, mx, heads, fl).reshape(-1)] == got
+
+
 @pytest.mark.parametrize("name", ["tiny", "prefill", "long", "full"])
 def test_fit_layout_is_the_largest_fitting_floor(name):
     cfg = ei.get_config(name)
@@ -527,6 +544,48 @@ def test_gate_matches_expit_closed_form():
     got = bits_to_f64(y)
     # one bf16 rounding of the fp64 value: within half an ulp (2^-9 relative)
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-300)
+
+
+def test_gate_logit_hand_computed_values():
+    """Values worked out by hand from z = <x_s, v> / sqrt(hidden) and
+    g = 1 / (1 + e^-z).  hidden = 64, v = 0.5 everywhere:
+      stream 0: x = +0.5 -> <x, v> = 16, z = 2,  g = 1 / (1 + 0.1353352832366127)
+                = 0.8807970779778823; y = 0.5 + 0.5 g = 0.94039853898894 -> bf16
+                (step 2^-8 in [0.5, 1)) 241/256 = 0.94140625
+      stream 1: x = -0.5 -> z = -2, g = 0.11920292202211755; y = -0.5 + 0.5 g
+                = -0.44039853898894 -> bf16 (step 2^-9) -225/512 = -0.439453125
+      stream 2: x = 0    -> z = 0,  g = 0.5; y = 0.25
+      stream 3: x = +1.0 -> z = 4,  g = 1 / (1 + 0.01831563888873418)
+                = 0.9820137900379085; y = 1 + 0.5 g = 1.4910068950189543 -> bf16
+                (step 2^-7 in [1, 2)) 191/128 = 1.4921875
+    A sign slip (sigma(-z)) or a 1/hidden scale (z = 0.25 for stream 0) fails here."""
+    hidden = 64
+    xs = np.array([0.5, -0.5, 0.0, 1.0])
+    x = bf16_bits(np.repeat(xs[None, :, None], hidden, axis=2))     # [1][4][64]
+    v = np.full((1, hidden), 0.5)
+    y, g = oracle.gate_add(x, v)
+    g_hand = [0.8807970779778823, 0.11920292202211755, 0.5, 0.9820137900379085]
+    np.testing.assert_allclose(g[0], g_hand, rtol=1e-15, atol=0)
+    y_hand = [0.94140625, -0.439453125, 0.25, 1.4921875]
+    for s in range(4):
+        assert np.all(bits_to_f64(y[0, s]) == y_hand[s]), s
+    # one-hot: v has 8.0 at element 3 only and x_s has 1.0 there -> <x, v> = 8,
+    # z = 1, g = 1 / (1 + 0.36787944117144233) = 0.7310585786300049; element 3
+    # becomes 1 + 8 g = 6.848468629040039 -> bf16 (step 2^-5 in [4, 8)) 219/32 =
+    # 6.84375; every other element keeps x exactly (v is 0 there)
+    rng = np.random.default_rng(12)
+    xr = bits_to_f64(bf16_bits(rng.standard_normal((1, 4, hidden))))
+    xr[:, :, 3] = 1.0
+    xr[:, :, 2] = 0.0   # element 2 of x never meets a non-zero v
+    vr = np.zeros((1, hidden))
+    vr[0, 3] = 8.0
+    y2, g2 = oracle.gate_add(bf16_bits(xr), vr)
+    np.testing.assert_allclose(g2[0], [0.7310585786300049] * 4, rtol=1e-15, atol=0)
+    got = bits_to_f64(y2)
+    assert np.all(got[0, :, 3] == 6.84375)
+    keep = np.ones(hidden, bool)
+    keep[3] = False
+    assert np.array_equal(got[0][:, keep], xr[0][:, keep])
 
 
 # ---------------------------------------------------------------------------
