@@ -317,7 +317,7 @@ def main():
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     tok, cu, ss, sl = d(batch.tokens), d(batch.cu_seqlens), d(batch.seq_start), d(batch.slots)
-    store = d(ei.make_store_init(cfg)) if cfg.decode_steps else None
+    store = site.make_store(cfg.n_seqs, ids=d(ei.make_store_init(cfg))) if cfg.decode_steps else None
     L = site.layout
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -345,15 +345,12 @@ def main():
                                  slots=sl, store=store)
         mark()
         for si in range(NS):
-            kind = site.project(si, site.site_rows[si], T)
+            site.project(si, site.site_rows[si], T)
             mark()
             eng.engram_gather_dequant(L, site.site_tables[si], site.site_scales[si], site.row_ids,
                                       site.site_rows[si], site=si, T=T)
             mark()
-            if kind == "splitk":
-                eng.engram_gate_add_partials(L, site.partials, site.proj_splits, site_streams[si], T=T)
-            else:
-                eng.engram_gate_add(L, site.v, site_streams[si], T=T)
+            site.gate(si, site_streams[si], T)
             mark()
 
     def step_sequential(ev=None):
@@ -379,10 +376,10 @@ def main():
                 mark()
                 site.project(si, site.rows, T)
                 mark()
-            if args.path != "fused" and site.projection_kind(si, T) == "splitk":
-                eng.engram_gate_add_partials(L, site.partials, site.proj_splits, site_streams[si], T=T)
-            else:
+            if args.path == "fused":
                 eng.engram_gate_add(L, site.v, site_streams[si], T=T)
+            else:
+                site.gate(si, site_streams[si], T)
             mark()
 
     def timed(step_fn, sq):
@@ -493,6 +490,7 @@ def main():
         "kernels": kernels,
         "wall_s_timed": wall,
         "setup_s": setup_s,
+        "library": eng.engram_build_id(),
     }
     if args.path != "fused":
         result["roofline_projection"] = roofline_projection

@@ -109,11 +109,14 @@ _sig("engram_layout_create", [ctypes.POINTER(engram_layout_desc), ctypes.POINTER
 _sig("engram_layout_destroy", [_P], None)
 _sig("engram_layout_query", [_P, ctypes.POINTER(engram_layout_info)])
 _sig("engram_tid2eid_check", [_P, _P, ctypes.POINTER(_i32), _P])
-_sig("engram_store_reset", [_P, _P, _i32, _P, _i32, _i32, _P])
-_sig("engram_store_write", [_P, _P, _i32, _P, _i32, _P, _P])
-_sig("engram_store_read", [_P, _P, _i32, _P, _i32, _P, _P])
-_sig("engram_store_rollback", [_P, _P, _P, _i32, _P, _i32, _P, _i32, _P, _P, _P, _P, _P, _P])
-_sig("engram_compress_hash", [_P, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _P, _P, _P, _P])
+_sig("engram_store_create", [_P, _i32, _i32, _P, ctypes.POINTER(_P)])
+_sig("engram_store_destroy", [_P], None)
+_sig("engram_store_query", [_P, ctypes.POINTER(_i32), ctypes.POINTER(_i32)])
+_sig("engram_store_reset", [_P, _P, _i32, _P])
+_sig("engram_store_write", [_P, _P, _i32, _P, _P])
+_sig("engram_store_read", [_P, _P, _i32, _P, _P])
+_sig("engram_store_rollback", [_P, _P, _P, _P, _i32, _P, _i32, _P, _P, _P, _P, _P, _P])
+_sig("engram_compress_hash", [_P, _P, _P, _i32, _P, _i32, _P, _P, _P, _P, _P, _P, _P])
 _sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _i32, _P, _i64, _P])
 _sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
 _sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _i32, _P, _P])
@@ -123,7 +126,13 @@ _sig("engram_pack_weight", [_P, _P, _i64, _i32, _P, _P])
 _sig("engram_project_packed", [_P, _P, _i64, _P, _i32, _P, _i32, _P])
 _sig("engram_project_splitk", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _i32, _P])
 _sig("engram_gate_add_partials", [_P, _P, _i32, _i32, _i32, _P, _P, _P, _i32, _P])
-_sig("engram_gated_residual", [_P, _P, _i64, _P, _i64, _i32, _i32, _P, _P, _P, _i32, _P])
+_sig("engram_projection_plan", [_P, _i32, _i32, _i32, _i32, _P])
+_sig("engram_wkv_create", [_P, _P, _i64, _i32, _i32, _i32, _P, ctypes.POINTER(_P)])
+_sig("engram_wkv_destroy", [_P], None)
+_sig("engram_wkv_plan", [_P, _i32, _P])
+_sig("engram_wkv_project", [_P, _P, _i64, _P, _P, _i32, _P])
+_sig("engram_wkv_gate_add", [_P, _P, _P, _i32, _P, _P, _i32, _P])
+_sig("engram_gated_residual", [_P, _P, _i64, _P, _i32, _P, _P, _P, _i32, _P])
 _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
 _sig("engram_host_device_pointer", [_P, ctypes.POINTER(_P)])
 _sig("engram_get_error", [_P])
@@ -283,32 +292,79 @@ def engram_tid2eid_check(layout: Layout, tid2eid, stream=None) -> int:
 # store
 # ---------------------------------------------------------------------------
 
-def engram_store_reset(layout: Layout, store, pad_eid: int, slots=None, stream=None):
-    import torch
-    n = 0 if slots is None else slots.numel()
-    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
-    _check(_lib.engram_store_reset(layout.handle, _dev(store, torch.int32, "store"), store.shape[0],
-                                   _dev(slots, torch.int32, "slots"), n, pad_eid, _stream(stream)),
-           "engram_store_reset")
+class Store:
+    """Owner of an ``engram_store*`` handle: the slot-keyed rolling store of the last
+    three compressed ids per sequence, library-owned device memory bound to the
+    layout it was made for."""
+
+    def __init__(self, layout: Layout, pad_eid: int, num_slots: int, stream=None):
+        h = _P()
+        _check(_lib.engram_store_create(layout.handle, int(pad_eid), int(num_slots), _stream(stream),
+                                        ctypes.byref(h)), "engram_store_create")
+        self.handle = h.value
+        self.layout = layout  # keeps the layout alive while the store is
+        self.num_slots = int(num_slots)
+        self.pad_eid = int(pad_eid)
+
+    def __del__(self, _destroy=_lib.engram_store_destroy):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            _destroy(h)
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+    def ids(self, stream=None):
+        """A device int32 [num_slots][3] copy of every slot (engram_store_read)."""
+        import torch
+        out = torch.empty((self.num_slots, 3), dtype=torch.int32, device="cuda")
+        engram_store_read(self, None, out, stream=stream)
+        return out
+
+    def load(self, ids, stream=None):
+        """Every slot <- ids (int32 [num_slots][3], device), by engram_store_write."""
+        _need(ids.numel() == 3 * self.num_slots, "ids must be [num_slots][3]")
+        engram_store_write(self, None, ids, stream=stream)
+        return self
 
 
-def engram_store_write(layout: Layout, store, slots, ids, stream=None):
+def engram_store_create(layout: Layout, pad_eid: int, num_slots: int, *, ids=None, stream=None) -> Store:
+    """A store of num_slots slots, all pad ids; with ``ids`` (int32 [num_slots][3] on
+    the device) the slots are then loaded with them."""
+    st = Store(layout, pad_eid, num_slots, stream=stream)
+    if ids is not None:
+        st.load(ids, stream=stream)
+    return st
+
+
+def _slots_arg(slots):
     import torch
-    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
-    _need(ids.numel() >= 3 * slots.numel(), "ids must be [n][3]")
-    _check(_lib.engram_store_write(layout.handle, _dev(store, torch.int32, "store"), store.shape[0],
-                                   _dev(slots, torch.int32, "slots"), slots.numel(),
-                                   _dev(ids, torch.int32, "ids"), _stream(stream)),
+    if slots is None:
+        return None, 0
+    return _dev(slots, torch.int32, "slots"), slots.numel()
+
+
+def engram_store_reset(store: Store, slots=None, stream=None):
+    sp, n = _slots_arg(slots)
+    _check(_lib.engram_store_reset(store.handle, sp, n, _stream(stream)), "engram_store_reset")
+
+
+def engram_store_write(store: Store, slots, ids, stream=None):
+    """store[slots[i]] <- ids[i]; slots None = every slot in order."""
+    import torch
+    sp, n = _slots_arg(slots)
+    _need(ids.numel() >= 3 * (n if slots is not None else store.num_slots), "ids must be [n][3]")
+    _check(_lib.engram_store_write(store.handle, sp, n, _dev(ids, torch.int32, "ids"), _stream(stream)),
            "engram_store_write")
 
 
-def engram_store_read(layout: Layout, store, slots, ids, stream=None):
+def engram_store_read(store: Store, slots, ids, stream=None):
+    """ids[i] <- store[slots[i]]; slots None = every slot in order."""
     import torch
-    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
-    _need(ids.numel() >= 3 * slots.numel(), "ids must be [n][3]")
-    _check(_lib.engram_store_read(layout.handle, _dev(store, torch.int32, "store"), store.shape[0],
-                                  _dev(slots, torch.int32, "slots"), slots.numel(),
-                                  _dev(ids, torch.int32, "ids"), _stream(stream)),
+    sp, n = _slots_arg(slots)
+    _need(ids.numel() >= 3 * (n if slots is not None else store.num_slots), "ids must be [n][3]")
+    _check(_lib.engram_store_read(store.handle, sp, n, _dev(ids, torch.int32, "ids"), _stream(stream)),
            "engram_store_read")
 
 
@@ -324,7 +380,7 @@ def engram_store_rollback(layout: Layout, tid2eid, store, slots, cu_seqlens, eid
     S = slots.numel()
     T = eids.numel()
     _need(cu_seqlens.numel() == S + 1 and keep_len.numel() == S, "cu_seqlens / keep_len size")
-    _need(store.dim() == 2 and store.shape[1] == 3, "store must be [num_slots][3]")
+    _need(isinstance(store, Store), "store must be a Store")
     if snapshot is not None:
         _need(snapshot.numel() >= 3 * S, "snapshot must be [S][3]")
     if seq_start is not None:
@@ -332,8 +388,8 @@ def engram_store_rollback(layout: Layout, tid2eid, store, slots, cu_seqlens, eid
     if dead is not None:
         _need(dead.numel() >= T, "dead must cover the call's tokens")
     _check(_lib.engram_store_rollback(
-        layout.handle, _dev(tid2eid, torch.int32, "tid2eid"), _dev(store, torch.int32, "store"),
-        store.shape[0], _dev(slots, torch.int32, "slots"), S, _dev(cu_seqlens, torch.int32, "cu_seqlens"),
+        layout.handle, _dev(tid2eid, torch.int32, "tid2eid"), store.handle,
+        _dev(slots, torch.int32, "slots"), S, _dev(cu_seqlens, torch.int32, "cu_seqlens"),
         T, _dev(eids, torch.int32, "eids"), None if dead is None else _dev(dead, torch.uint8, "dead"),
         None if seq_start is None else _dev(seq_start, torch.uint8, "seq_start"),
         None if snapshot is None else _dev(snapshot, torch.int32, "snapshot"),
@@ -352,12 +408,12 @@ def engram_compress_hash(layout: Layout, tid2eid, tokens, cu_seqlens, eids, row_
     _need(seq_start is None or seq_start.numel() >= S, "seq_start too small")
     _need(slots is None or slots.numel() >= S, "slots too small")
     _need(dead is None or dead.numel() >= T, "dead too small")
-    _need(store is None or (store.dim() == 2 and store.shape[1] == 3), "store must be [num_slots][3]")
+    _need(store is None or isinstance(store, Store), "store must be a Store (engram_store_create)")
     _check(_lib.engram_compress_hash(
         layout.handle, _dev(tid2eid, torch.int32, "tid2eid"), _dev(tokens, torch.int32, "tokens"), T,
         _dev(cu_seqlens, torch.int32, "cu_seqlens"), S, _dev(seq_start, torch.uint8, "seq_start"),
-        _dev(slots, torch.int32, "slots"), _dev(store, torch.int32, "store"),
-        0 if store is None else store.shape[0], _dev(dead, torch.uint8, "dead"),
+        _dev(slots, torch.int32, "slots"), None if store is None else store.handle,
+        _dev(dead, torch.uint8, "dead"),
         _dev(eids, torch.int32, "eids"), _dev(row_ids, torch.int32, "row_ids"), _stream(stream)),
         "engram_compress_hash")
 
@@ -517,21 +573,97 @@ def engram_gate_add(layout: Layout, v, streams, *, keep=None, T: Optional[int] =
            "engram_gate_add")
 
 
-def engram_gated_residual(layout: Layout, rows, w, streams, v, *, keep=None,
+class engram_proj_plan(ctypes.Structure):
+    _fields_ = [("kernel", _i32), ("splits", _i32)]
+
+
+ENGRAM_PROJ_PLAIN, ENGRAM_PROJ_PACKED, ENGRAM_PROJ_SPLITK = 0, 1, 2
+_PROJ_NAMES = {ENGRAM_PROJ_PLAIN: "plain", ENGRAM_PROJ_PACKED: "packed", ENGRAM_PROJ_SPLITK: "splitk"}
+
+
+def engram_projection_plan(layout: Layout, hidden: int, T: int, *, packed: bool, splits: int = 0):
+    """(kernel name, splits) a T-token projection runs (host logic, no device)."""
+    p = engram_proj_plan()
+    _check(_lib.engram_projection_plan(layout.handle, int(hidden), int(T), int(bool(packed)), int(splits),
+                                       ctypes.byref(p)), "engram_projection_plan")
+    return _PROJ_NAMES[p.kernel], int(p.splits)
+
+
+class Wkv:
+    """Owner of an ``engram_wkv*`` handle: a site's projection weight bound to the
+    layout and the largest call, with the packed copy and split-K workspace the
+    library allocates for it.  Keeps a reference to ``w`` (the library reads it)."""
+
+    def __init__(self, layout: Layout, w, max_tokens: int, splits: int = 0, stream=None):
+        import torch
+        _need(w.dim() == 2, "w must be [hidden][w_ld]")
+        h = _P()
+        _check(_lib.engram_wkv_create(layout.handle, _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0],
+                                      int(max_tokens), int(splits), _stream(stream), ctypes.byref(h)),
+               "engram_wkv_create")
+        self.handle = h.value
+        self.layout = layout
+        self.w = w
+        self.hidden = int(w.shape[0])
+        self.max_tokens = int(max_tokens)
+
+    def __del__(self, _destroy=_lib.engram_wkv_destroy):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            _destroy(h)
+
+    def plan(self, T: int):
+        """(kernel name, splits) of a T-token call."""
+        p = engram_proj_plan()
+        _check(_lib.engram_wkv_plan(self.handle, int(T), ctypes.byref(p)), "engram_wkv_plan")
+        return _PROJ_NAMES[p.kernel], int(p.splits)
+
+
+def engram_wkv_create(layout: Layout, w, max_tokens: int, *, splits: int = 0, stream=None) -> Wkv:
+    return Wkv(layout, w, max_tokens, splits=splits, stream=stream)
+
+
+def _check_gate_args(wkv: Wkv, streams, v, keep, T):
+    _need(streams.dim() == 3 and streams.shape[0] >= T and streams.shape[2] == wkv.hidden,
+          "streams must be [T][hc][hidden]")
+    _need(v.dim() == 2 and v.shape[0] >= T and v.shape[1] == wkv.hidden, "v must be [T][hidden]")
+    _need(keep is None or keep.numel() >= T, "keep too small")
+
+
+def engram_gated_residual(layout: Layout, rows, wkv: Wkv, streams, v, *, keep=None,
                           T: Optional[int] = None, stream=None):
     import torch
     if T is None:
         T = streams.shape[0]
-    _need(streams.dim() == 3 and streams.shape[0] >= T, "streams must be [T][hc][hidden]")
     _need(rows.dim() == 2 and rows.shape[0] >= T, "rows too small")
-    _need(v.dim() == 2 and v.shape[0] >= T and v.shape[1] == streams.shape[2] == w.shape[0],
-          "v must be [T][hidden]")
-    _need(keep is None or keep.numel() >= T, "keep too small")
+    _check_gate_args(wkv, streams, v, keep, T)
     _check(_lib.engram_gated_residual(
-        layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
-        _dev(w, torch.bfloat16, "w"), w.shape[1], w.shape[0], streams.shape[1],
+        layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1], wkv.handle, streams.shape[1],
         _dev(keep, torch.uint8, "keep"), _dev(streams, torch.bfloat16, "streams"),
         _dev(v, torch.float32, "v"), T, _stream(stream)), "engram_gated_residual")
+
+
+def engram_wkv_project(layout: Layout, rows, wkv: Wkv, v, *, T: Optional[int] = None, stream=None):
+    import torch
+    if T is None:
+        T = rows.shape[0]
+    _need(rows.dim() == 2 and rows.shape[0] >= T, "rows too small")
+    _need(v.dim() == 2 and v.shape[0] >= T and v.shape[1] == wkv.hidden, "v must be [T][hidden]")
+    _check(_lib.engram_wkv_project(layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1],
+                                   wkv.handle, _dev(v, torch.float32, "v"), T, _stream(stream)),
+           "engram_wkv_project")
+
+
+def engram_wkv_gate_add(layout: Layout, wkv: Wkv, v, streams, *, keep=None, T: Optional[int] = None,
+                        stream=None):
+    import torch
+    if T is None:
+        T = streams.shape[0]
+    _check_gate_args(wkv, streams, v, keep, T)
+    _check(_lib.engram_wkv_gate_add(layout.handle, wkv.handle, _dev(v, torch.float32, "v"),
+                                    streams.shape[1], _dev(keep, torch.uint8, "keep"),
+                                    _dev(streams, torch.bfloat16, "streams"), T, _stream(stream)),
+           "engram_wkv_gate_add")
 
 
 def engram_get_error(stream=None) -> int:

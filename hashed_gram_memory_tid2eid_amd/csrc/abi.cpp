@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <new>
+
 #include "internal.h"
 
 namespace {
@@ -47,60 +49,119 @@ extern "C" int engram_tid2eid_check(const engram_layout* L, const int32_t* d_tid
 
 // ---- store ------------------------------------------------------------------
 
-static int store_op(const engram_layout* L, int32_t* d_store, int32_t num_slots,
-                    const int32_t* d_slots, int32_t n, int32_t* d_ids, int32_t pad, int op,
-                    hipStream_t stream) {
-  if (!L || !d_store || num_slots < 1) return ENGRAM_E_ARG;
-  if (op != engram::STORE_RESET && (!d_slots || (n > 0 && !d_ids))) return ENGRAM_E_ARG;
+static int current_device(int32_t* dev) {
+  int d = 0;
+  const hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) return hip_status(e);
+  *dev = d;
+  return ENGRAM_OK;
+}
+
+// The store belongs to the device that is current now, and was made for a layout
+// with the same compressed vocabulary and pad token.
+static int store_usable(const engram_store* st, const engram_layout* L) {
+  if (!st) return ENGRAM_E_ARG;
+  if (L && (st->vc != L->desc.compressed_vocab || st->pad_token_id != L->desc.pad_token_id))
+    return ENGRAM_E_ARG;
+  int32_t dev = 0;
+  const int rc = current_device(&dev);
+  if (rc != ENGRAM_OK) return rc;
+  return dev == st->device ? ENGRAM_OK : ENGRAM_E_ARG;
+}
+
+static int store_op(const engram_store* st, const int32_t* d_slots, int32_t n, int32_t* d_ids,
+                    int op, hipStream_t stream) {
+  int rc = store_usable(st, nullptr);
+  if (rc != ENGRAM_OK) return rc;
   if (d_slots && n < 0) return ENGRAM_E_ARG;
+  const int32_t count = d_slots ? n : st->num_slots;
+  if (op != engram::STORE_RESET && count > 0 && !d_ids) return ENGRAM_E_ARG;
   engram::StoreArgs a;
-  a.store = d_store;
-  a.num_slots = num_slots;
+  a.store = st->ids;
+  a.num_slots = st->num_slots;
   a.slots = d_slots;
-  a.n = d_slots ? n : num_slots;
+  a.n = count;
   a.ids = d_ids;
-  a.pad_eid = pad;
+  a.pad_eid = st->pad_eid;
+  a.vc = (int32_t)st->vc;
   a.op = op;
   return hip_status(engram::launch_store_op(a, stream));
 }
 
-extern "C" int engram_store_reset(const engram_layout* L, int32_t* d_store, int32_t num_slots,
-                                  const int32_t* d_slots, int32_t n, int32_t pad_eid,
-                                  hipStream_t stream) {
-  if (L && (pad_eid < 0 || pad_eid >= L->desc.compressed_vocab)) return ENGRAM_E_ARG;
-  return store_op(L, d_store, num_slots, d_slots, n, nullptr, pad_eid, engram::STORE_RESET,
-                  stream);
+extern "C" int engram_store_create(const engram_layout* L, int32_t pad_eid, int32_t num_slots,
+                                   hipStream_t stream, engram_store** out) {
+  if (!L || !out || num_slots < 1) return ENGRAM_E_ARG;
+  *out = nullptr;
+  if (pad_eid < 0 || pad_eid >= L->desc.compressed_vocab) return ENGRAM_E_ARG;
+  engram_store* st = new (std::nothrow) engram_store();
+  if (!st) return ENGRAM_E_ARG;
+  int rc = current_device(&st->device);
+  if (rc != ENGRAM_OK) {
+    delete st;
+    return rc;
+  }
+  const hipError_t e = hipMalloc(&st->ids, (size_t)num_slots * 3 * sizeof(int32_t));
+  if (e != hipSuccess) {
+    delete st;
+    return hip_status(e);
+  }
+  st->num_slots = num_slots;
+  st->pad_eid = pad_eid;
+  st->vc = L->desc.compressed_vocab;
+  st->pad_token_id = L->desc.pad_token_id;
+  rc = store_op(st, nullptr, 0, nullptr, engram::STORE_RESET, stream);
+  if (rc != ENGRAM_OK) {
+    engram_store_destroy(st);
+    return rc;
+  }
+  *out = st;
+  return ENGRAM_OK;
 }
 
-extern "C" int engram_store_write(const engram_layout* L, int32_t* d_store, int32_t num_slots,
-                                  const int32_t* d_slots, int32_t n, const int32_t* d_ids,
-                                  hipStream_t stream) {
-  return store_op(L, d_store, num_slots, d_slots, n, const_cast<int32_t*>(d_ids), 0,
-                  engram::STORE_WRITE, stream);
+extern "C" void engram_store_destroy(engram_store* st) {
+  if (!st) return;
+  (void)hipFree(st->ids);
+  delete st;
 }
 
-extern "C" int engram_store_read(const engram_layout* L, const int32_t* d_store,
-                                 int32_t num_slots, const int32_t* d_slots, int32_t n,
+extern "C" int engram_store_query(const engram_store* st, int32_t* num_slots, int32_t* pad_eid) {
+  if (!st) return ENGRAM_E_ARG;
+  if (num_slots) *num_slots = st->num_slots;
+  if (pad_eid) *pad_eid = st->pad_eid;
+  return ENGRAM_OK;
+}
+
+extern "C" int engram_store_reset(engram_store* st, const int32_t* d_slots, int32_t n,
+                                  hipStream_t stream) {
+  return store_op(st, d_slots, n, nullptr, engram::STORE_RESET, stream);
+}
+
+extern "C" int engram_store_write(engram_store* st, const int32_t* d_slots, int32_t n,
+                                  const int32_t* d_ids, hipStream_t stream) {
+  return store_op(st, d_slots, n, const_cast<int32_t*>(d_ids), engram::STORE_WRITE, stream);
+}
+
+extern "C" int engram_store_read(const engram_store* st, const int32_t* d_slots, int32_t n,
                                  int32_t* d_ids, hipStream_t stream) {
-  return store_op(L, const_cast<int32_t*>(d_store), num_slots, d_slots, n, d_ids, 0,
-                  engram::STORE_READ, stream);
+  return store_op(st, d_slots, n, d_ids, engram::STORE_READ, stream);
 }
 
 extern "C" int engram_store_rollback(const engram_layout* L, const int32_t* d_tid2eid,
-                                    int32_t* d_store, int32_t num_slots, const int32_t* d_slots,
-                                    int32_t S, const int32_t* d_cu_seqlens, int32_t T,
-                                    const int32_t* d_eids, const uint8_t* d_dead,
-                                    const uint8_t* d_seq_start, const int32_t* d_snapshot,
-                                    const int32_t* d_keep_len, hipStream_t stream) {
+                                    engram_store* st, const int32_t* d_slots, int32_t S,
+                                    const int32_t* d_cu_seqlens, int32_t T, const int32_t* d_eids,
+                                    const uint8_t* d_dead, const uint8_t* d_seq_start,
+                                    const int32_t* d_snapshot, const int32_t* d_keep_len,
+                                    hipStream_t stream) {
   if (!L || S < 0 || T < 0) return ENGRAM_E_ARG;
   if (S == 0) return ENGRAM_OK;
-  if (!d_tid2eid || !d_store || num_slots < 1 || !d_slots || !d_cu_seqlens || !d_keep_len)
-    return ENGRAM_E_ARG;
+  if (!d_tid2eid || !d_slots || !d_cu_seqlens || !d_keep_len) return ENGRAM_E_ARG;
+  const int rc = store_usable(st, L);
+  if (rc != ENGRAM_OK) return rc;
   if (T > 0 && !d_eids) return ENGRAM_E_ARG;
   if (d_seq_start && !d_snapshot) return ENGRAM_E_ARG;  // continuing sequences need their tails
   engram::RollbackArgs a;
-  a.store = d_store;
-  a.num_slots = num_slots;
+  a.store = st->ids;
+  a.num_slots = st->num_slots;
   a.slots = d_slots;
   a.S = S;
   a.T = T;
@@ -121,13 +182,17 @@ extern "C" int engram_compress_hash(const engram_layout* L, const int32_t* d_tid
                                     const int32_t* d_tokens, int32_t T,
                                     const int32_t* d_cu_seqlens, int32_t S,
                                     const uint8_t* d_seq_start, const int32_t* d_slots,
-                                    int32_t* d_store, int32_t num_slots, const uint8_t* d_dead,
-                                    int32_t* d_eids, int32_t* d_row_ids, hipStream_t stream) {
+                                    engram_store* store, const uint8_t* d_dead, int32_t* d_eids,
+                                    int32_t* d_row_ids, hipStream_t stream) {
   if (!L || T < 0 || S < 0 || !d_tid2eid) return ENGRAM_E_ARG;
   if (T > 0 && (S < 1 || !d_tokens || !d_eids || !d_row_ids)) return ENGRAM_E_ARG;
   if (S > 0 && !d_cu_seqlens) return ENGRAM_E_ARG;
-  if (d_store && num_slots < 1) return ENGRAM_E_ARG;
-  if (!d_store) num_slots = 0;
+  if (store) {
+    const int rc = store_usable(store, L);
+    if (rc != ENGRAM_OK) return rc;
+  }
+  int32_t* d_store = store ? store->ids : nullptr;
+  const int32_t num_slots = store ? store->num_slots : 0;
   if (T == 0 && S == 0) return ENGRAM_OK;
   engram::HashArgs a;
   a.tid2eid = d_tid2eid;
@@ -432,17 +497,186 @@ extern "C" int engram_gate_add_partials(const engram_layout* L, const float* d_p
   return hip_status(engram::launch_gate_add(a, stream));
 }
 
-extern "C" int engram_gated_residual(const engram_layout* L, const void* d_rows,
-                                     int64_t rows_ld, const void* d_w, int64_t w_ld,
-                                     int32_t hidden, int32_t hc_mult, const uint8_t* d_keep,
-                                     void* d_streams, float* d_v, int32_t T, hipStream_t stream) {
+// ---- 3'. the wkv handle: the projection kernel chosen per call ------------------
+
+namespace {
+
+// Calls with at least this many outputs (tokens x hidden), i.e. 64 tiles of
+// 256 x 256, take the packed kernel's 256-row tiles.
+constexpr int64_t kBigProjection = 64 * 256 * 256;
+constexpr int kCUs = 256;
+
+// Split-K factor chosen for a call: the largest of 2, 4, 8 that keeps the 128 x 128
+// tiles times the splits within one workgroup per CU, at least 4 k-steps of 64 per
+// split, and k_pad a multiple of 64 x splits; 1 when none does.  (Decode, 256 tokens
+// x 4,096 outputs: 64 tiles -> 4 splits, measured 24 us against 42 us unsplit.)
+int choose_splits(int64_t T, int64_t hidden, int64_t k_pad) {
+  const int64_t tiles = ((T + 127) / 128) * ((hidden + 127) / 128);
+  int best = 1;
+  for (int s = 2; s <= 8; s *= 2)
+    if (tiles * s <= kCUs && k_pad % (64 * s) == 0 && k_pad / s >= 256) best = s;
+  return best;
+}
+
+engram_proj_plan plan_for(int64_t T, int64_t hidden, int64_t k_pad, bool packed, int forced) {
+  engram_proj_plan p;
+  p.kernel = ENGRAM_PROJ_PLAIN;
+  p.splits = 1;
+  if (packed && T * hidden >= kBigProjection) {
+    p.kernel = ENGRAM_PROJ_PACKED;
+    return p;
+  }
+  const int s = forced > 0 ? forced : (T * hidden >= kBigProjection ? 1 : choose_splits(T, hidden, k_pad));
+  if (s > 1) {
+    p.kernel = ENGRAM_PROJ_SPLITK;
+    p.splits = s;
+  }
+  return p;
+}
+
+// The packed kernel addresses 8 column tiles of the packed weight with 32-bit offsets.
+bool packed_weight_addressable(int64_t k_pad) { return (int64_t)8 * k_pad * 64 <= INT32_MAX; }
+
+int wkv_usable(const engram_wkv* W, const engram_layout* L, int32_t T) {
+  if (!W || !L || T < 0 || T > W->max_tokens || W->k_pad != L->k_pad) return ENGRAM_E_ARG;
+  int d = 0;
+  const hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) return hip_status(e);
+  return d == W->device ? ENGRAM_OK : ENGRAM_E_ARG;
+}
+
+int gate_shape(int32_t hidden, int32_t hc_mult) {
   if (hc_mult != 4) return ENGRAM_E_UNSUPPORTED;
   if (hidden < 8 || hidden % 8 != 0) return ENGRAM_E_ALIGN;
   if (hidden > 8192) return ENGRAM_E_UNSUPPORTED;
-  if (d_v && !aligned(d_v, 16)) return ENGRAM_E_ALIGN;
-  int rc = engram_project(L, d_rows, rows_ld, d_w, w_ld, hidden, d_v, T, stream);
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+extern "C" int engram_projection_plan(const engram_layout* L, int32_t hidden, int32_t T,
+                                      int32_t packed, int32_t splits, engram_proj_plan* plan) {
+  if (!L || hidden < 1 || T < 0 || splits < 0 || !plan) return ENGRAM_E_ARG;
+  *plan = plan_for(T, hidden, L->k_pad, packed != 0 && packed_weight_addressable(L->k_pad), splits);
+  return ENGRAM_OK;
+}
+
+extern "C" int engram_wkv_create(const engram_layout* L, const void* d_w, int64_t w_ld,
+                                 int32_t hidden, int32_t max_tokens, int32_t splits,
+                                 hipStream_t stream, engram_wkv** out) {
+  if (!L || !d_w || !out || hidden < 1 || max_tokens < 1 || splits < 0 || splits > 64)
+    return ENGRAM_E_ARG;
+  *out = nullptr;
+  if (w_ld < L->k_pad || w_ld % 8 || !aligned(d_w, 16)) return ENGRAM_E_ALIGN;
+  if (splits > 1 && L->k_pad % (64 * (int64_t)splits) != 0) return ENGRAM_E_ALIGN;
+  engram_wkv* W = new (std::nothrow) engram_wkv();
+  if (!W) return ENGRAM_E_ARG;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    delete W;
+    return hip_status(e);
+  }
+  W->device = dev;
+  W->w = d_w;
+  W->w_ld = w_ld;
+  W->hidden = hidden;
+  W->max_tokens = max_tokens;
+  W->forced_splits = splits;
+  W->k_pad = L->k_pad;
+  // packed copy: only if some call of up to max_tokens tokens takes the packed kernel
+  const bool can_pack = packed_weight_addressable(L->k_pad);
+  if (can_pack && (int64_t)max_tokens * hidden >= kBigProjection) {
+    int64_t bytes = 0;
+    (void)engram_packed_weight_bytes(L, hidden, &bytes);
+    e = hipMalloc(&W->packed, (size_t)bytes);
+    int rc = e == hipSuccess ? ENGRAM_OK : hip_status(e);
+    if (rc == ENGRAM_OK) rc = engram_pack_weight(L, d_w, w_ld, hidden, W->packed, stream);
+    if (rc != ENGRAM_OK) {
+      engram_wkv_destroy(W);
+      return rc;
+    }
+  }
+  // split-K workspace: the largest splits x T x hidden any call will need
+  int64_t need = 0;
+  for (int64_t T = 1; T <= max_tokens; ++T) {
+    const engram_proj_plan p = plan_for(T, hidden, L->k_pad, W->packed != nullptr, splits);
+    if (p.kernel == ENGRAM_PROJ_SPLITK && (int64_t)p.splits * T * hidden > need)
+      need = (int64_t)p.splits * T * hidden;
+    if (p.kernel == ENGRAM_PROJ_PACKED) break;  // every larger call is packed too
+  }
+  if (need > 0) {
+    e = hipMalloc(&W->partials, (size_t)need * sizeof(float));
+    if (e != hipSuccess) {
+      engram_wkv_destroy(W);
+      return hip_status(e);
+    }
+    W->partial_elems = need;
+  }
+  *out = W;
+  return ENGRAM_OK;
+}
+
+extern "C" void engram_wkv_destroy(engram_wkv* W) {
+  if (!W) return;
+  if (W->packed) (void)hipFree(W->packed);
+  if (W->partials) (void)hipFree(W->partials);
+  delete W;
+}
+
+extern "C" int engram_wkv_plan(const engram_wkv* W, int32_t T, engram_proj_plan* plan) {
+  if (!W || !plan || T < 0 || T > W->max_tokens) return ENGRAM_E_ARG;
+  *plan = plan_for(T, W->hidden, W->k_pad, W->packed != nullptr, W->forced_splits);
+  return ENGRAM_OK;
+}
+
+extern "C" int engram_wkv_project(const engram_layout* L, const void* d_rows, int64_t rows_ld,
+                                  const engram_wkv* W, float* d_v, int32_t T, hipStream_t stream) {
+  int rc = wkv_usable(W, L, T);
   if (rc != ENGRAM_OK) return rc;
-  return engram_gate_add(L, d_v, hidden, hc_mult, d_keep, d_streams, T, stream);
+  if (T == 0) return ENGRAM_OK;
+  if (!d_v) return ENGRAM_E_ARG;
+  const engram_proj_plan p = plan_for(T, W->hidden, W->k_pad, W->packed != nullptr, W->forced_splits);
+  if (p.kernel == ENGRAM_PROJ_PACKED) {
+    rc = engram_project_packed(L, d_rows, rows_ld, W->packed, W->hidden, d_v, T, stream);
+    if (rc != ENGRAM_E_UNSUPPORTED) return rc;
+    // rows too wide for the packed kernel's 32-bit tile offsets: the plain kernel
+  } else if (p.kernel == ENGRAM_PROJ_SPLITK) {
+    if ((int64_t)p.splits * T * W->hidden > W->partial_elems) return ENGRAM_E_ARG;
+    return engram_project_splitk(L, d_rows, rows_ld, W->w, W->w_ld, W->hidden, W->partials,
+                                 p.splits, T, stream);
+  }
+  return engram_project(L, d_rows, rows_ld, W->w, W->w_ld, W->hidden, d_v, T, stream);
+}
+
+extern "C" int engram_wkv_gate_add(const engram_layout* L, const engram_wkv* W, float* d_v,
+                                   int32_t hc_mult, const uint8_t* d_keep, void* d_streams,
+                                   int32_t T, hipStream_t stream) {
+  int rc = wkv_usable(W, L, T);
+  if (rc != ENGRAM_OK) return rc;
+  rc = gate_shape(W->hidden, hc_mult);
+  if (rc != ENGRAM_OK) return rc;
+  if (T == 0) return ENGRAM_OK;
+  const engram_proj_plan p = plan_for(T, W->hidden, W->k_pad, W->packed != nullptr, W->forced_splits);
+  if (p.kernel == ENGRAM_PROJ_SPLITK)
+    return engram_gate_add_partials(L, W->partials, p.splits, W->hidden, hc_mult, d_keep, d_streams,
+                                    d_v, T, stream);
+  return engram_gate_add(L, d_v, W->hidden, hc_mult, d_keep, d_streams, T, stream);
+}
+
+extern "C" int engram_gated_residual(const engram_layout* L, const void* d_rows, int64_t rows_ld,
+                                     const engram_wkv* W, int32_t hc_mult, const uint8_t* d_keep,
+                                     void* d_streams, float* d_v, int32_t T, hipStream_t stream) {
+  int rc = wkv_usable(W, L, T);
+  if (rc != ENGRAM_OK) return rc;
+  rc = gate_shape(W->hidden, hc_mult);
+  if (rc != ENGRAM_OK) return rc;
+  if (T == 0) return ENGRAM_OK;
+  if (!d_rows || !d_streams || !d_v) return ENGRAM_E_ARG;
+  if (!aligned(d_v, 16) || !aligned(d_streams, 16)) return ENGRAM_E_ALIGN;
+  rc = engram_wkv_project(L, d_rows, rows_ld, W, d_v, T, stream);
+  if (rc != ENGRAM_OK) return rc;
+  return engram_wkv_gate_add(L, W, d_v, hc_mult, d_keep, d_streams, T, stream);
 }
 
 extern "C" int engram_get_error(hipStream_t stream) {

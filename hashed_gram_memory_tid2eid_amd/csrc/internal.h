@@ -24,6 +24,32 @@ struct engram_layout {
   uint64_t vc_pow[4];                    // V_c^0 .. V_c^3
 };
 
+// A rolling store: device int32 [num_slots][3] owned by the handle, bound to the
+// compressed vocabulary and pad id of the layout it was made for.
+struct engram_store {
+  int32_t* ids;
+  int32_t num_slots;
+  int32_t pad_eid;
+  int64_t vc;
+  int64_t pad_token_id;
+  int32_t device;
+};
+
+// A site's projection weight: the caller's bf16 [hidden][w_ld] matrix, its packed
+// copy (or null) and the split-K workspace (or null), owned by the handle.
+struct engram_wkv {
+  const void* w;
+  int64_t w_ld;
+  int32_t hidden;
+  int32_t max_tokens;
+  int32_t forced_splits;   // 0: chosen per call
+  int64_t k_pad;
+  void* packed;            // packed weight, or null
+  float* partials;         // float [splits][T][hidden] workspace, or null
+  int64_t partial_elems;   // capacity of partials
+  int32_t device;
+};
+
 namespace engram {
 
 // Device-side status word (one per device, see engram_get_error).
@@ -80,6 +106,7 @@ struct StoreArgs {
   int32_t n;
   int32_t* ids;          // [n][3]
   int32_t pad_eid;
+  int32_t vc;            // STORE_WRITE: ids must lie in [0, vc)
   int32_t op;
 };
 hipError_t launch_store_op(const StoreArgs& a, hipStream_t stream);

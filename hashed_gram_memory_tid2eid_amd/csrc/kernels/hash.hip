@@ -277,12 +277,21 @@ __global__ __launch_bounds__(256) void store_op_kernel(StoreArgs a) {
     return;
   }
   int32_t* cell = a.store + 3 * (int64_t)slot + c;
-  if (a.op == STORE_RESET)
+  if (a.op == STORE_RESET) {
     *cell = a.pad_eid;
-  else if (a.op == STORE_WRITE)
-    *cell = a.ids[i];
-  else
+  } else if (a.op == STORE_WRITE) {
+    // a row with any id outside [0, vc) is not written at all
+    const int32_t* row = a.ids + 3 * r;
+    bool ok = true;
+    for (int j = 0; j < 3; ++j) ok = ok && row[j] >= 0 && row[j] < a.vc;
+    if (!ok) {
+      if (c == 0) latch_error(ENGRAM_E_ID_RANGE);
+      return;
+    }
+    *cell = row[c];
+  } else {
     a.ids[i] = *cell;
+  }
 }
 
 hipError_t launch_store_op(const StoreArgs& a, hipStream_t stream) {

@@ -240,6 +240,7 @@ extern "C" const char* engram_strerror(int s) {
     case ENGRAM_E_HIP: return "HIP runtime error";
     case ENGRAM_E_NOFIT: return "no bucket floor fits the table rows";
     case ENGRAM_E_UNSUPPORTED: return "unsupported shape";
+    case ENGRAM_E_ID_RANGE: return "compressed id written to the store outside [0, compressed_vocab)";
     default: return "unknown status";
   }
 }

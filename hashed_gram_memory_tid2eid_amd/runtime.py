@@ -2,11 +2,12 @@
 device buffers.
 
 ``Engram.forward`` = engram_compress_hash (every site in one pass) -> for each
-site engram_gather_dequant -> projection (engram_project_packed for many tokens,
-engram_project_splitk for few, else engram_project) -> engram_gate_add, on one
-stream, no host synchronisation, no allocation (path "split", the default).  Path "fused" (e4m3fn tables) replaces the
-gather and the projection by engram_gather_project, which keeps the gathered
-rows on chip: no [T][k_pad] bf16 row buffer, at a lower projection rate.
+site engram_gather_dequant -> engram_gated_residual (the projection kernel the
+site's wkv handle plans for the call, then the gated add), on one stream, no
+host synchronisation, no allocation (path "split", the default).  Path "fused"
+(e4m3fn tables) replaces the gather and the projection by engram_gather_project,
+which keeps the gathered rows on chip: no [T][k_pad] bf16 row buffer, at a lower
+projection rate.
 
 The order follows the pages' forward: one hash pass over the flattened batch
 before the layers ([vLLM-V41] "vllm/models/deepseek_v41/nvidia/model",
@@ -19,14 +20,10 @@ from __future__ import annotations
 from typing import Optional, Sequence
 
 from . import (ENGRAM_DTYPE_BF16, ENGRAM_DTYPE_FP8_E4M3FN, ENGRAM_SCALE_BLOCK32_E8M0,
-               ENGRAM_SCALE_ROW_F32, ENGRAM_TABLE_PER_SITE, ENGRAM_TABLES_PER_ORDER, Layout,
-               engram_compress_hash, engram_gate_add_partials, engram_project_splitk,
-               engram_gate_add, engram_gather_dequant, engram_gather_project,
-               engram_layout_create, engram_pack_weight, engram_packed_weight_bytes,
-               engram_project, engram_project_packed, engram_tid2eid_check)
-
-# calls with at least this many outputs (tokens x hidden) take the 256 x 256 tiles
-BIG_PROJECTION = 64 * 256 * 256
+               ENGRAM_SCALE_ROW_F32, ENGRAM_TABLE_PER_SITE, ENGRAM_TABLES_PER_ORDER, Layout, Wkv,
+               engram_compress_hash, engram_gate_add, engram_gated_residual, engram_gather_dequant,
+               engram_gather_project, engram_layout_create, engram_tid2eid_check,
+               engram_wkv_gate_add, engram_wkv_project)
 
 
 def pad_weight(w, layout: Layout):
@@ -44,23 +41,6 @@ def pad_weight(w, layout: Layout):
     out = torch.zeros((hidden, info.k_pad), dtype=torch.bfloat16, device=w.device)
     out.view(hidden, cols, sp)[:, :, :D].copy_(w.view(hidden, cols, D))
     return out
-
-
-def choose_proj_splits(tokens: int, hidden: int, k_pad: int) -> int:
-    """Split-K factor for the projection of `tokens` tokens: 1 while the 128 x 128
-    tiles alone give the chip (256 CUs) a workgroup per CU, else the largest of
-    2, 4, 8 that keeps at most one workgroup per CU, at least 4 k-stages of 64
-    per split, and k_pad a multiple of 64 x splits.  (Decode, 256 tokens x 4,096
-    outputs: 64 tiles -> 4 splits, measured 24 us for the projection against
-    42 us unsplit; 8 splits measured no faster.)"""
-    if tokens * hidden >= BIG_PROJECTION:  # the 256 x 256 path: many tiles already
-        return 1
-    tiles = -(-tokens // 128) * -(-hidden // 128)
-    best = 1
-    for s in (2, 4, 8):
-        if tiles * s <= 256 and k_pad % (64 * s) == 0 and k_pad // s >= 256:
-            best = s
-    return best
 
 
 class Engram:
@@ -115,13 +95,11 @@ class Engram:
         self.hidden = hidden
         self.hc_mult = hc_mult
         self.max_tokens = max_tokens
-        # many-token calls project from the weight in fragment order (packed once here)
-        self.site_packed = [None] * num_sites
-        if path == "split" and max_tokens * hidden >= BIG_PROJECTION:
-            nbytes = engram_packed_weight_bytes(self.layout, hidden)
-            for s, w in enumerate(self.site_weights):
-                self.site_packed[s] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-                engram_pack_weight(self.layout, w, self.site_packed[s], stream)
+        # the split path projects through a wkv handle per site: the library packs the
+        # weight when calls can be large, keeps the split-K workspace when they can be
+        # small, and picks the kernel per call (proj_splits 0 = its choice)
+        self.site_wkv = ([Wkv(self.layout, w, max_tokens, splits=proj_splits, stream=stream)
+                          for w in self.site_weights] if path == "split" else [None] * num_sites)
         self.eids = torch.empty(max_tokens, dtype=torch.int32, device=dev)
         rid_shape = ((max_tokens, 3, info.heads) if num_sites == 1
                      else (max_tokens, num_sites, 3, info.heads))
@@ -137,15 +115,6 @@ class Engram:
                           if lookahead else None)
         self.pending_T = None  # tokens of the call whose rows wait for run_ahead
         self.v = torch.empty((max_tokens, hidden), dtype=torch.float32, device=dev)
-        # split-K projection for few tokens: the partial slices live in a workspace
-        # sized once here; 0 = choose from the call size
-        if proj_splits == 0:
-            proj_splits = choose_proj_splits(max_tokens, hidden, info.k_pad)
-        if proj_splits > 1 and info.k_pad % (64 * proj_splits) != 0:
-            raise ValueError(f"k_pad {info.k_pad} is not a multiple of 64 x {proj_splits} splits")
-        self.proj_splits = proj_splits if path == "split" else 1
-        self.partials = (torch.empty(self.proj_splits * max_tokens * hidden, dtype=torch.float32,
-                                     device=dev) if self.proj_splits > 1 else None)
         # prefetch ring: slot -> per-site gathered rows, and the event after which the
         # slot's last reader (apply) is done with it
         if prefetch_slots and path != "split":
@@ -155,6 +124,12 @@ class Engram:
         self.pre_free = [None] * prefetch_slots
         self.pre_pending = [set() for _ in range(prefetch_slots)]  # sites not yet applied
         self._next_slot = 0
+
+    def make_store(self, num_slots: int, ids=None, stream=None):
+        """A rolling store (engram_store_create) for this layout: num_slots slots of pad
+        ids, or loaded with ``ids`` (int32 [num_slots][3] on the device)."""
+        from . import engram_store_create
+        return engram_store_create(self.layout, self.pad_eid, num_slots, ids=ids, stream=stream)
 
     # single-site views
     @property
@@ -192,34 +167,39 @@ class Engram:
                               self.row_ids, self.rows, site=site, T=T, stream=stream)
         return self.project_gate(site, self.rows, streams, T, keep=keep, stream=stream)
 
+    def projection_plan(self, site: int, T: int):
+        """(kernel, splits) of a T-token projection of `site`: kernel "packed" (256-row
+        tiles from the packed weight), "splitk" (few tokens) or "plain", as the
+        library's wkv handle plans it."""
+        if self.site_wkv[site] is None:
+            return "fused", 1
+        return self.site_wkv[site].plan(T)
+
     def projection_kind(self, site: int, T: int) -> str:
-        """Which projection a T-token call of `site` runs: "packed" (256 x 256 tiles
-        from the packed weight), "splitk" (few tokens) or "plain"."""
-        if self.site_packed[site] is not None and T * self.hidden >= BIG_PROJECTION:
-            return "packed"
-        return "splitk" if self.proj_splits > 1 else "plain"
+        return self.projection_plan(site, T)[0]
+
+    @property
+    def proj_splits(self) -> int:
+        """Split-K factor of a max_tokens call of site 0."""
+        return self.projection_plan(0, self.max_tokens)[1]
 
     def project(self, site: int, rows, T: int, *, stream=None):
-        """v (or the split-K partial slices of v) of `rows` for `site`."""
-        kind = self.projection_kind(site, T)
-        if kind == "packed":
-            engram_project_packed(self.layout, rows, self.site_packed[site], self.hidden, self.v, T=T,
-                                  stream=stream)
-        elif kind == "splitk":
-            engram_project_splitk(self.layout, rows, self.site_weights[site], self.partials,
-                                  self.proj_splits, T=T, stream=stream)
-        else:
-            engram_project(self.layout, rows, self.site_weights[site], self.v, T=T, stream=stream)
-        return kind
+        """First half of engram_gated_residual: v (or, split-K, its partial slices in
+        the handle's workspace) of `rows` for `site`."""
+        engram_wkv_project(self.layout, rows, self.site_wkv[site], self.v, T=T, stream=stream)
+
+    def gate(self, site: int, streams, T: int, *, keep=None, stream=None):
+        """Second half of engram_gated_residual: the gated add of v (split-K: the slices
+        summed into v first) into `streams`."""
+        engram_wkv_gate_add(self.layout, self.site_wkv[site], self.v, streams, keep=keep, T=T,
+                            stream=stream)
 
     def project_gate(self, site: int, rows, streams, T: int, *, keep=None, stream=None):
-        """Projection and gated residual of `site` from gathered `rows`.  There is no
-        variant without rows: a site with no looked-up rows is a caller error."""
-        if self.project(site, rows, T, stream=stream) == "splitk":
-            engram_gate_add_partials(self.layout, self.partials, self.proj_splits, streams, keep=keep,
-                                     v=self.v, T=T, stream=stream)
-        else:
-            engram_gate_add(self.layout, self.v, streams, keep=keep, T=T, stream=stream)
+        """Projection and gated residual of `site` from gathered `rows`, one C call.
+        There is no variant without rows: a site with no looked-up rows is a caller
+        error."""
+        engram_gated_residual(self.layout, rows, self.site_wkv[site], streams, self.v, keep=keep, T=T,
+                              stream=stream)
         return streams
 
     def forward(self, tokens, cu_seqlens, streams, *, seq_start=None, slots=None, store=None,
@@ -287,15 +267,11 @@ class Engram:
             self.hash(next_tokens, next_cu_seqlens, seq_start=next_seq_start, slots=next_slots,
                       store=next_store, dead=next_dead, stream=stream)
         for s in range(self.num_sites):
-            kind = self.project(s, self.site_rows[s], T, stream=stream)
+            self.project(s, self.site_rows[s], T, stream=stream)
             if T_next is not None:
                 engram_gather_dequant(self.layout, self.site_tables[s], self.site_scales[s],
                                       self.row_ids, self.site_rows[s], site=s, T=T_next, stream=stream)
-            if kind == "splitk":
-                engram_gate_add_partials(self.layout, self.partials, self.proj_splits, per_site[s],
-                                         keep=keep, v=self.v, T=T, stream=stream)
-            else:
-                engram_gate_add(self.layout, self.v, per_site[s], keep=keep, T=T, stream=stream)
+            self.gate(s, per_site[s], T, keep=keep, stream=stream)
         self.pending_T = T_next
         return streams
 

@@ -8,8 +8,12 @@
  *   2. engram_gather_dequant  row ids -> e4m3fn (or bf16) table rows from HBM ->
  *                             row-wise dequantised bf16 (or fp32) rows;
  *   3. engram_gated_residual  rows -> wkv down-projection (MFMA) -> per-stream
- *                             sigmoid gate -> residual add into the hc streams.
- *                             engram_project + engram_gate_add are its two halves.
+ *                             sigmoid gate -> residual add into the hc streams,
+ *                             from a weight handle (engram_wkv_create) that picks
+ *                             the projection kernel per call; engram_wkv_project +
+ *                             engram_wkv_gate_add are its two halves, and
+ *                             engram_project* / engram_gate_add* the single
+ *                             kernels it dispatches to.
  *   engram_gather_project     steps 2 and the projection in one kernel for
  *                             e4m3fn tables (rows stay on chip).
  *   engram_project_splitk +   the projection split over K for few tokens
@@ -33,10 +37,12 @@
  *  - Device pointers ("d_" prefix) are caller-owned device memory on the
  *    current HIP device; the library never frees or keeps them.  Host pointers
  *    have no prefix.  Sizes are element counts unless the name says bytes.
- *  - Hot calls (compress_hash, gather_dequant, gather_project, project,
- *    project_splitk, gate_add, gate_add_partials, gated_residual, store_*)
- *    allocate nothing, never synchronise, and only enqueue kernels on `stream`;
- *    none records a memset, so a caller may capture them in a HIP graph.
+ *  - Hot calls (compress_hash, gather_dequant, gather_project, project*,
+ *    gate_add*, gated_residual, wkv_project, wkv_gate_add, store_reset / write /
+ *    read / rollback) allocate nothing, never synchronise, and only enqueue
+ *    kernels on `stream`; none records a memset, so a caller may capture them in
+ *    a HIP graph.  Set-up calls (*_create, tid2eid_check) may allocate and
+ *    synchronise.
  *  - Faults that only the device can see (a token id outside the vocabulary,
  *    a row id outside its table, a bad slot, malformed cu_seqlens, a continuing
  *    sequence without a store) latch the first such status in a per-device
@@ -68,6 +74,7 @@ extern "C" {
 #define ENGRAM_E_HIP (-11)         /* a HIP runtime call failed                             */
 #define ENGRAM_E_NOFIT (-12)       /* no bucket floor fits the requested table rows         */
 #define ENGRAM_E_UNSUPPORTED (-13) /* a valid but unimplemented shape (e.g. hc_mult != 4)   */
+#define ENGRAM_E_ID_RANGE (-14)    /* device: a compressed id written to the store is outside [0, V_c) */
 
 /* ---- element types ------------------------------------------------------ */
 typedef enum engram_dtype {
@@ -176,23 +183,47 @@ int engram_tid2eid_check(const engram_layout* layout, const int32_t* d_tid2eid,
                          int32_t* pad_eid, hipStream_t stream);
 
 /* ---- rolling store ------------------------------------------------------ */
-/* The store is caller-owned device memory int32 [num_slots][3]: per slot the
- * last three window ids of its sequence, oldest first ([VeOmni#1370] n-gram
- * incremental decode cache commit: the whole cache is a fixed-width tail of
- * max_ngram_size - 1 ids; [vLLM-V41] DeepseekV4Model.__init__: compressed ids
- * are kept per KV-cache slot so chunked prefill and decode can look back).  A slot
- * holding pad ids behaves exactly like a sequence start. */
+/* The store keeps, per slot, the last three window ids of its sequence, oldest
+ * first ([VeOmni#1370] n-gram incremental decode cache commit: the whole cache
+ * is a fixed-width tail of max_ngram_size - 1 ids, which leaves no way to
+ * express a history that is missing while the position is past the start;
+ * [vLLM-V41] DeepseekV4Model.__init__: compressed ids are kept per KV-cache
+ * slot so chunked prefill and decode can look back).  A slot holding pad ids
+ * behaves exactly like a sequence start.
+ *
+ * The handle owns device memory int32 [num_slots][3] on the device that was
+ * current at creation, bound to the layout it was made for (its compressed
+ * vocabulary and pad id): every id it holds lies in [0, V_c).  Calls that use
+ * it must run on that device. */
+typedef struct engram_store engram_store; /* opaque */
 
-/* d_slots[n] (NULL = all slots, n ignored) <- (pad, pad, pad). */
-int engram_store_reset(const engram_layout* layout, int32_t* d_store, int32_t num_slots,
-                       const int32_t* d_slots, int32_t n, int32_t pad_eid, hipStream_t stream);
-/* store[d_slots[i]] <- d_ids[i][0..2] for i < n. */
-int engram_store_write(const engram_layout* layout, int32_t* d_store, int32_t num_slots,
-                       const int32_t* d_slots, int32_t n, const int32_t* d_ids,
+/* Set-up call (allocates; not a hot call): a store of num_slots >= 1 slots, every
+ * slot (pad_eid, pad_eid, pad_eid), the fill enqueued on `stream`.  pad_eid is
+ * tid2eid[pad_token_id] as engram_tid2eid_check returns it, in [0, V_c).
+ * Errors: ENGRAM_E_ARG, ENGRAM_E_HIP (allocation).  On success *out owns the
+ * memory; engram_store_destroy frees it (the caller first makes sure no work
+ * that uses the store is still pending). */
+int engram_store_create(const engram_layout* layout, int32_t pad_eid, int32_t num_slots,
+                        hipStream_t stream, engram_store** out);
+void engram_store_destroy(engram_store* store);
+/* Slot count and pad id of a store. */
+int engram_store_query(const engram_store* store, int32_t* num_slots, int32_t* pad_eid);
+
+/* Hot calls on the store (enqueue one kernel on `stream`, allocate nothing).
+ * d_slots: int32 [n] slot indices, or NULL for every slot in order (n is then
+ * ignored); d_ids: int32 [n][3] (or [num_slots][3]).
+ *   reset: the slots <- (pad, pad, pad);
+ *   write: store[d_slots[i]] <- d_ids[i][0..2]; a row holding an id outside
+ *          [0, V_c) is not written and latches ENGRAM_E_ID_RANGE;
+ *   read:  d_ids[i][0..2] <- store[d_slots[i]] (a snapshot before a
+ *          speculative call, or a check).
+ * Host errors: ENGRAM_E_ARG.  Device errors: ENGRAM_E_SLOT_RANGE (that slot is
+ * skipped), ENGRAM_E_ID_RANGE. */
+int engram_store_reset(engram_store* store, const int32_t* d_slots, int32_t n, hipStream_t stream);
+int engram_store_write(engram_store* store, const int32_t* d_slots, int32_t n, const int32_t* d_ids,
                        hipStream_t stream);
-/* d_ids[i][0..2] <- store[d_slots[i]] for i < n. */
-int engram_store_read(const engram_layout* layout, const int32_t* d_store, int32_t num_slots,
-                      const int32_t* d_slots, int32_t n, int32_t* d_ids, hipStream_t stream);
+int engram_store_read(const engram_store* store, const int32_t* d_slots, int32_t n, int32_t* d_ids,
+                      hipStream_t stream);
 
 /* Speculative rollback.  After an engram_compress_hash call that updated the
  * store for S sequences (a verify pass over draft tokens), sets each slot
@@ -208,13 +239,12 @@ int engram_store_read(const engram_layout* layout, const int32_t* d_store, int32
  * snapshot: state that only grows is rolled back by length, bounded state is
  * copied.  The tail is bounded, so its snapshot is the 3-id copy and rolling
  * back to a length replays at most the last three kept ids onto it.)
- * Host errors: ENGRAM_E_ARG.  Device errors: ENGRAM_E_SLOT_RANGE,
- * ENGRAM_E_SEQLENS (keep_len outside [0, length] or malformed cu_seqlens; that
- * slot is left unchanged). */
-int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid, int32_t* d_store,
-                          int32_t num_slots, const int32_t* d_slots, int32_t S,
-                          const int32_t* d_cu_seqlens, int32_t T, const int32_t* d_eids,
-                          const uint8_t* d_dead, const uint8_t* d_seq_start,
+ * Host errors: ENGRAM_E_ARG (also a store made for another layout).  Device
+ * errors: ENGRAM_E_SLOT_RANGE, ENGRAM_E_SEQLENS (keep_len outside [0, length]
+ * or malformed cu_seqlens; that slot is left unchanged). */
+int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid, engram_store* store,
+                          const int32_t* d_slots, int32_t S, const int32_t* d_cu_seqlens, int32_t T,
+                          const int32_t* d_eids, const uint8_t* d_dead, const uint8_t* d_seq_start,
                           const int32_t* d_snapshot, const int32_t* d_keep_len, hipStream_t stream);
 
 /* ---- 1. compress + hash -------------------------------------------------- */
@@ -226,9 +256,8 @@ int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid,
  *           (reads PAD from there on) at a dead position or before a sequence
  *           that starts here ([VeOmni#1370] n-gram memory lookup commit: no
  *           n-gram crosses an image span or reaches before the first
- *           position); a
- *           dead token's own window is all PAD; positions before a continuing
- *           sequence are read from its store slot;
+ *           position); a dead token's own window is all PAD; positions before
+ *           a continuing sequence are read from its store slot;
  *   key_n = sum_{j<n} w_j * V_c^j (exact in 64 bits), n = 2, 3, 4;
  *   row_ids[t][site][n-2][h] = offsets[site][n][h] + key_n mod primes[site][n][h]
  *           for every site of the layout in the same pass ([NeMo-V41]
@@ -244,17 +273,18 @@ int engram_store_rollback(const engram_layout* layout, const int32_t* d_tid2eid,
  *   d_seq_start uint8 [S] or NULL (= every sequence starts here)
  *   d_slots     int32 [S] or NULL; -1 = no slot.  Slots of one call must be
  *               distinct (two sequences updating one slot race).
- *   d_store     int32 [num_slots][3] or NULL
+ *   store       a store made for this layout (engram_store_create), or NULL
  *   d_dead      uint8 [T] or NULL (= no dead position)
  *   d_eids      int32 [T] out: e_t
  *   d_row_ids   int32 [T][num_sites][3][H] out
- * Host errors: ENGRAM_E_ARG.  Device errors: ENGRAM_E_TOKEN_RANGE,
- * ENGRAM_E_SEQLENS, ENGRAM_E_SLOT_RANGE, ENGRAM_E_NEED_STORE. */
+ * Host errors: ENGRAM_E_ARG (also a store made for another layout).  Device
+ * errors: ENGRAM_E_TOKEN_RANGE, ENGRAM_E_SEQLENS, ENGRAM_E_SLOT_RANGE,
+ * ENGRAM_E_NEED_STORE. */
 int engram_compress_hash(const engram_layout* layout, const int32_t* d_tid2eid,
                          const int32_t* d_tokens, int32_t T, const int32_t* d_cu_seqlens,
                          int32_t S, const uint8_t* d_seq_start, const int32_t* d_slots,
-                         int32_t* d_store, int32_t num_slots, const uint8_t* d_dead,
-                         int32_t* d_eids, int32_t* d_row_ids, hipStream_t stream);
+                         engram_store* store, const uint8_t* d_dead, int32_t* d_eids,
+                         int32_t* d_row_ids, hipStream_t stream);
 
 /* ---- 2. gather + dequant -------------------------------------------------- */
 /* For each token t, order n, head h, element d < D of site `site`:
@@ -378,14 +408,86 @@ int engram_gate_add_partials(const engram_layout* layout, const float* d_partial
                              int32_t hidden, int32_t hc_mult, const uint8_t* d_keep,
                              void* d_streams, float* d_v, int32_t T, hipStream_t stream);
 
-/* engram_project followed by engram_gate_add on the same stream; d_v is the
- * caller's fp32 [T][hidden] workspace.  There is no variant without rows: a
- * site that has Engram and no looked-up rows is a caller error, never a skip
- * ([VeOmni#1370] decode-stack commit: a missing n-gram embedding raises). */
+/* ---- 3'. the projection weight of a site, and the gated residual ------------ */
+/* A site's wkv weight bound once, at set-up, to the layout and to the largest call
+ * it will serve ([VeOmni#1370] config commit: the Engram connection is wkv plus a
+ * gate reading the mHC residual stream).  The handle decides, per call, which
+ * projection kernel runs (engram_projection_plan), and owns what that needs:
+ *   - the weight packed in fragment order (engram_pack_weight), when some call of
+ *     up to max_tokens tokens reaches the packed kernel;
+ *   - the split-K workspace float [splits][T][hidden], when some call takes the
+ *     split-K form.
+ * d_w (bf16 [hidden][w_ld], as for engram_project) stays caller-owned and must
+ * outlive the handle: calls that take the plain or split-K kernel read it. */
+typedef struct engram_wkv engram_wkv; /* opaque */
+
+/* Projection kernels a call can run. */
+typedef enum engram_proj_kernel {
+  ENGRAM_PROJ_PLAIN = 0,  /* engram_project: 256 x 256 or 128 x 128 tiles, both operands via LDS */
+  ENGRAM_PROJ_PACKED = 1, /* engram_project_packed: many tokens, weight in fragment order */
+  ENGRAM_PROJ_SPLITK = 2  /* engram_project_splitk + the slice sum in the gate: few tokens */
+} engram_proj_kernel;
+
+typedef struct engram_proj_plan {
+  int32_t kernel; /* engram_proj_kernel */
+  int32_t splits; /* split-K factor (1 unless kernel == ENGRAM_PROJ_SPLITK) */
+} engram_proj_plan;
+
+/* The kernel a T-token projection of a [hidden][k_pad] weight runs (host only,
+ * no HIP call):
+ *   PACKED when `packed` (a packed weight exists) and T * hidden >= 64 * 256 * 256
+ *     (enough 256 x 256 tiles to fill the chip);
+ *   else SPLITK with s splits when s > 1, where s = `splits` if given (> 0),
+ *     otherwise the largest of 2, 4, 8 such that the call's 128 x 128 tiles times s
+ *     stay within one workgroup per CU (256), each split keeps at least 4 k-steps
+ *     of 64, and k_pad is a multiple of 64 s (none: s = 1);
+ *   else PLAIN.
+ * Errors: ENGRAM_E_ARG. */
+int engram_projection_plan(const engram_layout* layout, int32_t hidden, int32_t T, int32_t packed,
+                           int32_t splits, engram_proj_plan* plan);
+
+/* Set-up call (allocates; packs on `stream`): the handle for calls of up to
+ * max_tokens tokens.  splits: 0 = chosen per call as engram_projection_plan says,
+ * s >= 1 = every call below the packed size takes s splits (1: never split).
+ * Errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN (as engram_project; k_pad not a multiple
+ * of 64 s for a forced s), ENGRAM_E_HIP (allocation). */
+int engram_wkv_create(const engram_layout* layout, const void* d_w, int64_t w_ld, int32_t hidden,
+                      int32_t max_tokens, int32_t splits, hipStream_t stream, engram_wkv** out);
+void engram_wkv_destroy(engram_wkv* wkv);
+/* The plan a T-token call of this handle follows (T <= max_tokens). */
+int engram_wkv_plan(const engram_wkv* wkv, int32_t T, engram_proj_plan* plan);
+
+/* Step 3 of the path: v = W rows^T by the planned kernel, then for each token and
+ * stream the gated add of engram_gate_add, in place, on one stream:
+ *   z = <x[t][s][:], v[t][:]> / sqrt(hidden),  g = keep_t * sigmoid(z),
+ *   x[t][s][:] <- bf16(x[t][s][:] + g * v[t][:]).
+ * d_rows bf16 [T][rows_ld] (rows_ld >= k_pad, multiple of 8, 16-byte aligned),
+ * d_keep uint8 [T] or NULL, d_streams bf16 [T][hc_mult][hidden] in/out, d_v
+ * float [T][hidden] (caller-owned workspace; receives v), T <= max_tokens.
+ * Every planned kernel sums the same products of each k-step of 16 in the same
+ * order within its slice, so v is the fp32 accumulation the plain kernel makes,
+ * except that split-K sums s slices (each in that order), deterministically.
+ * Calls sharing one handle must not overlap (the split-K workspace is the
+ * handle's).  There is no variant without rows: a site that has Engram and no
+ * looked-up rows is a caller error, never a skip ([VeOmni#1370] decode-stack
+ * commit: a missing n-gram embedding raises).
+ * Host errors: ENGRAM_E_ARG (also T > max_tokens, or a handle made for another
+ * layout), ENGRAM_E_ALIGN, ENGRAM_E_UNSUPPORTED (hc_mult != 4, hidden > 8192). */
 int engram_gated_residual(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
-                          const void* d_w, int64_t w_ld, int32_t hidden, int32_t hc_mult,
-                          const uint8_t* d_keep, void* d_streams, float* d_v, int32_t T,
-                          hipStream_t stream);
+                          const engram_wkv* wkv, int32_t hc_mult, const uint8_t* d_keep,
+                          void* d_streams, float* d_v, int32_t T, hipStream_t stream);
+
+/* The two halves of engram_gated_residual, for callers that put other work
+ * between them (the next call's gather, for example): engram_wkv_project runs
+ * the planned projection (for split-K it leaves the slices in the handle's
+ * workspace and d_v is written by the second half); engram_wkv_gate_add runs the
+ * gated add (summing the slices into d_v first for split-K).  Same T, d_v and
+ * handle in both; nothing else may use the handle in between. */
+int engram_wkv_project(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
+                       const engram_wkv* wkv, float* d_v, int32_t T, hipStream_t stream);
+int engram_wkv_gate_add(const engram_layout* layout, const engram_wkv* wkv, float* d_v,
+                        int32_t hc_mult, const uint8_t* d_keep, void* d_streams, int32_t T,
+                        hipStream_t stream);
 
 /* ---- errors ------------------------------------------------------------- */
 const char* engram_strerror(int status);

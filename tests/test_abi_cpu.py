@@ -193,19 +193,58 @@ def test_store_rollback_host_errors_need_no_device():
     lib = eng._lib
     P = ctypes.c_void_p
     # empty call is a no-op
-    assert lib.engram_store_rollback(L.handle, None, None, 0, None, 0, None, 0, None, None, None,
+    assert lib.engram_store_rollback(L.handle, None, None, None, 0, None, 0, None, None, None,
                                      None, None, None) == 0
     # missing store / slots / keep_len
-    rc = lib.engram_store_rollback(L.handle, P(256), None, 4, P(256), 2, P(256), 4, P(256), None, None,
+    rc = lib.engram_store_rollback(L.handle, P(256), None, P(256), 2, P(256), 4, P(256), None, None,
                                    None, P(256), None)
     assert rc == eng.ENGRAM_E_ARG
-    rc = lib.engram_store_rollback(L.handle, P(256), P(256), 4, P(256), 2, P(256), 4, P(256), None, None,
+    rc = lib.engram_store_rollback(L.handle, P(256), P(256), None, 2, P(256), 4, P(256), None, None,
+                                   None, P(256), None)
+    assert rc == eng.ENGRAM_E_ARG
+    rc = lib.engram_store_rollback(L.handle, P(256), P(256), P(256), 2, P(256), 4, P(256), None, None,
                                    None, None, None)
     assert rc == eng.ENGRAM_E_ARG
-    # continuing sequences (seq_start given) need the snapshot
-    rc = lib.engram_store_rollback(L.handle, P(256), P(256), 4, P(256), 2, P(256), 4, P(256), None,
-                                   P(256), None, P(256), None)
-    assert rc == eng.ENGRAM_E_ARG
+
+
+def test_store_and_wkv_handles_host_errors_need_no_device():
+    """The store and weight handles refuse bad arguments before touching a device:
+    a store needs a layout, at least one slot and a pad id inside [0, V_c); a weight
+    handle needs a weight with a leading dimension of at least k_pad (a multiple of
+    8), 16-byte alignment, a positive size, and a forced split count that divides
+    k_pad into steps of 64.  Calls with no handle are refused too."""
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg)
+    lib = eng._lib
+    P = ctypes.c_void_p
+    K = L.info.k_pad
+    out = P()
+    assert lib.engram_store_create(None, 0, 4, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert lib.engram_store_create(L.handle, 0, 0, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert lib.engram_store_create(L.handle, -1, 4, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert lib.engram_store_create(L.handle, cfg.vc, 4, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert lib.engram_store_create(L.handle, 0, 4, None, None) == eng.ENGRAM_E_ARG
+    for fn in (lib.engram_store_reset,):
+        assert fn(None, None, 0, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_store_write(None, None, 0, P(256), None) == eng.ENGRAM_E_ARG
+    assert lib.engram_store_read(None, None, 0, P(256), None) == eng.ENGRAM_E_ARG
+    n, pad = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.engram_store_query(None, ctypes.byref(n), ctypes.byref(pad)) == eng.ENGRAM_E_ARG
+    ok = P(256)
+    wc = lib.engram_wkv_create
+    assert wc(L.handle, None, K, cfg.hidden, 64, 0, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert wc(L.handle, ok, K, 0, 64, 0, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert wc(L.handle, ok, K, cfg.hidden, 0, 0, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert wc(L.handle, ok, K, cfg.hidden, 64, -1, None, ctypes.byref(out)) == eng.ENGRAM_E_ARG
+    assert wc(L.handle, ok, K - 8, cfg.hidden, 64, 0, None, ctypes.byref(out)) == eng.ENGRAM_E_ALIGN
+    assert wc(L.handle, P(264), K, cfg.hidden, 64, 0, None, ctypes.byref(out)) == eng.ENGRAM_E_ALIGN
+    # k_pad 768 = 64 x 12: 4 splits divide it, 5 do not
+    assert wc(L.handle, ok, K, cfg.hidden, 64, 5, None, ctypes.byref(out)) == eng.ENGRAM_E_ALIGN
+    plan = eng.engram_proj_plan()
+    assert lib.engram_wkv_plan(None, 4, ctypes.byref(plan)) == eng.ENGRAM_E_ARG
+    assert lib.engram_wkv_project(L.handle, ok, K, None, ok, 4, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_wkv_gate_add(L.handle, None, ok, 4, None, ok, 4, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_gated_residual(L.handle, ok, K, None, 4, None, ok, ok, 4, None) == eng.ENGRAM_E_ARG
 
 
 def test_projection_and_gate_host_errors_need_no_device():
@@ -240,11 +279,6 @@ def test_projection_and_gate_host_errors_need_no_device():
                                         None) == eng.ENGRAM_E_ALIGN
     assert lib.engram_gate_add(L.handle, P(260), cfg.hidden, 4, None, ok, 4, None) == eng.ENGRAM_E_ALIGN
     assert lib.engram_gate_add(L.handle, None, cfg.hidden, 4, None, ok, 4, None) == eng.ENGRAM_E_ARG
-    # the chained call checks the gate's shape before it launches the projection
-    assert lib.engram_gated_residual(L.handle, ok, K, ok, K, cfg.hidden, 3, None, ok, ok, 4,
-                                     None) == eng.ENGRAM_E_UNSUPPORTED
-    assert lib.engram_gated_residual(L.handle, ok, K, ok, K, cfg.hidden, 4, None, ok, P(260), 4,
-                                     None) == eng.ENGRAM_E_ALIGN
 
 
 def test_packed_projection_host_errors_need_no_device():
@@ -349,24 +383,41 @@ def test_bench_refuses_more_than_one_gpu():
     assert out.returncode == 2 and "one GPU" in out.stderr
 
 
-def test_projection_split_choice():
-    """The runtime's split-K choice for a call (host logic, no device): no split once
-    the 256 x 256 tiles have many tiles; for few tokens the largest of 2, 4, 8 that keeps
-    at most one workgroup of 128 x 128 tiles per CU, four k-stages per split and k_pad a
-    multiple of 64 x splits."""
-    from hashed_gram_memory_tid2eid_amd.runtime import BIG_PROJECTION, choose_proj_splits
-    assert BIG_PROJECTION == 64 * 256 * 256
-    # the full and prefill workloads: many tokens, no split
-    assert choose_proj_splits(65536, 4096, 19584) == 1
-    assert choose_proj_splits(16384, 4096, 3072) == 1
+def test_projection_plan():
+    """The library's choice of projection kernel for a call (engram_projection_plan,
+    host logic, no device): the packed kernel once a packed weight exists and the call
+    has 64 x 256 x 256 outputs or more; below that, split-K with the largest of 2, 4, 8
+    splits that keeps at most one workgroup of 128 x 128 tiles per CU, four k-steps of
+    64 per split and k_pad a multiple of 64 x splits; else the plain kernel."""
+    def lay(k_cols, D):
+        return eng.engram_layout_create(vocab_size=8, compressed_vocab=4, pad_token_id=7,
+                                        heads_per_order=k_cols // 3, rows=[100_000] * 3, row_dim=D,
+                                        table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN,
+                                        row_pitch_bytes=(D + 15) // 16 * 16)
+    full = lay(3, 6500)        # k_pad 19,584
+    pre = lay(6, 512)          # k_pad 3,072
+    tiny = lay(6, 128)         # k_pad 768
+    odd = lay(3, 100)          # k_pad 384 = 64 x 6: 2 splits divide it, 4 do not
+    plan = eng.engram_projection_plan
+    # many tokens: the packed kernel when a packed weight exists, else the plain one
+    assert plan(full, 4096, 65536, packed=True) == ("packed", 1)
+    assert plan(full, 4096, 65536, packed=False) == ("plain", 1)
+    assert plan(pre, 4096, 16384, packed=True) == ("packed", 1)
+    assert plan(pre, 4096, 1024, packed=True) == ("packed", 1)   # 1,024 x 4,096 = 64 x 256 x 256
     # decode: 256 tokens x 4,096 outputs = 64 tiles -> 4 splits (8 would need 512 CUs)
-    assert choose_proj_splits(256, 4096, 3072) == 4
-    # tiny: 512 x 256 = 8 tiles; 4 splits would leave 192 k per split (< 4 stages)
-    assert choose_proj_splits(512, 256, 768) == 2
-    # k_pad not a multiple of 64 x 2: no split
-    assert choose_proj_splits(64, 256, 320) == 1
-    # a single token: 32 tiles of 128 columns -> 8 splits when k_pad allows
-    assert choose_proj_splits(1, 4096, 4096) == 8
+    assert plan(pre, 4096, 256, packed=True) == ("splitk", 4)
+    # tiny: 512 x 256 = 8 tiles; 4 splits would leave 192 k per split (< 4 steps)
+    assert plan(tiny, 256, 512, packed=False) == ("splitk", 2)
+    # k_pad 384: 2 splits leave 192 k (< 4 steps), so none
+    assert plan(odd, 256, 64, packed=False) == ("plain", 1)
+    # a single token: 32 tiles of 128 columns -> 8 splits when k_pad allows (3,072 =
+    # 64 x 48); 19,584 = 64 x 306 allows only 2
+    assert plan(pre, 4096, 1, packed=True) == ("splitk", 8)
+    assert plan(full, 4096, 1, packed=True) == ("splitk", 2)
+    # a forced split count applies below the packed size
+    assert plan(pre, 4096, 256, packed=True, splits=2) == ("splitk", 2)
+    assert plan(pre, 4096, 256, packed=True, splits=1) == ("plain", 1)
+    assert plan(pre, 4096, 16384, packed=True, splits=2) == ("packed", 1)
 
 
 def test_bench_traffic_is_keyed_to_the_kernel_source(tmp_path):

@@ -78,7 +78,7 @@ def test_speculative_rollback_matches_truncated_oracle(eng):
     nxt = ei.Batch(tokens=ei.zipf_tokens(rng, S), cu_seqlens=np.arange(S + 1, dtype=np.int32),
                    seq_start=np.zeros(S, np.uint8), slots=slots, dead=None)
 
-    store = _d(store0.copy())
+    store = site.site.make_store(num_slots, ids=_d(store0))
     e = torch.empty(512, dtype=torch.int32, device=DEV)
     r = torch.empty((512, 3, cfg.heads), dtype=torch.int32, device=DEV)
 
@@ -92,13 +92,13 @@ def test_speculative_rollback_matches_truncated_oracle(eng):
     run(prompt)
     slots_d = _d(slots)
     snap = torch.empty((S, 3), dtype=torch.int32, device=DEV)
-    eng.engram_store_read(L, store, slots_d, snap)
+    eng.engram_store_read(store, slots_d, snap)
     dbv = run(verify)
     eng.engram_store_rollback(L, site.tid2eid, store, slots_d, dbv["cu_seqlens"], e[:Tv], _d(keep),
                               snapshot=snap, seq_start=dbv["seq_start"], dead=dbv["dead"])
     torch.cuda.synchronize()
     assert eng.engram_get_error() == 0
-    got_store = store.cpu().numpy()
+    got_store = store.ids().cpu().numpy()
 
     ref = store0.copy()
     site.oracle_hash(prompt, ref)
@@ -108,16 +108,61 @@ def test_speculative_rollback_matches_truncated_oracle(eng):
     torch.cuda.synchronize()
     _, r_ref = site.oracle_hash(nxt, ref)
     assert np.array_equal(r[:S].cpu().numpy(), r_ref)
-    assert np.array_equal(store.cpu().numpy(), ref)
+    assert np.array_equal(store.ids().cpu().numpy(), ref)
     log(f"rollback: {S} sequences, keep {keep.tolist()}")
 
     # keep_len beyond the call's length: latched, that slot untouched
-    before = store.clone()
+    before = store.ids()
     bad = _d(np.full(S, draft + 2, np.int32))
     eng.engram_store_rollback(L, site.tid2eid, store, slots_d, dbv["cu_seqlens"], e[:Tv], bad,
                               snapshot=snap, seq_start=dbv["seq_start"], dead=dbv["dead"])
     assert eng.engram_get_error() == eng.ENGRAM_E_SEQLENS
-    assert torch.equal(store, before)
+    assert torch.equal(store.ids(), before)
+    _free()
+
+
+def test_store_handle_checks_ids_and_layout(eng):
+    """The store is bound to its layout: writes of ids outside [0, V_c) are refused
+    on the device (row untouched, ENGRAM_E_ID_RANGE latched), slots outside the
+    store latch ENGRAM_E_SLOT_RANGE, reset returns slots to the pad id, and a
+    layout with another compressed vocabulary cannot use it (ENGRAM_E_ARG)."""
+    cfg = ei.get_config("tiny")
+    site = Site(cfg, max_tokens=64)
+    pad = site.pad_eid
+    st = site.site.make_store(8)
+    assert np.array_equal(st.ids().cpu().numpy(), np.full((8, 3), pad, np.int32))
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, cfg.vc, size=(8, 3)).astype(np.int32)
+    st.load(_d(ids))
+    torch.cuda.synchronize()
+    assert eng.engram_get_error() == 0
+    assert np.array_equal(st.ids().cpu().numpy(), ids)
+    bad = np.array([[1, 2, 3], [4, cfg.vc, 5], [-1, 0, 0]], np.int32)
+    eng.engram_store_write(st, _d(np.array([0, 1, 2], np.int32)), _d(bad))
+    assert eng.engram_get_error() == eng.ENGRAM_E_ID_RANGE
+    want = ids.copy()
+    want[0] = [1, 2, 3]
+    assert np.array_equal(st.ids().cpu().numpy(), want)
+    eng.engram_store_write(st, _d(np.array([8], np.int32)), _d(np.zeros((1, 3), np.int32)))
+    assert eng.engram_get_error() == eng.ENGRAM_E_SLOT_RANGE
+    eng.engram_store_reset(st, _d(np.array([3, 5], np.int32)))
+    want[[3, 5]] = pad
+    assert np.array_equal(st.ids().cpu().numpy(), want)
+    assert eng.engram_get_error() == 0
+    # another layout (other compressed vocabulary): its calls refuse this store
+    other = eng.engram_layout_create(vocab_size=cfg.vocab, compressed_vocab=cfg.vc // 2,
+                                     pad_token_id=cfg.pad_token_id, heads_per_order=cfg.heads,
+                                     rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
+                                     table_dtype=eng.ENGRAM_DTYPE_FP8_E4M3FN,
+                                     row_pitch_bytes=cfg.row_pitch_bytes)
+    e = torch.empty(4, dtype=torch.int32, device=DEV)
+    r = torch.empty((4, 3, cfg.heads), dtype=torch.int32, device=DEV)
+    tok = _d(np.array([1, 2, 3, 4], np.int32))
+    with pytest.raises(eng.EngramError) as ex:
+        eng.engram_compress_hash(other, site.tid2eid, tok, _d(np.array([0, 4], np.int32)), e, r,
+                                 slots=_d(np.array([0], np.int32)), store=st,
+                                 seq_start=_d(np.zeros(1, np.uint8)))
+    assert ex.value.status == eng.ENGRAM_E_ARG
     _free()
 
 
@@ -131,15 +176,16 @@ def test_decode_step_graph_replays_equal_eager(eng):
     cu = _d(b0.cu_seqlens)
     ss = _d(b0.seq_start)
     sl = _d(b0.slots)
-    store_g = _d(ei.make_store_init(cfg))
-    store_e = store_g.clone()
+    init = _d(ei.make_store_init(cfg))
+    store_g = site.site.make_store(S, ids=init)
+    store_e = site.site.make_store(S, ids=init)
     streams_g = torch.zeros((S, cfg.hc_mult, cfg.hidden), dtype=torch.bfloat16, device=DEV)
 
     def step(streams, store):
         site.site.forward(tok, cu, streams, seq_start=ss, slots=sl, store=store)
 
     # warm up eagerly on a scratch store (kernel attributes are set on first use)
-    scratch = store_g.clone()
+    scratch = site.site.make_store(S, ids=init)
     step(streams_g.clone(), scratch)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -151,7 +197,7 @@ def test_decode_step_graph_replays_equal_eager(eng):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     # capture does not run the work: the graph's state is still the initial one
-    assert torch.equal(store_g, store_e)
+    assert torch.equal(store_g.ids(), store_e.ids())
     for k, b in enumerate(steps[1:]):
         tok.copy_(_d(b.tokens))
         x = ei.make_streams(cfg, S, DEV, step=k)
@@ -159,13 +205,13 @@ def test_decode_step_graph_replays_equal_eager(eng):
         g.replay()
         torch.cuda.synchronize()
         rows_g, v_g, y_g, st_g = (site.site.row_ids.clone(), site.site.v.clone(), streams_g.clone(),
-                                  store_g.clone())
+                                  store_g.ids())
         streams_e = x.clone()
         step(streams_e, store_e)
         torch.cuda.synchronize()
         assert eng.engram_get_error() == 0
         assert torch.equal(rows_g, site.site.row_ids), k
-        assert torch.equal(st_g, store_e), k
+        assert torch.equal(st_g, store_e.ids()), k
         assert torch.equal(v_g.view(torch.int32), site.site.v.view(torch.int32)), k
         assert np.array_equal(bf16_bits_np(y_g), bf16_bits_np(streams_e)), k
     log(f"graph: {len(steps) - 1} replays equal eager")

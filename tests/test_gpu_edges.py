@@ -57,7 +57,10 @@ def test_calls_without_tokens_leave_outputs_untouched(eng):
     eng.engram_project_splitk(L, rows, w, partials, 4, T=0)
     eng.engram_gate_add(L, v, streams, T=0)
     eng.engram_gate_add_partials(L, partials, 4, streams, T=0)
-    eng.engram_gated_residual(L, rows, w, streams, v, T=0)
+    wkv = eng.engram_wkv_create(L, w, 64)
+    eng.engram_gated_residual(L, rows, wkv, streams, v, T=0)
+    eng.engram_wkv_project(L, rows, wkv, v, T=0)
+    eng.engram_wkv_gate_add(L, wkv, v, streams, T=0)
     torch.cuda.synchronize()
     assert eng.engram_get_error() == 0
     for a, b in zip(before, (eids, rid, rows, v, partials, streams)):
@@ -83,7 +86,7 @@ def test_empty_sequences_update_the_store_like_the_oracle(eng):
         ei.Batch(tokens=ei.zipf_tokens(rng, 9), cu_seqlens=np.array([0, 0, 4, 4, 9, 9], np.int32),
                  seq_start=np.array([1, 0, 1, 0, 0], np.uint8), slots=np.array([0, 2, 3, 5, 8], np.int32)),
     ]
-    store = torch.from_numpy(store0.copy()).to(DEV)
+    store = site.site.make_store(num_slots, ids=torch.from_numpy(store0).to(DEV))
     ref = store0.copy()
     after = []
     for b in calls:
@@ -93,7 +96,7 @@ def test_empty_sequences_update_the_store_like_the_oracle(eng):
         torch.cuda.synchronize()
         assert eng.engram_get_error() == 0
         e_ref, r_ref = site.oracle_hash(b, ref)
-        assert np.array_equal(store.cpu().numpy(), ref)
+        assert np.array_equal(store.ids().cpu().numpy(), ref)
         if b.T:
             assert np.array_equal(e[:b.T].cpu().numpy(), e_ref)
             assert np.array_equal(r[:b.T].cpu().numpy(), r_ref)
@@ -183,7 +186,7 @@ def test_many_short_sequences_against_the_oracle(eng, S):
                      slots=rng.permutation(num_slots)[:S].astype(np.int32),
                      dead=ei.make_dead_spans(T, 11, n_spans=T // 50, max_len=3))
     store0 = rng.integers(0, cfg.vc, size=(num_slots, 3)).astype(np.int32)
-    store = torch.from_numpy(store0.copy()).to(DEV)
+    store = site.site.make_store(num_slots, ids=torch.from_numpy(store0).to(DEV))
     e = torch.empty(T, dtype=torch.int32, device=DEV)
     r = torch.empty((T, 3, cfg.heads), dtype=torch.int32, device=DEV)
     db = site.device_batch(batch)
@@ -195,6 +198,6 @@ def test_many_short_sequences_against_the_oracle(eng, S):
     e_ref, r_ref = site.oracle_hash(batch, ref)
     assert np.array_equal(e.cpu().numpy(), e_ref)
     assert np.array_equal(r.cpu().numpy(), r_ref)
-    assert np.array_equal(store.cpu().numpy(), ref)
+    assert np.array_equal(store.ids().cpu().numpy(), ref)
     log(f"{S} sequences, {T} tokens: ids, row ids and store equal the oracle")
     _free()

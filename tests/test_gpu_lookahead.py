@@ -159,16 +159,17 @@ def test_lookahead_decode_steps_with_store(eng):
                  for b in steps]
     store0 = torch.from_numpy(ei.make_store_init(cfg)).to(DEV)
     seq_site = _engram(eng, cfg, T, False)
-    store_seq = store0.clone()
+    store_seq = seq_site.make_store(cfg.n_seqs, ids=store0)
     seq_out = [ei.make_streams(cfg, T, DEV, step=k) for k in range(len(steps))]
     for c, x in zip(dev_steps, seq_out):
         seq_site.forward(c["tokens"], c["cu"], x, seq_start=c["ss"], slots=c["sl"], store=store_seq)
     torch.cuda.synchronize()
     kind = seq_site.projection_kind(0, T)
-    del seq_site
+    ids_seq = store_seq.ids()
+    del seq_site, store_seq
     _free()
     la_site = _engram(eng, cfg, T, True)
-    store_la = store0.clone()
+    store_la = la_site.make_store(cfg.n_seqs, ids=store0)
     la_out = [ei.make_streams(cfg, T, DEV, step=k) for k in range(len(steps))]
     c0 = dev_steps[0]
     la_site.gather_ahead(c0["tokens"], c0["cu"], seq_start=c0["ss"], slots=c0["sl"], store=store_la)
@@ -183,7 +184,7 @@ def test_lookahead_decode_steps_with_store(eng):
     assert eng.engram_get_error() == 0
     for x, y in zip(seq_out, la_out):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
-    assert torch.equal(store_seq, store_la)
+    assert torch.equal(ids_seq, store_la.ids())
     assert kind == "splitk"
     log(f"look-ahead order, {len(steps)} decode steps with the store ({kind} projection): bit-identical")
     del la_site

@@ -132,8 +132,9 @@ def test_packed_projection_prefill_shape_and_row_stride(eng):
 
 
 def test_runtime_picks_packed_for_many_tokens(eng):
-    """The runtime packs the weight when its calls can be large and uses the packed
-    kernel exactly for calls of at least 64 x 256 x 256 outputs."""
+    """The library's weight handle (behind the runtime) packs the weight when its
+    calls can be large and plans the packed kernel exactly for calls of at least
+    64 x 256 x 256 outputs."""
     import engram_inputs as ei
     cfg = ei.get_config("tiny")
     tid2eid = torch.from_numpy(ei.make_tid2eid(cfg.vocab, cfg.vc)).to(DEV)
@@ -145,11 +146,9 @@ def test_runtime_picks_packed_for_many_tokens(eng):
               tables=tables.data, scales=tables.scale, weight=weight, hidden=cfg.hidden)
     T_small = cfg.n_seqs * cfg.seq_len
     small = eng.Engram(max_tokens=T_small, **kw)
-    assert small.site_packed == [None]
-    assert small.projection_kind(0, T_small) in ("plain", "splitk")
+    assert all(small.projection_kind(0, t) in ("plain", "splitk") for t in (1, T_small // 2, T_small))
     big_T = 64 * 256 * 256 // cfg.hidden  # 16,384 tokens at hidden 256
     big = eng.Engram(max_tokens=big_T, **kw)
-    assert big.site_packed[0] is not None
     assert big.projection_kind(0, big_T) == "packed"
     assert big.projection_kind(0, big_T - 1) != "packed"
     # the same rows through both kinds
@@ -164,37 +163,67 @@ def test_runtime_picks_packed_for_many_tokens(eng):
     _free()
 
 
-def test_gated_residual_equals_its_halves_and_the_packed_pair(eng):
-    """engram_gated_residual (projection + gate in one call) leaves the same streams as
-    engram_project then engram_gate_add, and as engram_project_packed then
-    engram_gate_add, bit for bit (rows with a keep mask, prefill-like shape)."""
-    L = _layout(eng, 6, 512)
+@pytest.mark.parametrize("shape", ["prefill", "decode", "between", "full"])
+def test_gated_residual_runs_the_planned_kernel(eng, shape):
+    """engram_gated_residual, called straight through ctypes with a weight handle,
+    leaves the v and streams of the single kernel its plan names, bit for bit:
+    the packed projection at the prefill shape (16,384 x 3,072 -> 4,096) and the
+    full shape (65,536 x 19,584 -> 4,096), split-K at the decode shape (256 tokens),
+    the plain kernel in between (3,000 x 3,072 -> 1,024); then engram_gate_add (or
+    the slice sum) with a keep mask."""
+    import ctypes
+    M, cols, D, N, kind = {"prefill": (16384, 6, 512, 4096, "packed"),
+                           "decode": (256, 6, 512, 4096, "splitk"),
+                           "between": (3000, 6, 512, 1024, "plain"),
+                           "full": (65536, 3, 6500, 4096, "packed")}[shape]
+    L = _layout(eng, cols, D)
     K = L.info.k_pad
-    M, N = 3000, 1024
     A, B = _operands(L, M, N, seed=5)
     g = torch.Generator(device=DEV)
     g.manual_seed(6)
     x0 = torch.randn((M, 4, N), generator=g, device=DEV).to(torch.bfloat16)
     keep = (torch.rand(M, generator=g, device=DEV) > 0.1).to(torch.uint8)
-    packed = torch.empty(eng.engram_packed_weight_bytes(L, N), dtype=torch.uint8, device=DEV)
-    eng.engram_pack_weight(L, B, packed)
-    v = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    wkv = eng.engram_wkv_create(L, B, M)
+    plan = wkv.plan(M)
+    assert plan[0] == kind, plan
+    v1 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
     x1 = x0.clone()
-    eng.engram_gated_residual(L, A, B, x1, v, keep=keep)
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = eng._lib.engram_gated_residual(L.handle, ctypes.c_void_p(A.data_ptr()), K, wkv.handle, 4,
+                                        ctypes.c_void_p(keep.data_ptr()), ctypes.c_void_p(x1.data_ptr()),
+                                        ctypes.c_void_p(v1.data_ptr()), M, ctypes.c_void_p(stream))
+    assert rc == 0
+    v2 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     x2 = x0.clone()
-    eng.engram_project(L, A, B, v)
-    eng.engram_gate_add(L, v, x2, keep=keep)
-    x3 = x0.clone()
-    eng.engram_project_packed(L, A, packed, N, v)
-    eng.engram_gate_add(L, v, x3, keep=keep)
+    if kind == "packed":
+        packed = torch.empty(eng.engram_packed_weight_bytes(L, N), dtype=torch.uint8, device=DEV)
+        eng.engram_pack_weight(L, B, packed)
+        eng.engram_project_packed(L, A, packed, N, v2)
+        eng.engram_gate_add(L, v2, x2, keep=keep)
+    elif kind == "splitk":
+        parts = torch.empty(plan[1] * M * N, dtype=torch.float32, device=DEV)
+        eng.engram_project_splitk(L, A, B, parts, plan[1])
+        eng.engram_gate_add_partials(L, parts, plan[1], x2, keep=keep, v=v2)
+    else:
+        eng.engram_project(L, A, B, v2)
+        eng.engram_gate_add(L, v2, x2, keep=keep)
     torch.cuda.synchronize()
     assert eng.engram_get_error() == 0
+    assert torch.equal(v1.view(torch.int32), v2.view(torch.int32))
     assert torch.equal(x1.view(torch.int16), x2.view(torch.int16))
-    assert torch.equal(x1.view(torch.int16), x3.view(torch.int16))
     dropped = keep == 0
     assert torch.equal(x1[dropped].view(torch.int16), x0[dropped].view(torch.int16))
     assert not torch.equal(x1[~dropped].view(torch.int16), x0[~dropped].view(torch.int16))
-    del A, B, packed, v, x0, x1, x2, x3
+    # the two halves give the same again
+    v3 = torch.empty_like(v1)
+    x3 = x0.clone()
+    eng.engram_wkv_project(L, A, wkv, v3)
+    eng.engram_wkv_gate_add(L, wkv, v3, x3, keep=keep)
+    torch.cuda.synchronize()
+    assert torch.equal(v1.view(torch.int32), v3.view(torch.int32))
+    assert torch.equal(x1.view(torch.int16), x3.view(torch.int16))
+    log(f"gated_residual {shape}: {kind} plan {plan}, bit-identical to the single kernels")
+    del A, B, v1, v2, v3, x0, x1, x2, x3, wkv
     _free()
 
 

@@ -191,7 +191,7 @@ def test_tiny_ragged_store_and_dead(eng):
     site = Site(cfg, max_tokens=T)
     num_slots = 12
     store0 = np.random.default_rng(6).integers(0, cfg.vc, size=(num_slots, 3)).astype(np.int32)
-    store_d = torch.from_numpy(store0.copy()).to(DEV)
+    store_d = site.site.make_store(num_slots, ids=torch.from_numpy(store0).to(DEV))
     db = site.device_batch(batch)
     streams = ei.make_streams(cfg, T, DEV, step=3)
     x0 = bf16_bits_np(streams)
@@ -203,7 +203,7 @@ def test_tiny_ragged_store_and_dead(eng):
     e_ref, r_ref = site.oracle_hash(batch, store_ref)
     assert np.array_equal(site.site.eids[:T].cpu().numpy(), e_ref)
     assert np.array_equal(site.site.row_ids[:T].cpu().numpy(), r_ref)
-    assert np.array_equal(store_d.cpu().numpy(), store_ref)
+    assert np.array_equal(store_d.ids().cpu().numpy(), store_ref)
     b16_ref = _check_rows(site, r_ref, T, site.site.rows)
     E = b16_ref.reshape(T, -1)
     v_ref = oracle.project(E, site.weight_bits())
@@ -234,8 +234,9 @@ def test_decode_equals_prefill_at_five_splits(eng):
     eng.engram_compress_hash(L, site.tid2eid, db["tokens"], db["cu_seqlens"], eids, rows, dead=db["dead"])
     torch.cuda.synchronize()
     assert np.array_equal(rows.cpu().numpy(), r_ref)
+    others = torch.tensor([[1, 2, 3], [4, 5, 6], [0, 0, 0], [7, 8, 9]], dtype=torch.int32, device=DEV)
     for split in (0, 1, 3, 13, 40):
-        store = torch.full((4, 3), -1, dtype=torch.int32, device=DEV)
+        store = site.site.make_store(4, ids=others)
         slots = torch.tensor([2], dtype=torch.int32, device=DEV)
         got_e, got_r = [], []
         pieces = [(0, split, 1)] + [(t, t + 1, 0) for t in range(split, T)]
@@ -255,14 +256,15 @@ def test_decode_equals_prefill_at_five_splits(eng):
         _no_device_error(eng, f"split {split}")
         assert np.array_equal(np.concatenate(got_e), e_ref), split
         assert np.array_equal(np.concatenate(got_r), r_ref), split
-        assert (store[[0, 1, 3]].cpu().numpy() == -1).all()
+        # only slot 2 was used; the other slots keep their ids
+        assert torch.equal(store.ids()[[0, 1, 3]], others[[0, 1, 3]])
 
 
 def _decode_run(eng, name, steps, full_every, sample_n):
     cfg = ei.get_config(name)
     site = Site(cfg, max_tokens=cfg.n_seqs)
     store0 = ei.make_store_init(cfg)
-    store_d = torch.from_numpy(store0.copy()).to(DEV)
+    store_d = site.site.make_store(cfg.n_seqs, ids=torch.from_numpy(store0).to(DEV))
     store_ref = store0.copy()
     W = site.weight_bits()
     for k, batch in enumerate(ei.make_decode_steps(cfg, steps)):
@@ -276,7 +278,7 @@ def _decode_run(eng, name, steps, full_every, sample_n):
         e_ref, r_ref = site.oracle_hash(batch, store_ref)
         assert np.array_equal(site.site.eids[:batch.T].cpu().numpy(), e_ref), k
         assert np.array_equal(site.site.row_ids[:batch.T].cpu().numpy(), r_ref), k
-        assert np.array_equal(store_d.cpu().numpy(), store_ref), k
+        assert np.array_equal(store_d.ids().cpu().numpy(), store_ref), k
         if k % full_every == 0 or k == steps - 1:
             idx = (np.sort(np.random.default_rng(k).choice(batch.T, sample_n, replace=False))
                    if sample_n else np.arange(batch.T))
@@ -462,7 +464,7 @@ def test_device_errors_are_reported(eng):
     ss0 = torch.zeros(1, dtype=torch.uint8, device=DEV)
     eng.engram_compress_hash(L, site.tid2eid, tok, cu, e, r, seq_start=ss0)
     assert eng.engram_get_error() == eng.ENGRAM_E_NEED_STORE
-    store = torch.zeros((4, 3), dtype=torch.int32, device=DEV)
+    store = site.site.make_store(4)
     eng.engram_compress_hash(L, site.tid2eid, tok, cu, e, r, seq_start=ss0,
                              slots=torch.tensor([4], dtype=torch.int32, device=DEV), store=store)
     assert eng.engram_get_error() == eng.ENGRAM_E_SLOT_RANGE
