@@ -165,6 +165,7 @@ def _cpu_baseline_pinned(cfg, batch, site_tables, weights, streams_host_bits, bu
     order = rng.permutation(batch.T)
     H, D = cfg.heads, cfg.row_dim
     bf16 = cfg.table_dtype == "bf16"
+    per_site = cfg.table_split == "site"
     done, t_rest = 0, 0.0
     chunk = 4
     while done < batch.T and t_rest + t_hash_all * done / batch.T < budget_s:

@@ -485,3 +485,26 @@ def test_loaded_library_is_built_from_the_tree():
     assert eng.engram_build_id() == bl["BUILD_ID_PREFIX"] + sha
     assert bl["built_hash"](eng.LIB_PATH) == sha
     assert bl["built_hash"](os.path.join(ROOT, "README.md")) is None
+
+
+def test_bench_cpu_baseline_leg_runs_pinned_on_host_tensors():
+    """bench.py's oracle leg on CPU copies of small workloads (one site and the
+    two-site released structure): it reports a positive rate on one core with the
+    host CPU model, and gives the calling thread its CPU mask back afterwards."""
+    import importlib.util
+    import torch
+    spec = importlib.util.spec_from_file_location("bench_cpu_leg", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    mask = os.sched_getaffinity(0)
+    for name in ("tiny", "v41_small"):
+        cfg = ei.get_config(name)
+        batch = ei.make_batch(cfg)
+        tabs = [ei.make_tables(cfg, "cpu", site=s) for s in range(cfg.n_sites)]
+        ws = [ei.make_weight(cfg, "cpu", site=s) for s in range(cfg.n_sites)]
+        xs = [ei.make_streams(cfg, batch.T, "cpu", step=s).view(torch.int16).numpy().view(np.uint16)
+              for s in range(cfg.n_sites)]
+        r = bench.cpu_baseline(cfg, batch, tabs, ws, xs, 0.5)
+        assert r["value"] > 0 and r["cores"] == 1 and r["kind"] == "oracle"
+        assert r["cpu_model"] and "pinned to host core" in r["sample"]
+        assert os.sched_getaffinity(0) == mask

@@ -3,9 +3,17 @@
 Bars: compressed ids and row ids bit-exact; dequantised rows bit-exact in fp32
 and in bf16; projection within the fp32-accumulation bound; final bf16 streams
 within 2e-2 relative error (1e-3 absolute floor); keep = 0 streams bit for bit.
-Small workloads are compared on every output; the large ones on every integer
-output and on seeded token samples (always including the first three and the
-last token of each sequence), in the launch configuration the benchmark uses.
+
+Coverage (the oracle runs on host-thread token shards, see engram_harness):
+  tiny, prefill (with and without image spans), decode (both shapes, all 64 steps):
+      every output of every token;
+  long prefill: integers and fp32 / bf16 rows on every token, v and streams on a
+      seeded 4,096-token sample;
+  full FP8 and full BF16: integers on every token, rows, v and streams on a seeded
+      1,024-token sample.
+Samples always include the first three and the last token of each sequence.  The
+large workloads run in the launch configuration the benchmark uses, and the fused
+and look-ahead paths are compared with the oracle on the same tokens.
 """
 import gc
 
@@ -16,7 +24,7 @@ import torch
 import engram_inputs as ei
 import oracle
 from engram_harness import (DEV, Site, assert_streams_close, assert_v_close, bf16_bits_np,
-                            bits_to_f64, log, sample_tokens)
+                            bits_to_f64, log, oracle_gate_add, oracle_project, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,9 +125,9 @@ def test_tiny_end_to_end(eng):
     b16_ref = _check_rows(site, r_ref, T, site.site.rows, out32)
     E = b16_ref.reshape(T, -1)
     W = site.weight_bits()
-    v_ref = oracle.project(E, W)
+    v_ref = oracle_project(E, W)
     assert_v_close(site.site.v[:T].cpu().numpy(), v_ref, E, W, "tiny v")
-    y_ref, _ = oracle.gate_add(x0, v_ref)
+    y_ref, _ = oracle_gate_add(x0, v_ref)
     worst = assert_streams_close(bf16_bits_np(streams), y_ref, "tiny streams")
     log(f"tiny: worst stream rel err {worst:.2e}")
 
@@ -206,9 +214,9 @@ def test_tiny_ragged_store_and_dead(eng):
     assert np.array_equal(store_d.ids().cpu().numpy(), store_ref)
     b16_ref = _check_rows(site, r_ref, T, site.site.rows)
     E = b16_ref.reshape(T, -1)
-    v_ref = oracle.project(E, site.weight_bits())
+    v_ref = oracle_project(E, site.weight_bits())
     keep = (batch.dead == 0).astype(np.uint8)
-    y_ref, _ = oracle.gate_add(x0, v_ref, keep)
+    y_ref, _ = oracle_gate_add(x0, v_ref, keep)
     y = bf16_bits_np(streams)
     assert np.array_equal(y[keep == 0], x0[keep == 0]), "dead tokens' streams changed"
     assert_streams_close(y, y_ref, "ragged streams")
@@ -260,8 +268,9 @@ def test_decode_equals_prefill_at_five_splits(eng):
         assert torch.equal(store.ids()[[0, 1, 3]], others[[0, 1, 3]])
 
 
-def _decode_run(eng, name, steps, full_every, sample_n):
+def _decode_run(eng, name, steps):
     cfg = ei.get_config(name)
+    worst = 0.0
     site = Site(cfg, max_tokens=cfg.n_seqs)
     store0 = ei.make_store_init(cfg)
     store_d = site.site.make_store(cfg.n_seqs, ids=torch.from_numpy(store0).to(DEV))
@@ -279,23 +288,23 @@ def _decode_run(eng, name, steps, full_every, sample_n):
         assert np.array_equal(site.site.eids[:batch.T].cpu().numpy(), e_ref), k
         assert np.array_equal(site.site.row_ids[:batch.T].cpu().numpy(), r_ref), k
         assert np.array_equal(store_d.ids().cpu().numpy(), store_ref), k
-        if k % full_every == 0 or k == steps - 1:
-            idx = (np.sort(np.random.default_rng(k).choice(batch.T, sample_n, replace=False))
-                   if sample_n else np.arange(batch.T))
-            b16 = _check_rows(site, r_ref, batch.T, site.site.rows)
-            E = b16.reshape(batch.T, -1)[idx]
-            v_ref = oracle.project(E, W)
-            y_ref, _ = oracle.gate_add(x0[idx], v_ref)
-            assert_streams_close(bf16_bits_np(streams)[idx], y_ref, f"{name} step {k}")
-    log(f"{name}: {steps} steps ok")
+        # every token of every step: rows exact, v within the fp32 bound, streams
+        b16 = _check_rows(site, r_ref, batch.T, site.site.rows)
+        E = b16.reshape(batch.T, -1)
+        v_ref = oracle_project(E, W)
+        assert_v_close(site.site.v[:batch.T].cpu().numpy(), v_ref, E, W, f"{name} step {k} v")
+        y_ref, _ = oracle_gate_add(x0, v_ref)
+        worst = max(worst, assert_streams_close(bf16_bits_np(streams), y_ref, f"{name} step {k}"))
+    log(f"{name}: {steps} steps x {cfg.n_seqs} tokens, every output checked against the oracle "
+        f"(worst stream rel err {worst:.2e}; projection {site.site.projection_plan(0, cfg.n_seqs)})")
 
 
 def test_decode_tiny_64_steps(eng):
-    _decode_run(eng, "decode_tiny", 64, full_every=8, sample_n=0)
+    _decode_run(eng, "decode_tiny", 64)
 
 
 def test_decode_prefill_shapes_64_steps(eng):
-    _decode_run(eng, "decode", 64, full_every=32, sample_n=24)
+    _decode_run(eng, "decode", 64)
     _free()
 
 
@@ -312,7 +321,8 @@ def _large_run(eng, name, f32_sample, stream_sample, tables=None):
     streams = ei.make_streams(cfg, T, DEV)
     log(f"{name}: forward over {T} tokens, {batch.S} sequences")
     idx = sample_tokens(batch, stream_sample, seed=cfg.seed)
-    x0 = bf16_bits_np(streams[torch.from_numpy(idx).to(DEV)])
+    idx_d = torch.from_numpy(idx).to(DEV)
+    x0 = bf16_bits_np(streams[idx_d])
     site.site.forward(db["tokens"], db["cu_seqlens"], streams, seq_start=db["seq_start"])
     torch.cuda.synchronize()
     _no_device_error(eng, f"{name} forward")
@@ -334,15 +344,20 @@ def _large_run(eng, name, f32_sample, stream_sample, tables=None):
     assert np.array_equal(g16[:, :, :D], b16_ref)
     assert not g16[:, :, D:].any()
     log(f"{name}: fp32 / bf16 rows exact on {len(fidx)} sampled tokens")
-    _, b16_s = site.oracle_dequant(r_ref[idx])
+    if np.array_equal(idx, fidx):
+        b16_s = b16_ref
+    else:
+        _, b16_s = site.oracle_dequant(r_ref[idx])
     E = b16_s.reshape(len(idx), -1)
+    del b16_ref, f32_ref, g32, g16
     W = site.weight_bits()
-    v_ref = oracle.project(E, W)
-    assert_v_close(site.site.v[torch.from_numpy(idx).to(DEV)].cpu().numpy(), v_ref, E, W, f"{name} v")
-    y_ref, _ = oracle.gate_add(x0, v_ref)
-    worst = assert_streams_close(bf16_bits_np(streams[torch.from_numpy(idx).to(DEV)]), y_ref,
-                                 f"{name} streams")
-    log(f"{name}: streams within tolerance on {len(idx)} sampled tokens (worst {worst:.2e})")
+    v_ref = oracle_project(E, W)
+    v_rel = assert_v_close(site.site.v[idx_d].cpu().numpy(), v_ref, E, W, f"{name} v")
+    y_ref, _ = oracle_gate_add(x0, v_ref)
+    worst = assert_streams_close(bf16_bits_np(streams[idx_d]), y_ref, f"{name} streams")
+    log(f"{name}: v and streams against the oracle on {len(idx)} of {T} tokens "
+        f"(v within the fp32 bound, worst rel {v_rel:.1e}; streams worst {worst:.2e}; "
+        f"projection {site.site.projection_plan(0, T)})")
     if cfg.table_dtype == "fp8":
         # the fused gather + projection at the same size: v equal bit for bit on every token
         v_f = torch.empty((T, cfg.hidden), dtype=torch.float32, device=DEV)
@@ -351,7 +366,9 @@ def _large_run(eng, name, f32_sample, stream_sample, tables=None):
         torch.cuda.synchronize()
         _no_device_error(eng, f"{name} fused")
         assert torch.equal(v_f.view(torch.int32), site.site.v[:T].view(torch.int32))
-        log(f"{name}: fused gather+projection equals the split path on all {T} tokens")
+        assert_v_close(v_f[idx_d].cpu().numpy(), v_ref, E, W, f"{name} fused v")
+        log(f"{name}: fused gather+projection equals the split path on all {T} tokens, and the "
+            f"oracle on {len(idx)}")
         del v_f
         # the look-ahead order the benchmark times (next call's hash, projection, next
         # call's gather, gate), on the same tables: streams equal the sequential pass above
@@ -371,6 +388,7 @@ def _large_run(eng, name, f32_sample, stream_sample, tables=None):
             torch.cuda.synchronize()
             _no_device_error(eng, f"{name} look-ahead")
             assert torch.equal(x.view(torch.int16), streams.view(torch.int16))
+            assert_streams_close(bf16_bits_np(x[idx_d]), y_ref, f"{name} look-ahead streams")
             del x
         log(f"{name}: look-ahead order equals the sequential pass on all {T} tokens "
             f"({la.projection_kind(0, T)} projection)")
@@ -379,15 +397,16 @@ def _large_run(eng, name, f32_sample, stream_sample, tables=None):
 
 
 def test_prefill_parity(eng):
-    _large_run(eng, "prefill", f32_sample=4096, stream_sample=96)
+    _large_run(eng, "prefill", f32_sample=None, stream_sample=None)
     _free()
 
 
 def test_prefill_with_image_spans(eng):
     """The prefill workload with image spans (runs of dead positions, up to 64 long):
     compressed ids and row ids exact on every token, the streams of dead tokens
-    untouched bit for bit, and sampled streams (including the three positions after
-    each span, whose lookback the span blocks) within tolerance of the oracle."""
+    untouched bit for bit, and the rows, v and streams of every token (including
+    the three positions after each span, whose lookback the span blocks) against
+    the oracle."""
     cfg = ei.get_config("prefill")
     b0 = ei.make_batch(cfg)
     T = b0.T
@@ -409,34 +428,34 @@ def test_prefill_with_image_spans(eng):
     keep = (dead == 0).astype(np.uint8)
     assert np.array_equal(y[keep == 0], x_all[keep == 0]), "a dead token's streams changed"
     after = [p for p in range(1, T) if dead[p - 1] and not dead[p]]
-    near = {p + j for p in after for j in range(3) if p + j < T}
-    idx = np.array(sorted(set(sample_tokens(batch, 96, seed=cfg.seed).tolist()) | near), dtype=np.int64)
-    _, b16 = site.oracle_dequant(r_ref[idx])
-    E = b16.reshape(len(idx), -1)
+    _check_rows(site, r_ref, T, site.site.rows)
+    _, b16 = site.oracle_dequant(r_ref)
+    E = b16.reshape(T, -1)
     W = site.weight_bits()
-    v_ref = oracle.project(E, W)
-    y_ref, _ = oracle.gate_add(x_all[idx], v_ref, keep=keep[idx])
-    worst = assert_streams_close(y[idx], y_ref, "prefill with image spans")
+    v_ref = oracle_project(E, W)
+    assert_v_close(site.site.v[:T].cpu().numpy(), v_ref, E, W, "prefill with image spans v")
+    y_ref, _ = oracle_gate_add(x_all, v_ref, keep=keep)
+    worst = assert_streams_close(y, y_ref, "prefill with image spans")
     log(f"prefill with {int(dead.sum())} dead positions in {len(after)} spans: ids exact, dead streams "
-        f"untouched, {len(idx)} sampled streams within tolerance (worst {worst:.2e})")
+        f"untouched, rows, v and streams of all {T} tokens against the oracle (worst {worst:.2e})")
     del site
     _free()
 
 
 def test_long_prefill_parity(eng):
-    _large_run(eng, "long", f32_sample=4096, stream_sample=96)
+    _large_run(eng, "long", f32_sample=None, stream_sample=4096)
     _free()
 
 
 @pytest.mark.timeout(900)
 def test_full_scale_fp8_parity(eng):
-    _large_run(eng, "full", f32_sample=1024, stream_sample=24)
+    _large_run(eng, "full", f32_sample=1024, stream_sample=1024)
     _free()
 
 
 @pytest.mark.timeout(900)
 def test_full_scale_bf16_parity(eng):
-    _large_run(eng, "full_bf16", f32_sample=1024, stream_sample=24)
+    _large_run(eng, "full_bf16", f32_sample=1024, stream_sample=1024)
     _free()
 
 
