@@ -133,6 +133,7 @@ _sig("engram_wkv_plan", [_P, _i32, _P])
 _sig("engram_wkv_project", [_P, _P, _i64, _P, _P, _i32, _P])
 _sig("engram_wkv_gate_add", [_P, _P, _P, _i32, _P, _P, _i32, _P])
 _sig("engram_gated_residual", [_P, _P, _i64, _P, _i32, _P, _P, _P, _i32, _P])
+_sig("engram_gated_residual_noalloc", [_P, _P, _i64, _P, _i32, _P, _P, _i32, _P])
 _sig("engram_strerror", [ctypes.c_int], ctypes.c_char_p)
 _sig("engram_host_device_pointer", [_P, ctypes.POINTER(_P)])
 _sig("engram_get_error", [_P])
@@ -641,6 +642,23 @@ def engram_gated_residual(layout: Layout, rows, wkv: Wkv, streams, v, *, keep=No
         layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1], wkv.handle, streams.shape[1],
         _dev(keep, torch.uint8, "keep"), _dev(streams, torch.bfloat16, "streams"),
         _dev(v, torch.float32, "v"), T, _stream(stream)), "engram_gated_residual")
+
+
+def engram_gated_residual_noalloc(layout: Layout, rows, wkv: Wkv, streams, *, keep=None,
+                                  T: Optional[int] = None, stream=None):
+    """engram_gated_residual with its scratch in the library's per-GPU array (no
+    allocation; v is not returned)."""
+    import torch
+    if T is None:
+        T = streams.shape[0]
+    _need(rows.dim() == 2 and rows.shape[0] >= T, "rows too small")
+    _need(streams.dim() == 3 and streams.shape[0] >= T and streams.shape[2] == wkv.hidden,
+          "streams must be [T][hc][hidden]")
+    _need(keep is None or keep.numel() >= T, "keep too small")
+    _check(_lib.engram_gated_residual_noalloc(
+        layout.handle, _dev(rows, torch.bfloat16, "rows"), rows.shape[1], wkv.handle, streams.shape[1],
+        _dev(keep, torch.uint8, "keep"), _dev(streams, torch.bfloat16, "streams"), T, _stream(stream)),
+        "engram_gated_residual_noalloc")
 
 
 def engram_wkv_project(layout: Layout, rows, wkv: Wkv, v, *, T: Optional[int] = None, stream=None):

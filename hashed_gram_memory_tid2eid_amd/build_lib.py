@@ -34,7 +34,7 @@ COMMON = [
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["engram_device.hip", "abi.cpp", "layout.cpp"]
+SOURCES = ["engram_device.hip", "abi.cpp", "layout.cpp", "noalloc.cpp"]
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_ID_PREFIX = "engram-src-sha256:"
 

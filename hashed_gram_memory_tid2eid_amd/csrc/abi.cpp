@@ -630,38 +630,67 @@ extern "C" int engram_wkv_plan(const engram_wkv* W, int32_t T, engram_proj_plan*
   return ENGRAM_OK;
 }
 
-extern "C" int engram_wkv_project(const engram_layout* L, const void* d_rows, int64_t rows_ld,
-                                  const engram_wkv* W, float* d_v, int32_t T, hipStream_t stream) {
-  int rc = wkv_usable(W, L, T);
-  if (rc != ENGRAM_OK) return rc;
+namespace engram {
+
+int wkv_check(const engram_wkv* W, const engram_layout* L, int32_t T) { return wkv_usable(W, L, T); }
+
+engram_proj_plan wkv_plan_for(const engram_wkv* W, int32_t T) {
+  return plan_for(T, W->hidden, W->k_pad, W->packed != nullptr, W->forced_splits);
+}
+
+// The planned projection of a T-token call into d_v, or (split-K) into the slices
+// at d_partials ([splits][T][hidden]; capacity checked by the caller).
+int wkv_project_to(const engram_layout* L, const void* d_rows, int64_t rows_ld, const engram_wkv* W,
+                   float* d_v, float* d_partials, int32_t T, hipStream_t stream) {
   if (T == 0) return ENGRAM_OK;
   if (!d_v) return ENGRAM_E_ARG;
-  const engram_proj_plan p = plan_for(T, W->hidden, W->k_pad, W->packed != nullptr, W->forced_splits);
+  const engram_proj_plan p = wkv_plan_for(W, T);
   if (p.kernel == ENGRAM_PROJ_PACKED) {
-    rc = engram_project_packed(L, d_rows, rows_ld, W->packed, W->hidden, d_v, T, stream);
+    const int rc = engram_project_packed(L, d_rows, rows_ld, W->packed, W->hidden, d_v, T, stream);
     if (rc != ENGRAM_E_UNSUPPORTED) return rc;
     // rows too wide for the packed kernel's 32-bit tile offsets: the plain kernel
   } else if (p.kernel == ENGRAM_PROJ_SPLITK) {
-    if ((int64_t)p.splits * T * W->hidden > W->partial_elems) return ENGRAM_E_ARG;
-    return engram_project_splitk(L, d_rows, rows_ld, W->w, W->w_ld, W->hidden, W->partials,
+    return engram_project_splitk(L, d_rows, rows_ld, W->w, W->w_ld, W->hidden, d_partials,
                                  p.splits, T, stream);
   }
   return engram_project(L, d_rows, rows_ld, W->w, W->w_ld, W->hidden, d_v, T, stream);
 }
 
+// The gated add of a T-token call from d_v, or (split-K) from the slices at
+// d_partials, summed into d_v first.
+int wkv_gate_from(const engram_layout* L, const engram_wkv* W, float* d_v, const float* d_partials,
+                  int32_t hc_mult, const uint8_t* d_keep, void* d_streams, int32_t T,
+                  hipStream_t stream) {
+  const int rc = gate_shape(W->hidden, hc_mult);
+  if (rc != ENGRAM_OK) return rc;
+  if (T == 0) return ENGRAM_OK;
+  const engram_proj_plan p = wkv_plan_for(W, T);
+  if (p.kernel == ENGRAM_PROJ_SPLITK)
+    return engram_gate_add_partials(L, d_partials, p.splits, W->hidden, hc_mult, d_keep, d_streams,
+                                    d_v, T, stream);
+  return engram_gate_add(L, d_v, W->hidden, hc_mult, d_keep, d_streams, T, stream);
+}
+
+int hip_error_status(hipError_t e) { return hip_status(e); }
+
+}  // namespace engram
+
+extern "C" int engram_wkv_project(const engram_layout* L, const void* d_rows, int64_t rows_ld,
+                                  const engram_wkv* W, float* d_v, int32_t T, hipStream_t stream) {
+  const int rc = wkv_usable(W, L, T);
+  if (rc != ENGRAM_OK) return rc;
+  const engram_proj_plan p = engram::wkv_plan_for(W, T);
+  if (p.kernel == ENGRAM_PROJ_SPLITK && (int64_t)p.splits * T * W->hidden > W->partial_elems)
+    return ENGRAM_E_ARG;
+  return engram::wkv_project_to(L, d_rows, rows_ld, W, d_v, W->partials, T, stream);
+}
+
 extern "C" int engram_wkv_gate_add(const engram_layout* L, const engram_wkv* W, float* d_v,
                                    int32_t hc_mult, const uint8_t* d_keep, void* d_streams,
                                    int32_t T, hipStream_t stream) {
-  int rc = wkv_usable(W, L, T);
+  const int rc = wkv_usable(W, L, T);
   if (rc != ENGRAM_OK) return rc;
-  rc = gate_shape(W->hidden, hc_mult);
-  if (rc != ENGRAM_OK) return rc;
-  if (T == 0) return ENGRAM_OK;
-  const engram_proj_plan p = plan_for(T, W->hidden, W->k_pad, W->packed != nullptr, W->forced_splits);
-  if (p.kernel == ENGRAM_PROJ_SPLITK)
-    return engram_gate_add_partials(L, W->partials, p.splits, W->hidden, hc_mult, d_keep, d_streams,
-                                    d_v, T, stream);
-  return engram_gate_add(L, d_v, W->hidden, hc_mult, d_keep, d_streams, T, stream);
+  return engram::wkv_gate_from(L, W, d_v, W->partials, hc_mult, d_keep, d_streams, T, stream);
 }
 
 extern "C" int engram_gated_residual(const engram_layout* L, const void* d_rows, int64_t rows_ld,

@@ -191,4 +191,17 @@ struct GateArgs {
 };
 hipError_t launch_gate_add(const GateArgs& a, hipStream_t stream);
 
+// The wkv handle's dispatch (abi.cpp), shared by the entry points that bring their
+// own scratch: the argument check of a T-token call, its plan, the planned
+// projection into d_v or the split-K slices at d_partials, and the gated add from
+// them; and the status of a failed HIP call (recorded for engram_last_hip_error).
+int wkv_check(const engram_wkv* W, const engram_layout* L, int32_t T);
+engram_proj_plan wkv_plan_for(const engram_wkv* W, int32_t T);
+int wkv_project_to(const engram_layout* L, const void* d_rows, int64_t rows_ld, const engram_wkv* W,
+                   float* d_v, float* d_partials, int32_t T, hipStream_t stream);
+int wkv_gate_from(const engram_layout* L, const engram_wkv* W, float* d_v, const float* d_partials,
+                  int32_t hc_mult, const uint8_t* d_keep, void* d_streams, int32_t T,
+                  hipStream_t stream);
+int hip_error_status(hipError_t e);
+
 }  // namespace engram

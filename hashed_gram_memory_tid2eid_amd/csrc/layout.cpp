@@ -241,6 +241,7 @@ extern "C" const char* engram_strerror(int s) {
     case ENGRAM_E_NOFIT: return "no bucket floor fits the table rows";
     case ENGRAM_E_UNSUPPORTED: return "unsupported shape";
     case ENGRAM_E_ID_RANGE: return "compressed id written to the store outside [0, compressed_vocab)";
+    case ENGRAM_E_SCRATCH: return "call needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

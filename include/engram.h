@@ -75,6 +75,7 @@ extern "C" {
 #define ENGRAM_E_NOFIT (-12)       /* no bucket floor fits the requested table rows         */
 #define ENGRAM_E_UNSUPPORTED (-13) /* a valid but unimplemented shape (e.g. hc_mult != 4)   */
 #define ENGRAM_E_ID_RANGE (-14)    /* device: a compressed id written to the store is outside [0, V_c) */
+#define ENGRAM_E_SCRATCH (-15)     /* the call needs more scratch than engram_gated_residual_noalloc holds */
 
 /* ---- element types ------------------------------------------------------ */
 typedef enum engram_dtype {
@@ -488,6 +489,25 @@ int engram_wkv_project(const engram_layout* layout, const void* d_rows, int64_t 
 int engram_wkv_gate_add(const engram_layout* layout, const engram_wkv* wkv, float* d_v,
                         int32_t hc_mult, const uint8_t* d_keep, void* d_streams, int32_t T,
                         hipStream_t stream);
+
+/* ---- the gated residual without allocation --------------------------------- */
+/* For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same result as
+ * engram_gated_residual (the same planned kernels in the same order, so the
+ * streams are bit for bit the same), with its scratch -- v float [T][hidden],
+ * and for the split-K plan the slices float [splits][T][hidden] -- in a
+ * library-owned device array of ENGRAM_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the first call on that GPU until the process ends.  v is not returned.
+ * The call allocates nothing and never synchronises.  Calls on one GPU share its
+ * array: calls that overlap on one GPU (two streams, two threads) race, and must
+ * be ordered by the caller.  Nothing in the array needs clearing between calls.
+ * Errors: as engram_gated_residual, and ENGRAM_E_SCRATCH when
+ * round_up(T * hidden, 64) (+ splits * T * hidden for split-K) floats exceed the
+ * array (at hidden 4,096: up to 2,048 tokens, or 409 with 4 splits). */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES (32u << 20)
+int engram_gated_residual_noalloc(const engram_layout* layout, const void* d_rows, int64_t rows_ld,
+                                  const engram_wkv* wkv, int32_t hc_mult, const uint8_t* d_keep,
+                                  void* d_streams, int32_t T, hipStream_t stream);
 
 /* ---- errors ------------------------------------------------------------- */
 const char* engram_strerror(int status);

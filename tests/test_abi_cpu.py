@@ -245,6 +245,7 @@ def test_store_and_wkv_handles_host_errors_need_no_device():
     assert lib.engram_wkv_project(L.handle, ok, K, None, ok, 4, None) == eng.ENGRAM_E_ARG
     assert lib.engram_wkv_gate_add(L.handle, None, ok, 4, None, ok, 4, None) == eng.ENGRAM_E_ARG
     assert lib.engram_gated_residual(L.handle, ok, K, None, 4, None, ok, ok, 4, None) == eng.ENGRAM_E_ARG
+    assert lib.engram_gated_residual_noalloc(L.handle, ok, K, None, 4, None, ok, 4, None) == eng.ENGRAM_E_ARG
 
 
 def test_projection_and_gate_host_errors_need_no_device():
