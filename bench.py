@@ -241,6 +241,9 @@ def main():
     ap.add_argument("--no-alt-paths", action="store_true",
                     help="skip the fused-path comparison after the timed steps (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--compare-vendor", action="store_true",
+                    help="after the timed steps, time torch.mm (the vendor bf16 GEMM) on the "
+                         "projection's rows and weight")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
                          "(reference for the HBM byte counters of a profiler run)")
@@ -637,15 +640,70 @@ def main():
         torch.cuda.synchronize()
         eng.check_device_error("gather controls")
         u_ms, h_ms = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+
+        # one gather launch right after a given predecessor, with or without a 1 ms pause
+        # (host sleep after a synchronisation) in between: whether the in-step gather pays
+        # for the write-back of what the kernel before it wrote
+        def gather_after(pre, pause):
+            ts = []
+            for _ in range(reps):
+                pre()
+                if pause:
+                    torch.cuda.synchronize()
+                    time.sleep(0.001)
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record()
+                eng.engram_gather_dequant(L, site.site_tables[0], site.site_scales[0], site.row_ids,
+                                          site.rows, site=0, T=T)
+                a1.record()
+                torch.cuda.synchronize()
+                ts.append(a0.elapsed_time(a1))
+            ms = float(np.median(ts))
+            return {"ms": ms, "frac": gbs(gather_bytes, ms) / HBM_PEAK_GBS}
+
+        def gate0():
+            site.gate(0, site_streams[0], T)
+
+        def proj0():
+            site.project(0, site.rows, T)
+
+        def gather0():
+            eng.engram_gather_dequant(L, site.site_tables[0], site.site_scales[0], site.row_ids,
+                                      site.rows, site=0, T=T)
+        after = {"after_gather": gather_after(gather0, False),
+                 "after_gate": gather_after(gate0, False),
+                 "after_gate_then_1ms_pause": gather_after(gate0, True),
+                 "after_projection": gather_after(proj0, False),
+                 "after_projection_then_1ms_pause": gather_after(proj0, True)}
+        eng.check_device_error("gather after predecessors")
         result["gather_controls"] = {
             "unique_row_frac": unique,
             "uniform_rows": {"ms": u_ms, "GB/s": gbs(gather_bytes, u_ms),
                              "frac": gbs(gather_bytes, u_ms) / HBM_PEAK_GBS},
             "hashed_rows_back_to_back": {"ms": h_ms, "GB/s": gbs(gather_bytes, h_ms),
                                          "frac": gbs(gather_bytes, h_ms) / HBM_PEAK_GBS},
+            "single_launch_median": after,
             "reps": reps,
         }
         del rid_u
+    if args.compare_vendor and args.path == "split" and not cfg.decode_steps:
+        # the vendor library's bf16 GEMM (torch.mm, bf16 output) on the same rows and weight,
+        # outside the timed region: a reference point for the projection, not the product
+        wt = site.site_weights[0].t().contiguous()
+        out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
+        torch.mm(site.rows[:T], wt, out=out)
+        reps = max(3, min(args.steps, 10))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(reps):
+            torch.mm(site.rows[:T], wt, out=out)
+        e[1].record()
+        torch.cuda.synchronize()
+        v_ms = e[0].elapsed_time(e[1]) / reps
+        result["vendor_gemm"] = {"ms": v_ms, "TFLOP/s": proj_flops / (v_ms * 1e-3) / 1e12,
+                                 "frac": proj_flops / (v_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                 "reps": reps, "what": "torch.mm of the same bf16 rows and weight"}
+        del wt, out
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

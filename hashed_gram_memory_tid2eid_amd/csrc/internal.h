@@ -72,6 +72,7 @@ struct HashArgs {
   uint32_t prime[ENGRAM_MAX_COLUMNS];
   uint32_t offset[ENGRAM_MAX_COLUMNS];
   uint64_t barrett[ENGRAM_MAX_COLUMNS];
+  int32_t store_in_kernel;  // set by the launcher: slots inside one workgroup updated in the hash kernel
 };
 hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream);
 

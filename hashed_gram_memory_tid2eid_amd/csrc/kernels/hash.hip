@@ -41,9 +41,23 @@ __device__ __forceinline__ uint32_t packed_eid(const HashArgs& a, int q, uint32_
   return (uint32_t)a.tid2eid[tok] & kIdMask;
 }
 
-// Largest s in [0, S) with cu[s] <= t (cu[0] = 0 <= t).
-__device__ __forceinline__ int find_sequence(const int32_t* cu, int S, int t) {
+// Largest s in [0, S) with cu[s] <= t (cu[0] = 0 <= t < T = cu[S]).  The first probe
+// is the sequence an even split of the T tokens over the S sequences puts t in: exact
+// for decode steps (one token per sequence) and equal-length batches, where the
+// search is one pair of independent loads instead of a chain of log2(S); otherwise
+// it narrows a binary search.  The result stays in [0, S) even for malformed
+// cu_seqlens (which the kernel latches).
+__device__ __forceinline__ int find_sequence(const int32_t* cu, int S, int T, int t) {
   int lo = 0, hi = S - 1;
+  int g = (int)((int64_t)t * S / (T > 0 ? T : 1));
+  g = g < S - 1 ? g : S - 1;
+  const int cg = cu[g], cg1 = cu[g + 1];
+  if (cg <= t) {
+    if (cg1 > t) return g;
+    lo = g + 1 < S - 1 ? g + 1 : S - 1;
+  } else {
+    hi = g - 1 > 0 ? g - 1 : 0;
+  }
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (cu[mid] <= t)
@@ -54,33 +68,27 @@ __device__ __forceinline__ int find_sequence(const int32_t* cu, int S, int t) {
   return lo;
 }
 
-__global__ __launch_bounds__(256) void compress_hash_kernel(HashArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const bool valid = t < a.T;
-  const uint32_t pad = (uint32_t)a.tid2eid[a.pad_token_id] & kIdMask;
-
-  // cu_seqlens must be 0 = c0 <= c1 <= ... <= cS = T.
-  if (t < a.S && a.cu_seqlens[t] > a.cu_seqlens[t + 1]) latch_error(ENGRAM_E_SEQLENS);
-  if (t == 0 && (a.cu_seqlens[0] != 0 || a.cu_seqlens[a.S] != a.T)) latch_error(ENGRAM_E_SEQLENS);
-
-  const uint32_t own = valid ? packed_eid(a, t, pad, true) : 0u;
-  uint32_t halo = 0u;
-  if (lane < 3) {
-    const int q = (t - lane) - 3 + lane;  // the three positions before the wave
-    if (q >= 0 && q < a.T) halo = packed_eid(a, q, pad, false);
+// The workgroup of 256 tokens that updates sequence s's store slot inside the hash
+// kernel: the one holding both its first and its last position (an empty sequence:
+// its start, or the call's last token when it starts at T).  -1 when the sequence
+// spans two workgroups or its bounds are malformed; store_update_kernel then does it.
+__device__ __forceinline__ int store_owner(int b0, int b1, int T) {
+  if (b0 < 0 || b1 < b0 || b1 > T) return -1;
+  int lo, hi;
+  if (b1 > b0) {
+    lo = b0;
+    hi = b1 - 1;
+  } else {
+    lo = b0 < T ? b0 : (T > 0 ? T - 1 : 0);
+    hi = lo;
   }
-  // prev[j] = packed id of position t - j (all lanes take part in the shuffles)
-  uint32_t prev[4];
-#pragma unroll
-  for (int j = 1; j <= 3; ++j) {
-    const uint32_t from_wave = __shfl_up(own, (unsigned)j, 64);
-    const uint32_t from_halo = __shfl(halo, (lane - j + 3) & 63, 64);
-    prev[j] = lane >= j ? from_wave : from_halo;
-  }
-  if (!valid) return;
+  return (lo >> 8) == (hi >> 8) ? (lo >> 8) : -1;
+}
 
-  const int s = find_sequence(a.cu_seqlens, a.S, t);
+// One lane's token t: window with lookback blocking, keys, row ids of every site.
+__device__ __forceinline__ void hash_lane(const HashArgs& a, int t, uint32_t own,
+                                          const uint32_t prev[4], uint32_t pad) {
+  const int s = find_sequence(a.cu_seqlens, a.S, a.T, t);
   int start = a.cu_seqlens[s];
   if (start > t) {  // only when cu_seqlens[0] > 0, already latched above
     start = t;
@@ -170,20 +178,15 @@ __device__ __forceinline__ void tail_after(const int32_t* eids, const uint8_t* d
   out[2] = w[0];
 }
 
-// One thread per sequence: the slot keeps the last three window ids of its
-// sequence, oldest first.  Runs after compress_hash_kernel on the same stream,
-// so every read of the old slot content has happened.
-__global__ __launch_bounds__(256) void store_update_kernel(HashArgs a) {
-  const int s = blockIdx.x * 256 + threadIdx.x;
-  if (s >= a.S) return;
+// Sequence s (well-formed bounds b0 <= b1 in its call) leaves its last three
+// window ids, oldest first, in its slot.
+__device__ void update_slot(const HashArgs& a, int s, int b0, int b1) {
   const int slot = a.slots[s];
   if (slot < 0) return;
   if (slot >= a.num_slots) {
     latch_error(ENGRAM_E_SLOT_RANGE);
     return;
   }
-  const int b0 = a.cu_seqlens[s], b1 = a.cu_seqlens[s + 1];
-  if (b0 < 0 || b1 > a.T || b1 < b0) return;  // malformed: latched by the hash kernel
   const int32_t pad = a.tid2eid[a.pad_token_id];
   const bool starts = a.seq_start == nullptr || a.seq_start[s] != 0;
   int32_t* st = a.store + 3 * slot;
@@ -192,6 +195,70 @@ __global__ __launch_bounds__(256) void store_update_kernel(HashArgs a) {
   st[0] = w[0];
   st[1] = w[1];
   st[2] = w[2];
+}
+
+__global__ __launch_bounds__(256) void compress_hash_kernel(HashArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < a.T;
+  const uint32_t pad = (uint32_t)a.tid2eid[a.pad_token_id] & kIdMask;
+
+  // cu_seqlens must be 0 = c0 <= c1 <= ... <= cS = T.
+  if (t < a.S && a.cu_seqlens[t] > a.cu_seqlens[t + 1]) latch_error(ENGRAM_E_SEQLENS);
+  if (t == 0 && (a.cu_seqlens[0] != 0 || a.cu_seqlens[a.S] != a.T)) latch_error(ENGRAM_E_SEQLENS);
+
+  const uint32_t own = valid ? packed_eid(a, t, pad, true) : 0u;
+  uint32_t halo = 0u;
+  if (lane < 3) {
+    const int q = (t - lane) - 3 + lane;  // the three positions before the wave
+    if (q >= 0 && q < a.T) halo = packed_eid(a, q, pad, false);
+  }
+  // prev[j] = packed id of position t - j (all lanes take part in the shuffles)
+  uint32_t prev[4];
+#pragma unroll
+  for (int j = 1; j <= 3; ++j) {
+    const uint32_t from_wave = __shfl_up(own, (unsigned)j, 64);
+    const uint32_t from_halo = __shfl(halo, (lane - j + 3) & 63, 64);
+    prev[j] = lane >= j ? from_wave : from_halo;
+  }
+  if (valid) hash_lane(a, t, own, prev, pad);
+  if (!a.store_in_kernel) return;
+
+  // store update of the sequences that lie in this workgroup: every read of their
+  // old slot content (by their first three positions, all in this workgroup) and
+  // every compressed id they wrote happen before the barrier
+  __syncthreads();
+  const int w0 = blockIdx.x * 256;
+  if (w0 > 0 && w0 >= a.T) return;  // no token here (workgroup 0 owns the sequences of T = 0)
+  int first = 0;  // smallest s with cu[s] >= w0
+  if (w0 > 0) {
+    int lo = 0, hi = a.S;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_seqlens[mid] >= w0)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    first = lo;
+  }
+  for (int sq = first + (int)threadIdx.x; sq < a.S; sq += 256) {
+    const int b0 = a.cu_seqlens[sq], b1 = a.cu_seqlens[sq + 1];
+    if (b0 > w0 + 256) break;  // later sequences start in later workgroups
+    if (store_owner(b0, b1, a.T) == (int)blockIdx.x) update_slot(a, sq, b0, b1);
+  }
+}
+
+// One thread per sequence, for the slots the hash kernel did not update (sequences
+// that span two of its workgroups).  Runs after compress_hash_kernel on the same
+// stream, so every read of the old slot content has happened.
+__global__ __launch_bounds__(256) void store_update_kernel(HashArgs a) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= a.S) return;
+  const int b0 = a.cu_seqlens[s], b1 = a.cu_seqlens[s + 1];
+  if (b0 < 0 || b1 > a.T || b1 < b0) return;  // malformed: latched by the hash kernel
+  if (a.store_in_kernel && store_owner(b0, b1, a.T) >= 0) return;  // done in the hash kernel
+  update_slot(a, s, b0, b1);
 }
 
 // Speculative rollback: each slot is set to the tail it would hold had the last
@@ -232,14 +299,19 @@ hipError_t launch_store_rollback(const RollbackArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream) {
+hipError_t launch_compress_hash(const HashArgs& args, hipStream_t stream) {
   (void)hipGetLastError();  // drop a stale error another library left on this thread
+  HashArgs a = args;
+  a.store_in_kernel = (a.slots != nullptr && a.store != nullptr && a.S > 0) ? 1 : 0;
   const int work = a.T > a.S + 1 ? a.T : a.S + 1;
   const int blocks = (work + 255) / 256;
   hipLaunchKernelGGL(compress_hash_kernel, dim3(blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.slots != nullptr && a.store != nullptr && a.S > 0) {
+  // with at most 256 tokens one workgroup holds every position, so every sequence's
+  // slot was updated inside the hash kernel; otherwise the sequences that span two
+  // workgroups are left to a second kernel
+  if (a.store_in_kernel && a.T > 256) {
     hipLaunchKernelGGL(store_update_kernel, dim3((a.S + 255) / 256), dim3(256), 0, stream, a);
     e = hipGetLastError();
   }
