@@ -47,13 +47,16 @@ __device__ __forceinline__ uint32_t packed_eid(const HashArgs& a, int q, uint32_
 // search is one pair of independent loads instead of a chain of log2(S); otherwise
 // it narrows a binary search.  The result stays in [0, S) even for malformed
 // cu_seqlens (which the kernel latches).
-__device__ __forceinline__ int find_sequence(const int32_t* cu, int S, int T, int t) {
+__device__ __forceinline__ int find_sequence(const int32_t* cu, int S, int T, int t, int* next) {
   int lo = 0, hi = S - 1;
   int g = (int)((int64_t)t * S / (T > 0 ? T : 1));
   g = g < S - 1 ? g : S - 1;
   const int cg = cu[g], cg1 = cu[g + 1];
   if (cg <= t) {
-    if (cg1 > t) return g;
+    if (cg1 > t) {
+      *next = cg1;
+      return g;
+    }
     lo = g + 1 < S - 1 ? g + 1 : S - 1;
   } else {
     hi = g - 1 > 0 ? g - 1 : 0;
@@ -65,6 +68,7 @@ __device__ __forceinline__ int find_sequence(const int32_t* cu, int S, int T, in
     else
       hi = mid - 1;
   }
+  *next = cu[lo + 1];
   return lo;
 }
 
@@ -85,10 +89,36 @@ __device__ __forceinline__ int store_owner(int b0, int b1, int T) {
   return (lo >> 8) == (hi >> 8) ? (lo >> 8) : -1;
 }
 
+// An empty sequence q of the call leaves its slot as it was, or PAD when it starts
+// here.
+__device__ __forceinline__ void empty_slot(const HashArgs& a, int q, int32_t pad) {
+  const int slot = a.slots[q];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    latch_error(ENGRAM_E_SLOT_RANGE);
+    return;
+  }
+  if (a.seq_start == nullptr || a.seq_start[q] != 0) {
+    int32_t* st = a.store + 3 * slot;
+    st[0] = pad;
+    st[1] = pad;
+    st[2] = pad;
+  }
+}
+
 // One lane's token t: window with lookback blocking, keys, row ids of every site.
+// With the store updated in this kernel: the window of a sequence's last position
+// holds the sequence's new tail (its three newest ids, oldest first: w3 is dropped,
+// and a dead position's all-PAD window is the PAD tail); when the whole sequence
+// lies in this workgroup its last lane returns that slot in *pending and the ids in
+// tail[], to be written after the workgroup barrier.  The lane of a sequence's last
+// position also settles the empty sequences right after it, and lane 0 those before
+// the first position (an empty sequence's slot is read by no lane).
 __device__ __forceinline__ void hash_lane(const HashArgs& a, int t, uint32_t own,
-                                          const uint32_t prev[4], uint32_t pad) {
-  const int s = find_sequence(a.cu_seqlens, a.S, a.T, t);
+                                          const uint32_t prev[4], uint32_t pad, int* pending,
+                                          int32_t tail[3]) {
+  int b1 = 0;
+  const int s = find_sequence(a.cu_seqlens, a.S, a.T, t, &b1);
   int start = a.cu_seqlens[s];
   if (start > t) {  // only when cu_seqlens[0] > 0, already latched above
     start = t;
@@ -129,6 +159,17 @@ __device__ __forceinline__ void hash_lane(const HashArgs& a, int t, uint32_t own
   const uint64_t k3 = k2 + (uint64_t)w[2] * a.vc2;
   const uint64_t k4 = k3 + (uint64_t)w[3] * a.vc3;
   a.eids[t] = (int32_t)w[0];
+  if (a.store_in_kernel && t == b1 - 1) {
+    if (slot >= 0 && store_owner(start, b1, a.T) == (t >> 8)) {
+      *pending = slot;
+      tail[0] = (int32_t)w[2];
+      tail[1] = (int32_t)w[1];
+      tail[2] = (int32_t)w[0];
+    }
+    for (int q = s + 1; q < a.S && a.cu_seqlens[q + 1] == b1; ++q) empty_slot(a, q, (int32_t)pad);
+  }
+  if (a.store_in_kernel && t == 0)
+    for (int q = 0; q < s; ++q) empty_slot(a, q, (int32_t)pad);
   // every site from the same keys: [site][order][head]
   const int cols = 3 * a.heads;
   int32_t* out = a.row_ids + (int64_t)t * (cols * a.num_sites);
@@ -221,43 +262,33 @@ __global__ __launch_bounds__(256) void compress_hash_kernel(HashArgs a) {
     const uint32_t from_halo = __shfl(halo, (lane - j + 3) & 63, 64);
     prev[j] = lane >= j ? from_wave : from_halo;
   }
-  if (valid) hash_lane(a, t, own, prev, pad);
+  int pending = -1;
+  int32_t tail[3];
+  if (valid) hash_lane(a, t, own, prev, pad, &pending, tail);
   if (!a.store_in_kernel) return;
 
-  // store update of the sequences that lie in this workgroup: every read of their
-  // old slot content (by their first three positions, all in this workgroup) and
-  // every compressed id they wrote happen before the barrier
+  // the new tails of the sequences that lie in this workgroup: every read of their
+  // old slot content (by their first three positions, all in this workgroup) happens
+  // before the barrier
   __syncthreads();
-  const int w0 = blockIdx.x * 256;
-  if (w0 > 0 && w0 >= a.T) return;  // no token here (workgroup 0 owns the sequences of T = 0)
-  int first = 0;  // smallest s with cu[s] >= w0
-  if (w0 > 0) {
-    int lo = 0, hi = a.S;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_seqlens[mid] >= w0)
-        hi = mid;
-      else
-        lo = mid + 1;
-    }
-    first = lo;
-  }
-  for (int sq = first + (int)threadIdx.x; sq < a.S; sq += 256) {
-    const int b0 = a.cu_seqlens[sq], b1 = a.cu_seqlens[sq + 1];
-    if (b0 > w0 + 256) break;  // later sequences start in later workgroups
-    if (store_owner(b0, b1, a.T) == (int)blockIdx.x) update_slot(a, sq, b0, b1);
+  if (pending >= 0) {
+    int32_t* st = a.store + 3 * pending;
+    st[0] = tail[0];
+    st[1] = tail[1];
+    st[2] = tail[2];
   }
 }
 
-// One thread per sequence, for the slots the hash kernel did not update (sequences
-// that span two of its workgroups).  Runs after compress_hash_kernel on the same
-// stream, so every read of the old slot content has happened.
+// One thread per sequence, for the slots the hash kernel did not update: sequences
+// that span two of its workgroups (or every sequence of a call without tokens).
+// Runs after compress_hash_kernel on the same stream, so every read of the old slot
+// content has happened.
 __global__ __launch_bounds__(256) void store_update_kernel(HashArgs a) {
   const int s = blockIdx.x * 256 + threadIdx.x;
   if (s >= a.S) return;
   const int b0 = a.cu_seqlens[s], b1 = a.cu_seqlens[s + 1];
   if (b0 < 0 || b1 > a.T || b1 < b0) return;  // malformed: latched by the hash kernel
-  if (a.store_in_kernel && store_owner(b0, b1, a.T) >= 0) return;  // done in the hash kernel
+  if (a.store_in_kernel && (b1 == b0 || store_owner(b0, b1, a.T) >= 0)) return;  // done there
   update_slot(a, s, b0, b1);
 }
 
@@ -302,16 +333,17 @@ hipError_t launch_store_rollback(const RollbackArgs& a, hipStream_t stream) {
 hipError_t launch_compress_hash(const HashArgs& args, hipStream_t stream) {
   (void)hipGetLastError();  // drop a stale error another library left on this thread
   HashArgs a = args;
-  a.store_in_kernel = (a.slots != nullptr && a.store != nullptr && a.S > 0) ? 1 : 0;
+  const bool with_store = a.slots != nullptr && a.store != nullptr && a.S > 0;
+  a.store_in_kernel = (with_store && a.T > 0) ? 1 : 0;
   const int work = a.T > a.S + 1 ? a.T : a.S + 1;
   const int blocks = (work + 255) / 256;
   hipLaunchKernelGGL(compress_hash_kernel, dim3(blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // with at most 256 tokens one workgroup holds every position, so every sequence's
-  // slot was updated inside the hash kernel; otherwise the sequences that span two
-  // workgroups are left to a second kernel
-  if (a.store_in_kernel && a.T > 256) {
+  // with 1..256 tokens one workgroup holds every position, so every slot was settled
+  // inside the hash kernel; otherwise the sequences that span two workgroups (or, with
+  // no tokens, all of them) are left to a second kernel
+  if (with_store && (a.T > 256 || a.T == 0)) {
     hipLaunchKernelGGL(store_update_kernel, dim3((a.S + 255) / 256), dim3(256), 0, stream, a);
     e = hipGetLastError();
   }
