@@ -236,6 +236,25 @@ static bool in_host_memory(const void* p) {
   return attr.type == hipMemoryTypeHost;
 }
 
+// in_host_memory for the gather's launch shape, remembered per thread for the last few
+// table pointers: a hot call then makes no runtime query.  The answer only chooses
+// between the full grid and the grid-stride launch on a few workgroups, which write
+// the same output, so a stale entry (memory freed and reallocated elsewhere at the
+// same address) can cost speed but never change a result.
+static bool in_host_memory_cached(const void* p) {
+  constexpr int kEntries = 8;
+  thread_local const void* keys[kEntries] = {};
+  thread_local bool vals[kEntries] = {};
+  thread_local int next = 0;
+  for (int i = 0; i < kEntries; ++i)
+    if (keys[i] == p) return vals[i];
+  const bool v = in_host_memory(p);
+  keys[next] = p;
+  vals[next] = v;
+  next = (next + 1) % kEntries;
+  return v;
+}
+
 // Resolves the tables and scales one gather reads: the site's three order
 // tables, or its one table (entry 0) repeated for every order.
 static int site_tables(const engram_layout* L, const void* const* d_tables,
@@ -290,7 +309,7 @@ extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* 
   // chip to work overlapping it (the next projection, on another stream).
   g.max_blocks = 0;
   for (int n = 0; n < 3; ++n)
-    if (in_host_memory(g.table[n])) g.max_blocks = kHostGatherBlocks;
+    if (in_host_memory_cached(g.table[n])) g.max_blocks = kHostGatherBlocks;
   const size_t out_elt = out_dtype == ENGRAM_DTYPE_F32 ? 4 : 2;
   g.out_ld = out_ld;
   // one launch covers fewer than 2^31 output chunks; split bigger calls by tokens
