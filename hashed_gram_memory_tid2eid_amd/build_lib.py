@@ -41,7 +41,8 @@ BUILD_ID_PREFIX = "engram-src-sha256:"
 
 def source_hash() -> str:
     """First 16 hex digits of a SHA-256 over every source file under csrc/ and
-    include/ (relative path and bytes, in sorted order) and the compiler flags."""
+    include/ (relative path and bytes, in sorted order) and the compiler flags (paths
+    inside the tree written relative to it)."""
     h = hashlib.sha256()
     for top in (CSRC, INCLUDE):
         for root, dirs, files in os.walk(top):
@@ -52,7 +53,9 @@ def source_hash() -> str:
                     h.update(os.path.relpath(path, ROOT).encode())
                     with open(path, "rb") as fh:
                         h.update(fh.read())
-    h.update(" ".join(COMMON).encode())
+    # the flags with the tree's own location taken out, so a copy of the tree elsewhere
+    # (same sources, same flags) keeps the identity and its built library
+    h.update(" ".join(COMMON).replace(ROOT, ".").encode())
     return h.hexdigest()[:16]
 
 

@@ -380,8 +380,8 @@ extern "C" int engram_project_packed(const engram_layout* L, const void* d_rows,
   if (!d_rows || !d_packed || !d_v) return ENGRAM_E_ARG;
   if (rows_ld < L->k_pad || rows_ld % 8) return ENGRAM_E_ALIGN;
   if (!aligned(d_rows, 16) || !aligned(d_packed, 16) || !aligned(d_v, 4)) return ENGRAM_E_ALIGN;
-  // the kernel addresses one 256-row tile of rows and 8 column tiles of the packed
-  // weight with 32-bit byte offsets
+  // the kernel addresses one 256-row tile of rows and the 256 columns of the packed
+  // weight one tile reads (16 column tiles of 16) with 32-bit byte offsets
   if ((int64_t)256 * rows_ld * 2 > INT32_MAX || (int64_t)8 * L->k_pad * 64 > INT32_MAX)
     return ENGRAM_E_UNSUPPORTED;
   engram::GemmPackedArgs g;
@@ -553,7 +553,7 @@ engram_proj_plan plan_for(int64_t T, int64_t hidden, int64_t k_pad, bool packed,
   return p;
 }
 
-// The packed kernel addresses 8 column tiles of the packed weight with 32-bit offsets.
+// The packed kernel addresses 256 columns of the packed weight with 32-bit offsets.
 bool packed_weight_addressable(int64_t k_pad) { return (int64_t)8 * k_pad * 64 <= INT32_MAX; }
 
 int wkv_usable(const engram_wkv* W, const engram_layout* L, int32_t T) {

@@ -142,11 +142,11 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16_nt(const GemmArgs& a, hipStream_t stream);
 
 // The projection weight in matrix-core fragment order (see kernels/gemm_packed.hip):
-// out[N32][K16][64][8] bf16, N32 = ceil(N / 32), K16 = K / 16, rows past N zero.
+// out[N16][K32][64][8] bf16, N16 = ceil(N / 16), K32 = K / 32, rows past N zero.
 struct PackWeightArgs {
   const void* W;   // bf16 [N][ldw]
   int64_t ldw;
-  int32_t N, K;    // K multiple of 16
+  int32_t N, K;    // K multiple of 32
   void* out;
 };
 hipError_t launch_pack_weight(const PackWeightArgs& a, hipStream_t stream);

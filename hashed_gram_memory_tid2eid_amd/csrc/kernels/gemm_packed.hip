@@ -4,30 +4,40 @@
 // the hidden size before its gate).  Included into engram_device.hip after gemm.hip.
 //
 // The weight is static, so it is rearranged once (pack_weight_kernel) into
-//   Wp[N/32][K/16][64 lanes][8 bf16]:
-// the 16 bytes lane l needs as the B operand of v_mfma_f32_32x32x16_bf16 for column
-// tile j and k16 step s (column 32 j + l % 32, k 16 s + 8 (l / 32) .. +8) sit at
-// chunk (j K/16 + s) 64 + l.  A wave then fetches a whole B fragment with one
+//   Wp[N/16][K/32][64 lanes][8 bf16]:
+// the 16 bytes lane l needs as the B operand of v_mfma_f32_16x16x32_bf16 for column
+// tile j and k32 step s (column 16 j + l % 16, k 32 s + 8 (l / 16) .. +8) sit at
+// chunk (j K/32 + s) 64 + l.  A wave then fetches a whole B fragment with one
 // 16-byte-per-lane load of 1 KB of consecutive bytes (8 full cache lines) straight
 // into registers, and B takes no LDS at all: no direct-load writes and no
 // fragment reads.  The LDS keeps only the gathered rows (operand A), in a deeper
 // ring than the two-operand kernel can afford.
 //
-// Tile: 256 x 256 per workgroup, 8 waves as 2 (M) x 4 (N), 128 x 64 per wave (4 x 2
-// tiles of 32 x 32, two waves per SIMD), the same products accumulated in the same
-// k16 order as gemm_bf16_nt_kernel, so C is bit-identical to it.  Calls with a short
-// K take 128 x 256 tiles of 4 waves (1 x 4, the same 128 x 64 per wave) instead, two
-// workgroups per CU: one workgroup's prologue and epilogue then overlap the other's
-// main loop, and each stage barrier holds only one wave per SIMD.
+// Tile: 256 x 256 per workgroup, 8 waves as 2 (M) x 4 (N), 128 x 64 per wave (8 x 4
+// tiles of 16 x 16, two waves per SIMD).  Calls with a short K take 128 x 256 tiles of
+// 4 waves (1 x 4, the same 128 x 64 per wave) instead, two workgroups per CU: one
+// workgroup's prologue and epilogue then overlap the other's main loop, and each
+// stage barrier holds only one wave per SIMD.
+// The 16 x 16 x 32 shape instead of 32 x 32 x 16 (the two-operand kernel's): the
+// same flops per cycle with a quarter of the accumulator per instruction, so the
+// matrix core reads and writes a third fewer register bytes per flop; measured 2-4%
+// faster at every K here, with C bit-identical to gemm_bf16_nt_kernel's (the matrix
+// core sums each output's products in the same k order under both shapes).  Each wave
+// raises its issue priority over its MFMA runs (s_setprio 1, back to 0 after), so a
+// SIMD keeps issuing the wave whose products are ready while the other issues loads;
+// about 2% at k_pad 19,584.
 // A: direct loads into LDS of one 128-byte line per row per 64-k stage, in a ring
 // of A_STAGES stages, XOR-swizzled as in gemm.hip.
-// B: a ring of four k16 steps in registers; the fragments of step s of stage kt+1 are
-// requested right after step s of stage kt has been multiplied, one stage ahead.
+// Inside a stage four sub-steps run: k32 step 0 rows 0-63, step 0 rows 64-127, step 1
+// rows 0-63, step 1 rows 64-127 of the wave tile; the A fragments of the next sub-step
+// are read from LDS while this one multiplies.
+// B: a ring of the two k32 steps in registers; step s of stage kt+1 is requested right
+// after the last sub-step of stage kt that multiplies step s, two sub-steps ahead.
 //
 // Every iteration issues the same loads (the last stages re-read clamped, in-bounds
 // addresses into slots nothing reads again), so the vector-memory counter waits
-// below are fixed numbers: per iteration, in issue order, B steps 0..2 (2 loads
-// each), the stage wait, A (4 loads), B step 3 (2 loads).
+// below are fixed numbers: per iteration, in issue order, B step 0 (4 loads), the
+// stage wait, A (4 loads), B step 1 (4 loads).
 
 namespace engram {
 
@@ -40,11 +50,10 @@ constexpr int kBufferRsrcFlags = 0x00020000;
 
 struct GemmPackedKArgs {
   const __bf16* A;     // bf16 [M][lda]
-  const bf16x8* Bp;    // packed weight, [N32][K16][64] chunks of 8 bf16
+  const bf16x8* Bp;    // packed weight, [N16][K32][64] chunks of 8 bf16
   float* C;            // f32 [M][ldc]
   int64_t lda, ldc;
   int32_t M, N, K;     // K multiple of 64
-  int32_t n32;         // ceil(N / 32)
   int32_t tiles_m, tiles_n, group_m;
   int32_t vec_store;
 };
@@ -54,13 +63,13 @@ void pack_weight_kernel(const __bf16* __restrict__ W, int64_t ldw, int32_t N, in
                         int64_t total_chunks, bf16x8* __restrict__ out) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= total_chunks) return;
-  const int k16 = K >> 4;
+  const int k32 = K >> 5;
   const int lane = (int)(c & 63);
   const int64_t t = c >> 6;
-  const int s = (int)(t % k16);
-  const int j = (int)(t / k16);
-  const int n = j * 32 + (lane & 31);
-  const int k = s * 16 + 8 * (lane >> 5);
+  const int s = (int)(t % k32);
+  const int j = (int)(t / k32);
+  const int n = j * 16 + (lane & 15);
+  const int k = s * 32 + 8 * (lane >> 4);
   bf16x8 v = {};
   if (n < N) v = *reinterpret_cast<const bf16x8*>(W + (int64_t)n * ldw + k);
   out[c] = v;
@@ -70,13 +79,14 @@ template <int A_STAGES, int BM, int WM_WAVES>
 __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
   constexpr int BN = 256, WN_WAVES = 4, NWAVES = WM_WAVES * WN_WAVES;
   constexpr int BK = kGemmBK;
-  constexpr int WM = BM / WM_WAVES, WN = BN / WN_WAVES, TM = WM / 32, TN = WN / 32;
+  constexpr int WM = BM / WM_WAVES, WN = BN / WN_WAVES, TM = WM / 16, TN = WN / 16;
+  constexpr int HM = TM / 2;                   // 16-row blocks per half
   constexpr int STAGE = BM * BK * 2;           // bytes of A per stage
   constexpr int AI = BM / 8 / NWAVES;          // 1 KB direct loads per wave per stage
-  constexpr int BL = TN;                       // B loads per k16 step
-  constexpr int PER_ITER = 4 * BL + AI;        // vector-memory loads per iteration
-  static_assert(AI * 8 * NWAVES == BM, "A tile must fill whole load rounds");
+  constexpr int BL = TN;                       // B loads per k32 step
+  constexpr int PER_ITER = 2 * BL + AI;        // vector-memory loads per iteration
   static_assert(A_STAGES >= 2, "ring needs two stages");
+  static_assert(AI * 8 * NWAVES == BM, "A tile must fill whole load rounds");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   // ---- tile id: XCD-contiguous runs, then GROUP_M swizzle (as gemm.hip) -------
@@ -97,7 +107,7 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN_WAVES, wn = wave % WN_WAVES;
   const int nk = a.K / BK;
-  const int k16 = a.K >> 4;
+  const int k32 = a.K >> 5;
 
   // Both operands are read through buffer resources (MUBUF): the compiler counts
   // direct-to-LDS buffer loads and register buffer loads on one in-order vector
@@ -108,10 +118,11 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
   const int rows_here = min(a.M - m0, BM);
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.A + (int64_t)m0 * a.lda), (short)0, (int)((int64_t)rows_here * a.lda * 2), kBufferRsrcFlags);
-  const int jt0 = n0 / 32;
-  const int tiles_here = min(a.n32 - jt0, BN / 32);
+  const int n16 = (a.N + 15) / 16;
+  const int jt0 = n0 / 16;
+  const int tiles_here = min(n16 - jt0, BN / 16);
   const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.Bp + (int64_t)jt0 * k16 * 64), (short)0, tiles_here * k16 * 1024, kBufferRsrcFlags);
+      (void*)(a.Bp + (int64_t)jt0 * k32 * 64), (short)0, tiles_here * k32 * 1024, kBufferRsrcFlags);
 
   // ---- A: direct loads into LDS (wave w, load i fills LDS bytes
   //      [(NWAVES i + w) KB, +1 KB) of the stage; 8 lanes fetch one whole line).
@@ -136,108 +147,105 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int jt = min(wn * TN + j, tiles_here - 1);
-    boff[j] = (jt * k16 * 64 + lane) * 16;
+    boff[j] = (jt * k32 * 64 + lane) * 16;
   }
-  bf16x8 bfr[4][TN];
+  bf16x8 bfr[2][TN];
   auto issue_b = [&](int kt, int ks) {
-    const int s = min(kt, nk - 1) * 4 + ks;
+    const int s = min(kt, nk - 1) * 2 + ks;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       bfr[ks][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(brsrc, boff[j] + s * 1024, 0, 0));
   };
 
-  // ---- A fragment rows and swizzles inside a stage ---------------------------
-  const int lrow = lane & 31, lk = lane >> 5;
-  int arow[TM], aswz[TM];
+  // rows 16 apart share the swizzle ((row >> 1) & 7), so one base and one swizzle
+  // serve every block; the blocks are immediate offsets of 16 rows
+  const int lrow = lane & 15, lk = lane >> 4;
+  const int r0 = wm * WM + lrow;
+  const int arow0 = r0 * BK, aswz0 = gemm_swz(r0);
+  // fragments of rows half h (16-row blocks h HM .. +HM) for k32 step ks
+  auto load_a = [&](int kt, int ks, int h, bf16x8* fa) {
+    const __bf16* base = reinterpret_cast<const __bf16*>(smem + (kt % A_STAGES) * STAGE) + arow0 +
+                         8 * ((ks * 4 + lk) ^ aswz0);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = wm * WM + i * 32 + lrow;
-    arow[i] = r * BK;
-    aswz[i] = gemm_swz(r);
-  }
-  auto load_a = [&](int kt, int ks, bf16x8* fa) {
-    const __bf16* base = reinterpret_cast<const __bf16*>(smem + (kt % A_STAGES) * STAGE);
-    const int c = ks * 2 + lk;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + arow[i] + 8 * (c ^ aswz[i]));
+    for (int i = 0; i < HM; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(base + (h * HM + i) * 16 * BK);
   };
 
-  f32x16 acc[TM][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{};
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb, int h) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < HM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        acc[h * HM + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[h * HM + i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- prologue: B of stage 0, then A stages 0 .. A_STAGES-1; wait for A stage 0
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) issue_b(0, ks);
+  issue_b(0, 0);
+  issue_b(0, 1);
 #pragma unroll
   for (int s = 0; s < A_STAGES; ++s) issue_a(s);
   wait_vmcnt<(A_STAGES - 1) * AI>();
   __builtin_amdgcn_s_barrier();
 
   // Loads issued after A stage kt+1 when iteration kt waits for it: in steady state
-  // (A_STAGES-2) whole iterations plus B step 3 of the iteration that issued it and
-  // B steps 0..2 of this one; in the first A_STAGES-1 iterations the stage came from
+  // (A_STAGES-2) whole iterations plus B step 1 of the iteration that issued it and
+  // B step 0 of this one; in the first A_STAGES-1 iterations the stage came from
   // the prologue and fewer loads follow it, fewest at kt = 0.
-  constexpr int WAIT_SS = (A_STAGES - 2) * PER_ITER + 4 * BL;
-  constexpr int WAIT_EARLY = (A_STAGES - 2) * AI + 3 * BL;
+  constexpr int WAIT_SS = (A_STAGES - 2) * PER_ITER + 2 * BL;
+  constexpr int WAIT_EARLY = (A_STAGES - 2) * AI + BL;
   static_assert(WAIT_SS <= 63 && WAIT_EARLY <= WAIT_SS, "vmcnt field holds 6 bits");
 
-  bf16x8 fa0[TM], fa1[TM];
-  load_a(0, 0, fa0);
+  bf16x8 fa0[HM], fa1[HM];
+  load_a(0, 0, 0, fa0);
   for (int kt = 0; kt < nk; ++kt) {
     wait_lgkmcnt0();
     __builtin_amdgcn_sched_barrier(0);
-    load_a(kt, 1, fa1);
+    load_a(kt, 0, 1, fa1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fa0, bfr[0]);
+    mma(fa0, bfr[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kt, 1, 0, fa0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, bfr[0], 1);
     __builtin_amdgcn_sched_barrier(0);
     issue_b(kt + 1, 0);
     wait_lgkmcnt0();
     __builtin_amdgcn_sched_barrier(0);
-    load_a(kt, 2, fa0);
+    load_a(kt, 1, 1, fa1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, bfr[1]);
+    mma(fa0, bfr[1], 0);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b(kt + 1, 1);
-    wait_lgkmcnt0();
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(kt, 3, fa1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa0, bfr[2]);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(kt + 1, 2);
-    // this wave has read all of A stage kt once step 3 has landed; the barrier makes
-    // that true for every wave and publishes A stage kt+1, then slot kt % A_STAGES
-    // is refilled with stage kt + A_STAGES
+    // this wave has read all of A stage kt once the last sub-step's fragments have
+    // landed; the barrier makes that true for every wave and publishes A stage kt+1,
+    // then slot kt % A_STAGES is refilled with stage kt + A_STAGES
     wait_lgkmcnt0();
     if (kt + 1 < A_STAGES) wait_vmcnt<WAIT_EARLY>(); else wait_vmcnt<WAIT_SS>();
     __builtin_amdgcn_s_barrier();
     issue_a(kt + A_STAGES);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(kt + 1 < nk ? kt + 1 : kt, 0, fa0);
+    load_a(kt + 1 < nk ? kt + 1 : kt, 0, 0, fa0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, bfr[3]);
+    mma(fa1, bfr[1], 1);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b(kt + 1, 3);
+    issue_b(kt + 1, 1);
   }
 
-  // ---- epilogue (as gemm.hip): stage one 32-row slab per wave in LDS, write
-  //      whole row segments of C with 16-byte stores.  The clamped loads of the
-  //      last iterations may still be landing in the ring: drain them first.
+  // ---- epilogue (as gemm.hip): stage one 16-row slab per wave in LDS, write whole
+  //      row segments of C with 16-byte stores.  The clamped loads of the last
+  //      iterations may still be landing in the ring: drain them first.
   constexpr int PITCH = WN + 4;
-  static_assert(NWAVES * 32 * PITCH * 4 <= A_STAGES * STAGE, "epilogue staging must fit in the ring");
+  static_assert(NWAVES * 16 * PITCH * 4 <= A_STAGES * STAGE, "epilogue staging must fit in the ring");
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
-  float* slab = reinterpret_cast<float*>(smem) + wave * 32 * PITCH;
+  float* slab = reinterpret_cast<float*>(smem) + wave * 16 * PITCH;
   const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N) && a.vec_store;
   constexpr int LANES_PER_ROW = WN / 4;
   constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
@@ -246,15 +254,15 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        slab[r * PITCH + j * 32 + (lane & 31)] = acc[i][j][v];
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * (lane >> 4) + v;
+        slab[r * PITCH + j * 16 + (lane & 15)] = acc[i][j][v];
       }
     }
-    const int gm0 = m0 + wm * WM + i * 32;
+    const int gm0 = m0 + wm * WM + i * 16;
     const int gn = n0 + wn * WN + (lane % LANES_PER_ROW) * 4;
 #pragma unroll
-    for (int q = 0; q < 32 / ROWS_PER_PASS; ++q) {
+    for (int q = 0; q < 16 / ROWS_PER_PASS; ++q) {
       const int r = q * ROWS_PER_PASS + lane / LANES_PER_ROW;
       const f32x4 val = *reinterpret_cast<const f32x4*>(slab + r * PITCH + (lane % LANES_PER_ROW) * 4);
       const int m = gm0 + r;
@@ -281,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt_packed128_kernel(GemmPack
 
 hipError_t launch_pack_weight(const PackWeightArgs& g, hipStream_t stream) {
   (void)hipGetLastError();
-  if (g.N <= 0 || g.K <= 0 || g.K % 16 != 0) return hipErrorInvalidValue;
-  const int64_t total = (int64_t)((g.N + 31) / 32) * (g.K / 16) * 64;
+  if (g.N <= 0 || g.K <= 0 || g.K % 32 != 0) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)((g.N + 15) / 16) * (g.K / 32) * 64;
   const int64_t blocks = (total + 255) / 256;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
@@ -304,7 +312,6 @@ hipError_t launch_gemm_bf16_nt_packed(const GemmPackedArgs& g, hipStream_t strea
   a.M = g.M;
   a.N = g.N;
   a.K = g.K;
-  a.n32 = (g.N + 31) / 32;
   a.tiles_n = (g.N + 255) / 256;
   a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
   // short K: two 128-row workgroups per CU (tile groups of 4 row blocks, the same rows
@@ -322,7 +329,7 @@ hipError_t launch_gemm_bf16_nt_packed(const GemmPackedArgs& g, hipStream_t strea
                                    lds_set256);
   if (e != hipSuccess) return e;
   // per-tile byte offsets are 32-bit: one tile's rows of A and 8 column tiles of B
-  if ((int64_t)256 * g.lda * 2 > 0x7FFFFFFF || (int64_t)8 * (g.K / 16) * 1024 > 0x7FFFFFFF)
+  if ((int64_t)256 * g.lda * 2 > 0x7FFFFFFF || (int64_t)16 * (g.K / 32) * 1024 > 0x7FFFFFFF)
     return hipErrorInvalidValue;
   const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;

@@ -339,9 +339,11 @@ int engram_project(const engram_layout* layout, const void* d_rows, int64_t rows
  *   ceil(hidden / 32) * 32 * k_pad * 2 bytes.
  * engram_pack_weight: d_w bf16 [hidden][w_ld] as for engram_project (columns
  *   k_pad.. ignored) -> d_packed (caller-owned, that many bytes, 16-byte aligned):
- *   for column tile j = o / 32, k16 step s = k / 16 and lane l = o % 32 + 32 ((k % 16) / 8),
- *   element W[o][k] sits at bf16 index ((j (k_pad / 16) + s) 64 + l) 8 + k % 8;
- *   rows past hidden are zero.  Enqueued on `stream`; d_w may be freed once it ran.
+ *   for column tile j = o / 16, k32 step s = k / 32 and lane l = o % 16 + 16 ((k % 32) / 8),
+ *   element W[o][k] sits at bf16 index ((j (k_pad / 32) + s) 64 + l) 8 + k % 8 (the B
+ *   operand of the 16 x 16 x 32 bf16 matrix-core instruction); rows past hidden up to
+ *   the next multiple of 16 are zero, the rest of the buffer is not written.  Enqueued
+ *   on `stream`; d_w may be freed once it ran.
  * engram_project_packed: v = rows W^T as engram_project, from the packed weight,
  *   bit-identical to engram_project (the same products summed in the same order).
  *   Meant for many tokens (tiles of 128 x 256 for k_pad up to 8,192, else 256 x 256);

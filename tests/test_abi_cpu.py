@@ -488,6 +488,25 @@ def test_loaded_library_is_built_from_the_tree():
     assert bl["built_hash"](os.path.join(ROOT, "README.md")) is None
 
 
+def test_build_identity_does_not_depend_on_where_the_tree_sits(tmp_path):
+    """A copy of the sources and the build script in another directory hashes to the
+    same identity, so a tree moved or copied elsewhere keeps its built library
+    instead of rebuilding it; a changed source byte changes the identity."""
+    import runpy
+    import shutil
+    pkg = os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd")
+    here = runpy.run_path(os.path.join(pkg, "build_lib.py"))["source_hash"]()
+    dst = tmp_path / "elsewhere"
+    shutil.copytree(os.path.join(pkg, "csrc"), dst / "hashed_gram_memory_tid2eid_amd" / "csrc")
+    shutil.copytree(os.path.join(ROOT, "include"), dst / "include")
+    shutil.copy(os.path.join(pkg, "build_lib.py"), dst / "hashed_gram_memory_tid2eid_amd" / "build_lib.py")
+    script = str(dst / "hashed_gram_memory_tid2eid_amd" / "build_lib.py")
+    assert runpy.run_path(script)["source_hash"]() == here
+    with open(dst / "include" / "engram.h", "a") as f:
+        f.write("\n")
+    assert runpy.run_path(script)["source_hash"]() != here
+
+
 def test_bench_cpu_baseline_leg_runs_pinned_on_host_tensors():
     """bench.py's oracle leg on CPU copies of small workloads (one site and the
     two-site released structure): it reports a positive rate on one core with the

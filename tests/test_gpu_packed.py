@@ -2,8 +2,9 @@
 (engram_pack_weight + engram_project_packed), through the C ABI.
 
 Bars: the packed bytes sit where the header's index formula puts them (checked
-element by element on the host); v is bit-identical to engram_project, which
-accumulates the same bf16 products in the same k16 order, and within the fp32
+element by element on the host); v is bit-identical to engram_project (16 x 16 x 32
+matrix-core products against its 32 x 32 x 16 ones: the matrix core sums each
+output's bf16 products in the same k order under both shapes), and within the fp32
 accumulation bound of torch's fp32 matmul of the same operands; the runtime
 picks the packed kernel for many-token calls and its streams match the oracle
 (the prefill and full-scale parity tests in test_gpu_parity.py run through it).
@@ -50,9 +51,10 @@ def _operands(L, M, N, seed):
 
 
 def test_packed_bytes_follow_the_index_formula(eng):
-    """Every element of a ragged weight (hidden 72: three column tiles, the last
-    one part padding; w_ld past k_pad) lands at the documented bf16 index, and
-    the padding rows are zero."""
+    """Every element of a ragged weight (hidden 72: five column tiles of 16, the last
+    one part padding; w_ld past k_pad) lands at the documented bf16 index, the padding
+    rows of the last tile are zero, and the buffer past the last tile (sized for
+    hidden rounded up to 32 rows) is left as it was."""
     L = _layout(eng, 3, 64)
     K = L.info.k_pad  # 192
     N, ld = 72, K + 8
@@ -63,14 +65,15 @@ def test_packed_bytes_follow_the_index_formula(eng):
     torch.cuda.synchronize()
     got = packed.view(torch.int16).cpu().numpy()
     wh = w.view(torch.int16).cpu().numpy()
-    n32 = (N + 31) // 32
-    assert got.size == n32 * 32 * K
-    o = np.arange(n32 * 32)[:, None]
+    n16 = (N + 15) // 16
+    assert got.size == (N + 31) // 32 * 32 * K
+    o = np.arange(n16 * 16)[:, None]
     k = np.arange(K)[None, :]
-    idx = (((o // 32) * (K // 16) + k // 16) * 64 + o % 32 + 32 * ((k % 16) // 8)) * 8 + k % 8
-    # the formula is a permutation of [0, n32 * 32 * K)
-    assert np.array_equal(np.sort(idx.ravel()), np.arange(n32 * 32 * K))
-    expect = np.zeros(n32 * 32 * K, np.int16)
+    idx = (((o // 16) * (K // 32) + k // 32) * 64 + o % 16 + 16 * ((k % 32) // 8)) * 8 + k % 8
+    # the formula is a permutation of [0, n16 * 16 * K)
+    assert np.array_equal(np.sort(idx.ravel()), np.arange(n16 * 16 * K))
+    expect = np.full(got.size, np.uint16(0xABAB).view(np.int16), np.int16)
+    expect[:n16 * 16 * K] = 0
     expect[idx[:N].ravel()] = wh[:, :K].ravel()
     assert np.array_equal(got, expect)
 
