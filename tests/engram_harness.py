@@ -112,7 +112,7 @@ def bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 class Site:
     def __init__(self, cfg: ei.EngramConfig, max_tokens: int, scale_mode: str = "pow2",
-                 tables: "ei.Tables | None" = None):
+                 tables: "ei.Tables | None" = None, proj_splits: int = 0):
         import hashed_gram_memory_tid2eid_amd as eng
         self.eng = eng
         self.cfg = cfg
@@ -126,7 +126,8 @@ class Site:
             heads_per_order=cfg.heads, rows=[cfg.rows] * 3, row_dim=cfg.row_dim,
             table_dtype=cfg.table_dtype, row_pitch_bytes=cfg.row_pitch_bytes,
             tid2eid=self.tid2eid, tables=self.tables.data, scales=self.tables.scale,
-            weight=self.weight, hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=max_tokens)
+            weight=self.weight, hidden=cfg.hidden, hc_mult=cfg.hc_mult, max_tokens=max_tokens,
+            proj_splits=proj_splits)
         self.olayout = oracle.fit_layout([cfg.rows] * 3, cfg.heads)
         self.pad_eid = int(self.tid2eid_h[cfg.pad_token_id])
         torch.cuda.synchronize()
