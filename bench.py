@@ -10,10 +10,12 @@ Default workload ("full"): 8 x 8,192 Zipf(1.1) tokens against three
 5,040,000-row e4m3fn tables (row dim 6,500 + an fp32 scale per row, 91.6 GiB),
 one hash head per order, projection 19,500 -> 4,096 into 4 residual streams.
 
-Prints one JSON line: tokens/s, the roofline of the gather kernel (HBM bytes
-the method must move / measured average launch time, against 8 TB/s), the
-per-kernel breakdown, and the oracle's single-core throughput on a bounded
-token sample.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line: tokens/s; `roofline`, the roofline of the kernel that takes
+the most time per step (at full scale the projection: flops / measured average
+launch time, against 2.5 PFLOP/s bf16); the rooflines of the gather (HBM bytes the
+method must move / launch time, against 8 TB/s: the metric's HBM figure), the
+projection and the gate under their own names; the per-kernel breakdown; and the
+oracle's single-core throughput on a bounded token sample.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 [--config full|full_bf16|long|prefill|decode|tiny|v41|v41_small] [--path split|fused] [--graph] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -58,11 +60,15 @@ def algorithmic_per_token(cfg):
     K = 3 * H * D
     scale = 0 if cfg.table_dtype != "fp8" else (D // 32 if cfg.scale_block else 4)
     return {
+        "project_weight_bytes": 2 * K * hidden,
         # token id, tid2eid entry, compressed id out, 3H row ids per site out
         "hash_bytes": 4 + 4 + 4 + 4 * 3 * H * cfg.n_sites,
         # per site: 3H rows of D elements + their scales in; K bf16 out
         "gather_bytes": 3 * H * (D * cfg.elt_bytes + scale) + 2 * K,
         "project_flops": 2 * K * hidden,
+        # per token: its row of E (bf16) in and its row of v (fp32) out; the weight's
+        # bytes (project_weight_bytes) are per call, not per token
+        "project_token_bytes": 2 * K + 4 * hidden,
         # 4 bf16 streams read and written, v (fp32) read
         "gate_bytes": cfg.hc_mult * hidden * 2 * 2 + 4 * hidden,
     }
@@ -445,26 +451,44 @@ def main():
         kernels["project"] = {"ms": kern_ms["project"], "bound": "mfma", "TFLOP/s": proj_tflops,
                               "frac": proj_tflops / BF16_PEAK_TFLOPS}
         traffic = measured_traffic(cfg)
-        roofline = {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
-                    "traffic": traffic, "bytes_per_launch": gather_bytes,
-                    "avg_launch_ms": kern_ms["gather_dequant"]}
+        roofline_gather = {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
+                           "traffic": traffic, "bytes_per_launch": gather_bytes,
+                           "avg_launch_ms": kern_ms["gather_dequant"]}
         if traffic is not None:
             # the HBM rate the counters imply for this run's launch time
             kernels["gather_dequant"]["hbm_GB/s_measured_bytes"] = gbs(traffic, kern_ms["gather_dequant"])
-        # the metric names the gather's HBM rate; the projection takes most of the step,
-        # so its own roofline goes beside it
         pkind = site.projection_kind(0, T)
         proj_traffic = (measured_traffic(cfg, "gemm_bf16_nt_packed_{tag}_counters.txt", "gemm_packed.hip")
                         if pkind == "packed" else None)
-        roofline_projection = {"bound": "mfma",
-                               "kernel": "gemm_bf16_nt_packed" if pkind == "packed" else "gemm_bf16_nt",
-                               "achieved": proj_tflops,
-                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": proj_tflops / BF16_PEAK_TFLOPS, "traffic": proj_traffic,
-                               "flops_per_launch": proj_flops, "avg_launch_ms": kern_ms["project"]}
+        # bound by the matrix cores when its flops per algorithmic byte (the weight once,
+        # E in, v out) reach the ridge of 2.5 PFLOP/s over 8 TB/s, else by HBM (few tokens:
+        # a decode step streams the whole weight for 256 rows)
+        proj_bytes = per["project_weight_bytes"] + per["project_token_bytes"] * T
+        kname = "gemm_bf16_nt_packed" if pkind == "packed" else "gemm_bf16_nt"
+        if proj_flops / proj_bytes >= BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            roofline_projection = {"bound": "mfma", "kernel": kname, "achieved": proj_tflops,
+                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": proj_tflops / BF16_PEAK_TFLOPS, "traffic": proj_traffic,
+                                   "flops_per_launch": proj_flops, "avg_launch_ms": kern_ms["project"]}
+        else:
+            proj_gbs = gbs(proj_bytes, kern_ms["project"])
+            kernels["project"].update({"bound": "hbm", "GB/s": proj_gbs})
+            roofline_projection = {"bound": "hbm", "kernel": kname, "achieved": proj_gbs,
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": proj_gbs / HBM_PEAK_GBS,
+                                   "traffic": proj_traffic, "bytes_per_launch": proj_bytes,
+                                   "flops_per_launch": proj_flops, "avg_launch_ms": kern_ms["project"]}
     kernels["gate_add"] = {"ms": kern_ms["gate_add"], "bound": "hbm", "GB/s": gate_gbs,
                            "frac": gate_gbs / HBM_PEAK_GBS}
+    if args.path != "fused":
+        roofline_gate = {"bound": "hbm", "kernel": "gate_add", "achieved": gate_gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gate_gbs / HBM_PEAK_GBS,
+                         "traffic": None, "bytes_per_launch": per["gate_bytes"] * T,
+                         "avg_launch_ms": kern_ms["gate_add"]}
+        # `roofline` is the dominant kernel's: the one with the most time per step (the
+        # hash is a few microseconds at every size and never dominates)
+        roofline = max((roofline_gather, roofline_projection, roofline_gate),
+                       key=lambda r: r["avg_launch_ms"])
     for n in kernels:
         kernels[n].setdefault("launches_per_step", NS)
 
@@ -497,7 +521,9 @@ def main():
         "library": eng.engram_build_id(),
     }
     if args.path != "fused":
+        result["roofline_gather"] = roofline_gather
         result["roofline_projection"] = roofline_projection
+        result["roofline_gate"] = roofline_gate
     if lookahead_ok:
         # the same K steps in the sequential order (hash, gather, projection, gate of one
         # call), on the same inputs, after the main line

@@ -1,7 +1,8 @@
 """bench.py keeps its output contract: one JSON line with the metric, the
-whole-job value, the roofline of the gather and of the projection, the per-kernel
-breakdown, the sequential step order timed beside the look-ahead one, and the
-oracle's CPU rate.  Runs the tiny workload in a child process
+whole-job value, the roofline of the dominant kernel (the one with the most time per
+step) and those of the gather, the projection and the gate under their own names,
+the per-kernel breakdown, the sequential step order timed beside the look-ahead one,
+and the oracle's CPU rate.  Runs the tiny workload in a child process
 (a few seconds)."""
 import json
 import os
@@ -32,11 +33,19 @@ def test_bench_json_line_contract():
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
     assert d["value"] == pytest.approx(d["config"]["tokens_per_step"] / (d["ms_per_step"] * 1e-3), rel=1e-6)
     assert "workload" in d["config"]
-    r = d["roofline"]
-    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
-        assert k in r, k
-    assert r["bound"] == "hbm" and r["frac"] == pytest.approx(r["achieved"] / r["peak"])
-    assert d["roofline_projection"]["bound"] == "mfma"
+    named = {"gather_dequant": d["roofline_gather"], "gemm": d["roofline_projection"],
+             "gate_add": d["roofline_gate"]}
+    for r in list(named.values()) + [d["roofline"]]:
+        for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "avg_launch_ms"):
+            assert k in r, k
+        assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
+    assert named["gather_dequant"]["bound"] == "hbm" and named["gate_add"]["bound"] == "hbm"
+    # tiny's projection (512 tokens, 768 -> 256) does 118 flops per algorithmic byte, below
+    # the ridge of 2.5 PFLOP/s over 8 TB/s (312.5): bound by HBM, against 8 TB/s
+    assert named["gemm"]["bound"] == "hbm" and named["gemm"]["unit"] == "GB/s"
+    # the dominant kernel: the named roofline with the longest launch
+    longest = max(named.values(), key=lambda r: r["avg_launch_ms"])
+    assert d["roofline"] == longest
     # the tiny workload is a many-token split-path call: the look-ahead order is timed,
     # and the sequential order beside it
     assert d["config"]["step_order"] == "lookahead"
