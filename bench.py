@@ -241,6 +241,10 @@ def main():
                          "call's hash, then per site this call's projection, the next call's "
                          "gather, this call's gate; sequential: hash, gather, projection, gate. "
                          "The other order is timed after the main line.")
+    ap.add_argument("--decode-lookup", default="fused", choices=["fused", "split"],
+                    help="decode steps: fused = compress, hash and gather in one launch "
+                         "(engram_lookup_decode, where the layout allows it); split = "
+                         "engram_compress_hash then engram_gather_dequant")
     ap.add_argument("--proj-splits", type=int, default=0,
                     help="split-K factor of the projection (0: chosen from the call size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -328,6 +332,10 @@ def main():
 
     tok, cu, ss, sl = d(batch.tokens), d(batch.cu_seqlens), d(batch.seq_start), d(batch.slots)
     store = site.make_store(cfg.n_seqs, ids=d(ei.make_store_init(cfg))) if cfg.decode_steps else None
+    # decode steps (one token per sequence, continuing from its slot) take the
+    # one-launch lookup where the layout allows it
+    use_lookup = (bool(cfg.decode_steps) and cfg.seq_len == 1 and args.decode_lookup == "fused"
+                  and args.path == "split" and site.decode_lookup_supported)
     L = site.layout
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -338,6 +346,8 @@ def main():
     # (this call's rows, gathered one step earlier) comes before the next call's gather
     if args.path == "fused":
         seq = ["compress_hash"] + ["gather_project", "gate_add"] * NS
+    elif use_lookup:
+        seq = ["lookup_decode", "project", "gate_add"]
     else:
         seq = ["compress_hash"] + ["gather_dequant", "project", "gate_add"] * NS
     seq_la = ["compress_hash"] + ["project", "gather_dequant", "gate_add"] * NS
@@ -372,6 +382,15 @@ def main():
                 ev[k].record()
             k += 1
         mark()
+        if use_lookup:
+            eng.engram_lookup_decode(L, tid2eid, tok, site.eids, site.row_ids, site.site_tables[0],
+                                     site.site_scales[0], site.rows, slots=sl, store=store)
+            mark()
+            site.project(0, site.rows, T)
+            mark()
+            site.gate(0, site_streams[0], T)
+            mark()
+            return
         eng.engram_compress_hash(L, tid2eid, tok, cu, site.eids, site.row_ids, seq_start=ss,
                                  slots=sl, store=store)
         mark()
@@ -432,9 +451,17 @@ def main():
     gather_bytes = per["gather_bytes"] * T
     proj_flops = per["project_flops"] * T
     gate_gbs = gbs(per["gate_bytes"] * T, kern_ms["gate_add"])
-    hash_gbs = gbs(per["hash_bytes"] * T, kern_ms["compress_hash"])
-    kernels = {"compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs,
-                                 "launches_per_step": 1}}
+    if use_lookup:
+        # the lookup is the hash and the gather in one launch: its bytes are both kernels'
+        kernels = {}
+        lookup_bytes = (per["hash_bytes"] + per["gather_bytes"]) * T
+        lookup_gbs = gbs(lookup_bytes, kern_ms["lookup_decode"])
+        kernels["lookup_decode"] = {"ms": kern_ms["lookup_decode"], "bound": "hbm", "GB/s": lookup_gbs,
+                                    "frac": lookup_gbs / HBM_PEAK_GBS, "launches_per_step": 1}
+    else:
+        hash_gbs = gbs(per["hash_bytes"] * T, kern_ms["compress_hash"])
+        kernels = {"compress_hash": {"ms": kern_ms["compress_hash"], "bound": "alu", "GB/s": hash_gbs,
+                                     "launches_per_step": 1}}
     if args.path == "fused":
         fused_tflops = proj_flops / (kern_ms["gather_project"] * 1e-3) / 1e12
         kernels["gather_project"] = {"ms": kern_ms["gather_project"], "bound": "mfma",
@@ -444,17 +471,24 @@ def main():
                     "traffic": None, "flops_per_launch": proj_flops,
                     "avg_launch_ms": kern_ms["gather_project"]}
     else:
-        gather_gbs = gbs(gather_bytes, kern_ms["gather_dequant"])
         proj_tflops = proj_flops / (kern_ms["project"] * 1e-3) / 1e12
-        kernels["gather_dequant"] = {"ms": kern_ms["gather_dequant"], "bound": "hbm", "GB/s": gather_gbs,
-                                     "frac": gather_gbs / HBM_PEAK_GBS}
+        if not use_lookup:
+            gather_gbs = gbs(gather_bytes, kern_ms["gather_dequant"])
+            kernels["gather_dequant"] = {"ms": kern_ms["gather_dequant"], "bound": "hbm",
+                                         "GB/s": gather_gbs, "frac": gather_gbs / HBM_PEAK_GBS}
         kernels["project"] = {"ms": kern_ms["project"], "bound": "mfma", "TFLOP/s": proj_tflops,
                               "frac": proj_tflops / BF16_PEAK_TFLOPS}
-        traffic = measured_traffic(cfg)
-        roofline_gather = {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
-                           "traffic": traffic, "bytes_per_launch": gather_bytes,
-                           "avg_launch_ms": kern_ms["gather_dequant"]}
+        traffic = None if use_lookup else measured_traffic(cfg)
+        if use_lookup:
+            roofline_gather = {"bound": "hbm", "kernel": "lookup_decode", "achieved": lookup_gbs,
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lookup_gbs / HBM_PEAK_GBS,
+                               "traffic": None, "bytes_per_launch": lookup_bytes,
+                               "avg_launch_ms": kern_ms["lookup_decode"]}
+        else:
+            roofline_gather = {"bound": "hbm", "kernel": "gather_dequant", "achieved": gather_gbs,
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
+                               "traffic": traffic, "bytes_per_launch": gather_bytes,
+                               "avg_launch_ms": kern_ms["gather_dequant"]}
         if traffic is not None:
             # the HBM rate the counters imply for this run's launch time
             kernels["gather_dequant"]["hbm_GB/s_measured_bytes"] = gbs(traffic, kern_ms["gather_dequant"])
@@ -513,7 +547,8 @@ def main():
                    "tables_in": "pinned host memory" if args.host_tables else "HBM",
                    "proj_splits": site.proj_splits,
                    "step_order": "lookahead" if lookahead_ok else "sequential",
-                   "projection": site.projection_kind(0, T) if args.path != "fused" else "fused"},
+                   "projection": site.projection_kind(0, T) if args.path != "fused" else "fused",
+                   "lookup": "lookup_decode" if use_lookup else "compress_hash + gather_dequant"},
         "roofline": roofline,
         "kernels": kernels,
         "wall_s_timed": wall,

@@ -118,6 +118,8 @@ _sig("engram_store_read", [_P, _P, _i32, _P, _P])
 _sig("engram_store_rollback", [_P, _P, _P, _P, _i32, _P, _i32, _P, _P, _P, _P, _P, _P])
 _sig("engram_compress_hash", [_P, _P, _P, _i32, _P, _i32, _P, _P, _P, _P, _P, _P, _P])
 _sig("engram_gather_dequant", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _i32, _P, _i64, _P])
+_sig("engram_lookup_decode", [_P, _P, _P, _i32, _P, _P, _P, _P, _P, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                              _P, _i64, _P])
 _sig("engram_project", [_P, _P, _i64, _P, _i64, _i32, _P, _i32, _P])
 _sig("engram_gather_project", [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _i32, _i32, _P, _i64, _i32, _P, _P])
 _sig("engram_gate_add", [_P, _P, _i32, _i32, _P, _P, _i32, _P])
@@ -466,6 +468,31 @@ def engram_gather_dequant(layout: Layout, tables: Sequence, scales: Optional[Seq
     _check(_lib.engram_gather_dequant(layout.handle, tp, sp, _dev(row_ids, torch.int32, "row_ids"), site,
                                       T, odt, _dev(out, None, "out"), out.shape[1], _stream(stream)),
            "engram_gather_dequant")
+
+
+def engram_lookup_decode(layout: Layout, tid2eid, tokens, eids, row_ids, tables: Sequence,
+                         scales: Sequence, rows, *, slots=None, store=None, dead=None, stream=None):
+    """One decode step's compress + hash + gather (one token per sequence, token t in
+    slot slots[t], -1 or no slots: it starts its sequence) into eids, row_ids, the
+    store and the bf16 rows [T][>= k_pad]."""
+    import torch
+    T = tokens.numel()
+    info = layout.info
+    _need(eids.numel() >= T and row_ids.numel() >= T * info.num_sites * info.cols,
+          "eids / row_ids too small")
+    _need(tid2eid.numel() == layout.desc.vocab_size, "tid2eid must hold vocab_size entries")
+    _need(slots is None or slots.numel() >= T, "slots too small")
+    _need(dead is None or dead.numel() >= T, "dead too small")
+    _need(store is None or isinstance(store, Store), "store must be a Store (engram_store_create)")
+    _need(rows.dim() == 2 and rows.shape[0] >= T and rows.shape[1] >= info.k_pad, "rows too small")
+    _need(rows.dtype == torch.bfloat16, "rows must be bfloat16")
+    tp, sp = _site_pointers(layout, tables, scales)
+    _check(_lib.engram_lookup_decode(
+        layout.handle, _dev(tid2eid, torch.int32, "tid2eid"), _dev(tokens, torch.int32, "tokens"), T,
+        _dev(slots, torch.int32, "slots"), None if store is None else store.handle,
+        _dev(dead, torch.uint8, "dead"), _dev(eids, torch.int32, "eids"),
+        _dev(row_ids, torch.int32, "row_ids"), tp, sp, _dev(rows, None, "rows"), rows.shape[1],
+        _stream(stream)), "engram_lookup_decode")
 
 
 def engram_project(layout: Layout, rows, w, v, *, T: Optional[int] = None, stream=None):

@@ -327,6 +327,71 @@ extern "C" int engram_gather_dequant(const engram_layout* L, const void* const* 
   return ENGRAM_OK;
 }
 
+// ---- 1 + 2 for a decode step: compress, hash and gather in one launch -------------
+
+extern "C" int engram_lookup_decode(const engram_layout* L, const int32_t* d_tid2eid,
+                                    const int32_t* d_tokens, int32_t T, const int32_t* d_slots,
+                                    engram_store* store, const uint8_t* d_dead, int32_t* d_eids,
+                                    int32_t* d_row_ids, const void* const* d_tables,
+                                    const void* const* d_scales, void* d_rows, int64_t rows_ld,
+                                    hipStream_t stream) {
+  if (!L) return ENGRAM_E_ARG;
+  if (L->num_sites != 1 || L->desc.table_dtype != ENGRAM_DTYPE_FP8_E4M3FN || L->scale_block != 0)
+    return ENGRAM_E_UNSUPPORTED;
+  if (T < 0 || !d_tid2eid || !d_tables || !d_scales) return ENGRAM_E_ARG;
+  if (d_slots && !store) return ENGRAM_E_NEED_STORE;
+  if (store) {
+    const int rc = store_usable(store, L);
+    if (rc != ENGRAM_OK) return rc;
+  }
+  if (T == 0) return ENGRAM_OK;
+  if (!d_tokens || !d_eids || !d_row_ids || !d_rows) return ENGRAM_E_ARG;
+  if (rows_ld < L->k_pad || rows_ld % 8 != 0) return ENGRAM_E_ALIGN;
+  if (!aligned(d_rows, 16)) return ENGRAM_E_ALIGN;
+  const uint8_t* table[3];
+  const void* scale[3];
+  int64_t rows[3];
+  const int rc = site_tables(L, d_tables, d_scales, table, scale, rows);
+  if (rc != ENGRAM_OK) return rc;
+  engram::LookupArgs a;
+  a.tid2eid = d_tid2eid;
+  a.tokens = d_tokens;
+  a.slots = d_slots;
+  a.store = store ? store->ids : nullptr;
+  a.dead = d_dead;
+  a.eids = d_eids;
+  a.row_ids = d_row_ids;
+  a.T = T;
+  a.num_slots = store ? store->num_slots : 0;
+  a.heads = L->heads;
+  a.vocab = (int32_t)L->desc.vocab_size;
+  a.pad_token_id = (int32_t)L->desc.pad_token_id;
+  a.vc1 = L->vc_pow[1];
+  a.vc2 = L->vc_pow[2];
+  a.vc3 = L->vc_pow[3];
+  for (int c = 0; c < 3 * L->heads; ++c) {  // site 0's columns come first
+    a.prime[c] = L->prime[c];
+    a.offset[c] = L->offset[c];
+    a.barrett[c] = L->barrett[c];
+  }
+  a.t0 = table[0];
+  a.t1 = table[1];
+  a.t2 = table[2];
+  a.s0 = static_cast<const float*>(scale[0]);
+  a.s1 = static_cast<const float*>(scale[1]);
+  a.s2 = static_cast<const float*>(scale[2]);
+  a.r0 = (int32_t)rows[0];
+  a.r1 = (int32_t)rows[1];
+  a.r2 = (int32_t)rows[2];
+  a.per_site_table = L->per_site_table;
+  a.pitch = L->desc.row_pitch_bytes;
+  a.row_dim = L->desc.row_dim;
+  a.chunks = (uint32_t)(L->seg_pitch / 16);
+  a.out = d_rows;
+  a.out_ld = rows_ld;
+  return hip_status(engram::launch_lookup_decode(a, stream));
+}
+
 // ---- 3. projection + gated residual ---------------------------------------------
 
 extern "C" int engram_project(const engram_layout* L, const void* d_rows, int64_t rows_ld,

@@ -48,6 +48,7 @@ hipError_t read_and_clear_device_error(hipStream_t stream, int* status) {
 
 #include "kernels/hash.hip"
 #include "kernels/gather.hip"
+#include "kernels/lookup.hip"
 #include "kernels/gemm.hip"
 #include "kernels/gemm_packed.hip"
 #include "kernels/gemm_gather.hip"

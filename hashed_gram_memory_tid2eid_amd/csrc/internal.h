@@ -76,6 +76,37 @@ struct HashArgs {
 };
 hipError_t launch_compress_hash(const HashArgs& a, hipStream_t stream);
 
+// One decode step's compress + hash + gather in one launch (every sequence one token
+// continuing from its slot; one site; e4m3fn tables with fp32 row scales; bf16 rows).
+struct LookupArgs {
+  const int32_t* tid2eid;
+  const int32_t* tokens;
+  const int32_t* slots;   // [T] or NULL (= every token starts its sequence)
+  int32_t* store;         // [num_slots][3] or NULL
+  const uint8_t* dead;    // [T] or NULL
+  int32_t* eids;          // [T]
+  int32_t* row_ids;       // [T][3H]
+  int32_t T, num_slots, heads, vocab, pad_token_id;
+  uint64_t vc1, vc2, vc3;
+  uint32_t prime[3 * ENGRAM_MAX_HEADS];  // site 0's columns, [order][head]
+  uint32_t offset[3 * ENGRAM_MAX_HEADS];
+  uint64_t barrett[3 * ENGRAM_MAX_HEADS];
+  const uint8_t* t0;
+  const uint8_t* t1;
+  const uint8_t* t2;
+  const float* s0;
+  const float* s1;
+  const float* s2;
+  int32_t r0, r1, r2;     // rows per table
+  int32_t per_site_table; // every segment reads t0
+  int64_t pitch;          // bytes per table row
+  int32_t row_dim;
+  uint32_t chunks;        // seg_pitch / 16
+  void* out;              // bf16 [T][out_ld]
+  int64_t out_ld;
+};
+hipError_t launch_lookup_decode(const LookupArgs& a, hipStream_t stream);
+
 struct MapCheckArgs {
   const int32_t* tid2eid;
   int32_t vocab, vc, pad_token_id;

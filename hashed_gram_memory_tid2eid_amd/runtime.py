@@ -22,7 +22,7 @@ from typing import Optional, Sequence
 from . import (ENGRAM_DTYPE_BF16, ENGRAM_DTYPE_FP8_E4M3FN, ENGRAM_SCALE_BLOCK32_E8M0,
                ENGRAM_SCALE_ROW_F32, ENGRAM_TABLE_PER_SITE, ENGRAM_TABLES_PER_ORDER, Layout, Wkv,
                engram_compress_hash, engram_gate_add, engram_gated_residual, engram_gather_dequant,
-               engram_gather_project, engram_layout_create, engram_tid2eid_check,
+               engram_gather_project, engram_layout_create, engram_lookup_decode, engram_tid2eid_check,
                engram_wkv_gate_add, engram_wkv_project)
 
 
@@ -223,6 +223,35 @@ class Engram:
         for s in range(self.num_sites):
             self.site_forward(s, per_site[s], T, keep=keep, stream=stream)
         return streams
+
+    @property
+    def decode_lookup_supported(self) -> bool:
+        """Whether decode_step runs its lookup as one launch (engram_lookup_decode):
+        one site, e4m3fn tables with fp32 row scales."""
+        return (self.num_sites == 1 and self.layout.desc.table_dtype == ENGRAM_DTYPE_FP8_E4M3FN
+                and self.layout.info.scale_layout == ENGRAM_SCALE_ROW_F32 and self.path == "split")
+
+    def decode_step(self, tokens, streams, *, slots=None, store=None, dead=None, keep=None,
+                    stream=None):
+        """One decode step: token t is sequence t, continuing from store slot slots[t]
+        (-1, or no slots: it starts its sequence).  The lookup (compress, hash with the
+        store, gather) is one launch, then the projection and gate as in forward.  The
+        result equals forward with cu_seqlens 0..T and seq_start 0 where a slot is given."""
+        T = tokens.numel()
+        if not self.decode_lookup_supported:
+            raise ValueError("decode_step needs one site with e4m3fn tables and fp32 row scales")
+        if T > self.max_tokens:
+            raise ValueError(f"{T} tokens > max_tokens {self.max_tokens}")
+        if dead is not None and keep is None:
+            raise ValueError("a dead mask needs the matching keep mask")
+        if self.pending_T is not None:
+            raise RuntimeError("a gathered call waits for run_ahead; decode_step would overwrite its rows")
+        if streams.shape[0] != T:
+            raise ValueError("streams must hold one row per token")
+        engram_lookup_decode(self.layout, self.tid2eid, tokens, self.eids, self.row_ids,
+                             self.site_tables[0], self.site_scales[0], self.rows, slots=slots,
+                             store=store, dead=dead, stream=stream)
+        return self.project_gate(0, self.rows, streams, T, keep=keep, stream=stream)
 
     # ---- look-ahead order: the next call's lookup between projection and gate -------
     def gather_ahead(self, tokens, cu_seqlens, *, seq_start=None, slots=None, store=None,

@@ -18,6 +18,8 @@
  *                             e4m3fn tables (rows stay on chip).
  *   engram_project_splitk +   the projection split over K for few tokens
  *   engram_gate_add_partials  (decode), summed deterministically in the gate.
+ *   engram_lookup_decode      steps 1 and 2 of a decode step (one token per
+ *                             sequence, continuing from the store) in one launch.
  *   engram_store_*            the rolling store: reset, write, read (snapshot)
  *                             and rollback to accepted lengths.
  *   One layout may describe several Engram sites sharing one hash pass; the
@@ -316,6 +318,30 @@ int engram_gather_dequant(const engram_layout* layout, const void* const* d_tabl
                           const void* const* d_scales, const int32_t* d_row_ids, int32_t site,
                           int32_t T, int32_t out_dtype, void* d_out, int64_t out_ld,
                           hipStream_t stream);
+
+/* ---- 1 + 2 for a decode step ------------------------------------------------- */
+/* A decode step's compress, hash and gather in one launch, for calls in which every
+ * sequence is one token that continues from its store slot ([VeOmni#1370] n-gram
+ * incremental decode cache commit: each step hashes the new token against the three
+ * ids kept per sequence; PR summary: FP8 rows dequantised with their row scale on
+ * lookup).  Token t is sequence t: with a slot (d_slots[t] >= 0) its window's three
+ * earlier ids come from the store, and its new tail goes back into the slot; without
+ * one (d_slots NULL, or d_slots[t] = -1) it starts its sequence (lookback PAD).
+ * Writes exactly what engram_compress_hash (cu_seqlens = 0, 1, ..., T; seq_start 0
+ * where the token has a slot, else 1) followed by engram_gather_dequant (site 0,
+ * bf16 rows) write: d_eids [T], d_row_ids [T][3][H], the store, and d_rows bf16
+ * [T][rows_ld] (rows_ld >= k_pad, a multiple of 8; 16-byte aligned).  Slots must
+ * be distinct within a call.  d_tables / d_scales as for engram_gather_dequant.
+ * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN, ENGRAM_E_NEED_STORE (slots without a
+ * store), ENGRAM_E_UNSUPPORTED (several sites, bf16 tables, BLOCK32 scales).
+ * Device errors: ENGRAM_E_TOKEN_RANGE, ENGRAM_E_SLOT_RANGE (that token starts its
+ * sequence), ENGRAM_E_ROW_RANGE. */
+int engram_lookup_decode(const engram_layout* layout, const int32_t* d_tid2eid,
+                         const int32_t* d_tokens, int32_t T, const int32_t* d_slots,
+                         engram_store* store, const uint8_t* d_dead, int32_t* d_eids,
+                         int32_t* d_row_ids, const void* const* d_tables,
+                         const void* const* d_scales, void* d_rows, int64_t rows_ld,
+                         hipStream_t stream);
 
 /* ---- 3. projection + gated residual ---------------------------------------- */
 /* v[t][o] = sum_{k < k_pad} rows[t][k] * W[o][k], bf16 x bf16 accumulated in

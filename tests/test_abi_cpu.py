@@ -248,6 +248,43 @@ def test_store_and_wkv_handles_host_errors_need_no_device():
     assert lib.engram_gated_residual_noalloc(L.handle, ok, K, None, 4, None, ok, 4, None) == eng.ENGRAM_E_ARG
 
 
+def test_lookup_decode_host_errors_need_no_device():
+    """engram_lookup_decode checks the layout it supports (one site, e4m3fn tables
+    with fp32 row scales), its pointers, the store and the rows' leading dimension on
+    the host, and returns before any launch."""
+    cfg = ei.get_config("tiny")
+    L = _layout(cfg)
+    lib = eng._lib
+    P = ctypes.c_void_p
+    K = L.info.k_pad
+    ok = P(256)
+    three = (P * 3)(ok, ok, ok)
+    f = lib.engram_lookup_decode
+
+    def call(layout, T=4, tid=ok, tok=ok, slots=None, store=None, rows=ok, ld=K, tables=three,
+             scales=three):
+        return f(layout, tid, tok, T, slots, store, None, ok, ok, tables, scales, rows, ld, None)
+    assert call(L.handle, T=0) == 0
+    assert call(L.handle, T=-1) == eng.ENGRAM_E_ARG
+    assert call(L.handle, tid=None) == eng.ENGRAM_E_ARG
+    assert call(L.handle, tok=None) == eng.ENGRAM_E_ARG
+    assert call(L.handle, rows=None) == eng.ENGRAM_E_ARG
+    assert call(L.handle, scales=None) == eng.ENGRAM_E_ARG
+    assert call(L.handle, ld=K - 8) == eng.ENGRAM_E_ALIGN
+    assert call(L.handle, ld=K + 4) == eng.ENGRAM_E_ALIGN
+    assert call(L.handle, rows=P(264)) == eng.ENGRAM_E_ALIGN
+    assert call(L.handle, tables=(P * 3)(P(8), ok, ok)) == eng.ENGRAM_E_ALIGN
+    assert call(L.handle, slots=ok) == eng.ENGRAM_E_NEED_STORE
+    assert call(None) == eng.ENGRAM_E_ARG
+    # layouts it does not take: bf16 tables, (1, 32) block scales, two sites
+    bf = _layout(cfg, table_dtype=eng.ENGRAM_DTYPE_BF16, row_pitch_bytes=2 * cfg.row_pitch_bytes)
+    assert call(bf.handle) == eng.ENGRAM_E_UNSUPPORTED
+    blk = _layout(cfg, scale_layout=eng.ENGRAM_SCALE_BLOCK32_E8M0)
+    assert call(blk.handle) == eng.ENGRAM_E_UNSUPPORTED
+    two = _layout(cfg, num_sites=2, rows=[cfg.rows * 2] * 3)
+    assert call(two.handle) == eng.ENGRAM_E_UNSUPPORTED
+
+
 def test_projection_and_gate_host_errors_need_no_device():
     """The projection, split-K and gate calls check sizes, leading dimensions and
     alignment on the host and return before any launch."""
