@@ -224,8 +224,10 @@ def _cpu_baseline_pinned(cfg, batch, site_tables, weights, streams_host_bits, bu
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for decode workloads, whose ~35 us steps "
+                         "vary by a few us over 20)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 20 for decode)")
     ap.add_argument("--config", default="full", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--path", default="split", choices=["split", "fused"],
                     help="split: gather_dequant + project (default, faster); fused: gather_project")
@@ -270,6 +272,11 @@ def main():
     import torch
 
     import engram_inputs as ei
+    decode_cfg = bool(ei.get_config(args.config).decode_steps)
+    if args.steps is None:
+        args.steps = 200 if decode_cfg else 20
+    if args.warmup is None:
+        args.warmup = 20 if decode_cfg else 5
     import runpy
     # builds only when the library is missing or was built from other sources
     runpy.run_path(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "build_lib.py"))["ensure_built"]()
