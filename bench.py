@@ -256,6 +256,9 @@ def main():
     ap.add_argument("--compare-vendor", action="store_true",
                     help="after the timed steps, time torch.mm (the vendor bf16 GEMM) on the "
                          "projection's rows and weight")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the matrix-core ceiling probe (16x16x32 bf16 products on "
+                         "operands in registers, every CU, no data movement) and print its rate")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
                          "(reference for the HBM byte counters of a profiler run)")
@@ -267,6 +270,27 @@ def main():
               "(tables are replicated per GPU, tokens split across them); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mfma_ceiling:
+        # a child process, started before this one touches the GPU
+        import re
+        import runpy
+        import subprocess
+        probe = runpy.run_path(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd",
+                                            "build_lib.py"))["build_mfma_ceiling"]()
+        out = subprocess.run([probe], capture_output=True, text=True, timeout=120)
+        if out.returncode != 0:
+            print(out.stdout + out.stderr, file=sys.stderr)
+            sys.exit(out.returncode)
+        runs = {}
+        for m in re.finditer(r"mfma chain (\d+): ([\d.]+) ms, ([\d.]+) TFLOP/s", out.stdout):
+            runs.setdefault(int(m.group(1)), []).append(float(m.group(3)))
+        best = {c: max(v) for c, v in runs.items()}
+        print(json.dumps({"metric": "bf16 matrix-core rate with no data movement",
+                          "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+                          "runs": runs, "best": best,
+                          "frac_of_peak": max(best.values()) / BF16_PEAK_TFLOPS}), flush=True)
+        return
 
     import numpy as np
     import torch

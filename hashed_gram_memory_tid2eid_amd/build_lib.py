@@ -103,6 +103,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+MFMA_CEILING_SRC = os.path.join(PKG, "calibrate", "mfma_ceiling.hip")
+MFMA_CEILING_BIN = os.path.join(BUILD, "mfma_ceiling")
+
+
+def build_mfma_ceiling() -> str:
+    """Builds the matrix-core ceiling probe (a measurement program beside the
+    library, run by `bench.py --mfma-ceiling`) and returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    cmd = [HIPCC, *COMMON, MFMA_CEILING_SRC, "-o", MFMA_CEILING_BIN]
+    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if out.returncode != 0:
+        print(out.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for the matrix-core ceiling probe")
+    return MFMA_CEILING_BIN
+
+
 def ensure_built() -> str:
     """Builds the library when it is missing or was built from other sources than
     the tree holds now (compared by the embedded source hash); otherwise leaves
