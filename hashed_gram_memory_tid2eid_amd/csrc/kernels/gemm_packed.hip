@@ -13,11 +13,15 @@
 // fragment reads.  The LDS keeps only the gathered rows (operand A), in a deeper
 // ring than the two-operand kernel can afford.
 //
-// Tile: 256 x 256 per workgroup, 8 waves as 2 (M) x 4 (N), 128 x 64 per wave (8 x 4
-// tiles of 16 x 16, two waves per SIMD).  Calls with a short K take 128 x 256 tiles of
-// 4 waves (1 x 4, the same 128 x 64 per wave) instead, two workgroups per CU: one
-// workgroup's prologue and epilogue then overlap the other's main loop, and each
-// stage barrier holds only one wave per SIMD.
+// Tile: 256 x 256 per workgroup, 8 waves as 1 (M) x 8 (N), 256 x 32 per wave (16 x 2
+// tiles of 16 x 16, two waves per SIMD).  Every wave reads the whole A stage from LDS
+// and fetches only its own 32 columns of B, so no B fragment is fetched twice: with
+// 2 x 4 waves of 128 x 64 the two waves of a column block each fetched it, a third
+// more vector-memory traffic per CU, and the kernel was 3-4% slower although it read
+// half as much from LDS.  Calls with a short K take 128 x 256 tiles of 4 waves (1 x 4,
+// 128 x 64 per wave) instead, two workgroups per CU: one workgroup's prologue and
+// epilogue then overlap the other's main loop, and each stage barrier holds only one
+// wave per SIMD.
 // The 16 x 16 x 32 shape instead of 32 x 32 x 16 (the two-operand kernel's): the
 // same flops per cycle with a quarter of the accumulator per instruction, so the
 // matrix core reads and writes a third fewer register bytes per flop; measured 2-4%
@@ -28,16 +32,16 @@
 // about 2% at k_pad 19,584.
 // A: direct loads into LDS of one 128-byte line per row per 64-k stage, in a ring
 // of A_STAGES stages, XOR-swizzled as in gemm.hip.
-// Inside a stage four sub-steps run: k32 step 0 rows 0-63, step 0 rows 64-127, step 1
-// rows 0-63, step 1 rows 64-127 of the wave tile; the A fragments of the next sub-step
-// are read from LDS while this one multiplies.
+// Inside a stage four sub-steps run: k32 step 0 on the first half of the wave tile's
+// rows, step 0 on the second half, then step 1 on each half; the A fragments of the
+// next sub-step are read from LDS while this one multiplies.
 // B: a ring of the two k32 steps in registers; step s of stage kt+1 is requested right
 // after the last sub-step of stage kt that multiplies step s, two sub-steps ahead.
 //
 // Every iteration issues the same loads (the last stages re-read clamped, in-bounds
-// addresses into slots nothing reads again), so the vector-memory counter waits
-// below are fixed numbers: per iteration, in issue order, B step 0 (4 loads), the
-// stage wait, A (4 loads), B step 1 (4 loads).
+// addresses into slots nothing reads again), so the vector-memory counter wait
+// below is a fixed number: per iteration, in issue order, B step 0, the stage wait,
+// A, B step 1.
 
 namespace engram {
 
@@ -75,9 +79,9 @@ void pack_weight_kernel(const __bf16* __restrict__ W, int64_t ldw, int32_t N, in
   out[c] = v;
 }
 
-template <int A_STAGES, int BM, int WM_WAVES>
+template <int A_STAGES, int BM, int WM_WAVES, int WN_WAVES>
 __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
-  constexpr int BN = 256, WN_WAVES = 4, NWAVES = WM_WAVES * WN_WAVES;
+  constexpr int BN = 256, NWAVES = WM_WAVES * WN_WAVES;
   constexpr int BK = kGemmBK;
   constexpr int WM = BM / WM_WAVES, WN = BN / WN_WAVES, TM = WM / 16, TN = WN / 16;
   constexpr int HM = TM / 2;                   // 16-row blocks per half
@@ -193,13 +197,15 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
   wait_vmcnt<(A_STAGES - 1) * AI>();
   __builtin_amdgcn_s_barrier();
 
-  // Loads issued after A stage kt+1 when iteration kt waits for it: in steady state
-  // (A_STAGES-2) whole iterations plus B step 1 of the iteration that issued it and
-  // B step 0 of this one; in the first A_STAGES-1 iterations the stage came from
-  // the prologue and fewer loads follow it, fewest at kt = 0.
-  constexpr int WAIT_SS = (A_STAGES - 2) * PER_ITER + 2 * BL;
-  constexpr int WAIT_EARLY = (A_STAGES - 2) * AI + BL;
-  static_assert(WAIT_SS <= 63 && WAIT_EARLY <= WAIT_SS, "vmcnt field holds 6 bits");
+  // Loads issued after A stage kt+1 when iteration kt waits for it: fewest at kt = 0,
+  // where the stage came from the prologue and only A stages 2 .. A_STAGES-1 and B
+  // step 0 of stage 1 follow it.  That count serves every iteration: later ones have
+  // more loads after the stage (in steady state (A_STAGES-2) whole iterations plus two
+  // B steps), so the wait also covers A stage kt+2, requested two iterations earlier.
+  // One count keeps the loop a single body; with an exact count per iteration the
+  // compiler peels the first iterations and runs out of registers there.
+  constexpr int WAIT = (A_STAGES - 2) * AI + BL;
+  static_assert(WAIT <= (A_STAGES - 2) * PER_ITER + 2 * BL && WAIT <= 63, "vmcnt field holds 6 bits");
 
   bf16x8 fa0[HM], fa1[HM];
   load_a(0, 0, 0, fa0);
@@ -227,7 +233,7 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
     // landed; the barrier makes that true for every wave and publishes A stage kt+1,
     // then slot kt % A_STAGES is refilled with stage kt + A_STAGES
     wait_lgkmcnt0();
-    if (kt + 1 < A_STAGES) wait_vmcnt<WAIT_EARLY>(); else wait_vmcnt<WAIT_SS>();
+    wait_vmcnt<WAIT>();
     __builtin_amdgcn_s_barrier();
     issue_a(kt + A_STAGES);
     __builtin_amdgcn_sched_barrier(0);
@@ -278,13 +284,13 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
   }
 }
 
-// 256 x 256 tiles, one workgroup of 8 waves per CU (calls with a long K)
+// 256 x 256 tiles, one workgroup of 8 waves (1 x 8) per CU (calls with a long K)
 __global__ __launch_bounds__(512, 1) void gemm_bf16_nt_packed_kernel(GemmPackedKArgs a) {
-  packed_gemm_tile<kPackedAStages, 256, 2>(a);
+  packed_gemm_tile<kPackedAStages, 256, 1, 8>(a);
 }
 // 128 x 256 tiles, two workgroups of 4 waves per CU (short K)
 __global__ __launch_bounds__(256, 2) void gemm_bf16_nt_packed128_kernel(GemmPackedKArgs a) {
-  packed_gemm_tile<kPackedAStages, 128, 1>(a);
+  packed_gemm_tile<kPackedAStages, 128, 1, 4>(a);
 }
 
 hipError_t launch_pack_weight(const PackWeightArgs& g, hipStream_t stream) {
