@@ -46,9 +46,10 @@
 namespace engram {
 
 constexpr int kPackedAStages = 4;  // A ring: 4 stages of 64 k (32 KB each at 256 rows, 16 KB at 128)
-// calls with k_pad up to this take 128 x 256 tiles (against 256 x 256, measured faster at
-// k_pad 3,072 and 6,144, level at 9,792 and slower at 19,584)
-constexpr int kPackedShortK = 8192;
+// calls with k_pad up to this take 128 x 256 tiles (against 256 x 256 at 65,536 tokens:
+// 5-6% faster at k_pad 3,072 and 6,144, 2% at 9,792, level at 13,056, 2% slower at
+// 16,320 and 3-4% at 19,584)
+constexpr int kPackedShortK = 12288;
 // dword 3 of a buffer resource on gfx9-family parts: 32-bit data format, no swizzle
 constexpr int kBufferRsrcFlags = 0x00020000;
 

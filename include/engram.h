@@ -372,7 +372,7 @@ int engram_project(const engram_layout* layout, const void* d_rows, int64_t rows
  *   on `stream`; d_w may be freed once it ran.
  * engram_project_packed: v = rows W^T as engram_project, from the packed weight,
  *   bit-identical to engram_project (the same products summed in the same order).
- *   Meant for many tokens (tiles of 128 x 256 for k_pad up to 8,192, else 256 x 256);
+ *   Meant for many tokens (tiles of 128 x 256 for k_pad up to 12,288, else 256 x 256);
  *   d_rows, rows_ld, d_v, T as for engram_project.
  * Host errors: ENGRAM_E_ARG, ENGRAM_E_ALIGN; ENGRAM_E_UNSUPPORTED when 256 rows of
  * rows_ld elements or k_pad * 64 bytes pass 2^31 - 1 (32-bit per-tile offsets). */

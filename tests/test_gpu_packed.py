@@ -81,11 +81,11 @@ def test_packed_bytes_follow_the_index_formula(eng):
 @pytest.mark.parametrize("M,N,cols,D", [(1, 8, 3, 64), (77, 200, 3, 100), (300, 512, 6, 128),
                                         (1000, 264, 3, 192), (4097, 4096, 3, 512),
                                         (513, 300, 6, 1000), (256, 256, 3, 64),
-                                        (700, 520, 3, 3000), (255, 40, 3, 2731)])
+                                        (700, 520, 6, 2200), (255, 40, 3, 4097)])
 def test_packed_projection_equals_unpacked(eng, M, N, cols, D):
     """Ragged M and N (row and column tile tails, a 264-wide weight whose last
     256-column block holds one 32-column tile) and K from 192 to 6,144 (128 x 256
-    tiles), and 9,024 and 8,256 (256 x 256 tiles, k_pad past 8,192)."""
+    tiles), and 13,248 and 12,352 (256 x 256 tiles, k_pad past 12,288)."""
     L = _layout(eng, cols, D)
     K = L.info.k_pad
     A, B = _operands(L, M, N, seed=M * 1000 + N)
@@ -233,15 +233,15 @@ def test_gated_residual_runs_the_planned_kernel(eng, shape):
 def test_packed_projection_random_shapes(eng):
     """24 seeded random shapes (tokens 1..2,000, hidden a multiple of 8 up to 1,200;
     1 or 2 heads with rows of 1..1,100 elements, and every fourth case 2 heads with rows
-    of 1,400..3,000, so k_pad past 8,192 and both tile heights): bit-identical to
+    of 2,100..3,000, so k_pad past 12,288 and both tile heights): bit-identical to
     engram_project each time."""
     import numpy as np
     rng = np.random.default_rng(20261202)
     for case in range(24):
         M = int(rng.integers(1, 2001))
         N = 8 * int(rng.integers(1, 151))
-        if case % 4 == 0:  # k_pad past 8,192: the 256-row tiles
-            cols, D = 6, int(rng.integers(1400, 3001))
+        if case % 4 == 0:  # k_pad past 12,288: the 256-row tiles
+            cols, D = 6, int(rng.integers(2100, 3001))
         else:
             cols, D = 3 * int(rng.integers(1, 3)), int(rng.integers(1, 1101))
         L = _layout(eng, cols, D)
