@@ -259,6 +259,9 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the matrix-core ceiling probe (16x16x32 bf16 products on "
                          "operands in registers, every CU, no data movement) and print its rate")
+    ap.add_argument("--hbm-reference", action="store_true",
+                    help="only run the HBM streaming references (read, copy, 1:2 expand, and the "
+                         "gated residual's traffic without its arithmetic) and print their rates")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB fp32 copy kernel three times "
                          "(reference for the HBM byte counters of a profiler run)")
@@ -290,6 +293,27 @@ def main():
                           "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
                           "runs": runs, "best": best,
                           "frac_of_peak": max(best.values()) / BF16_PEAK_TFLOPS}), flush=True)
+        return
+
+    if args.hbm_reference:
+        # a child process, started before this one touches the GPU
+        import re
+        import runpy
+        import subprocess
+        probe = runpy.run_path(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd",
+                                            "build_lib.py"))["build_hbm_reference"]()
+        out = subprocess.run([probe], capture_output=True, text=True, timeout=120)
+        if out.returncode != 0:
+            print(out.stdout + out.stderr, file=sys.stderr)
+            sys.exit(out.returncode)
+        runs = {}
+        for m in re.finditer(r"hbm (\w+): ([\d.]+) ms, ([\d.]+) GB/s", out.stdout):
+            runs.setdefault(m.group(1), []).append(float(m.group(3)))
+        best = {k: max(v) for k, v in runs.items()}
+        print(json.dumps({"metric": "HBM rate of plain streaming kernels", "unit": "GB/s",
+                          "peak": HBM_PEAK_GBS, "runs": runs, "best": best,
+                          "frac_of_peak": {k: v / HBM_PEAK_GBS for k, v in best.items()}}),
+              flush=True)
         return
 
     import numpy as np

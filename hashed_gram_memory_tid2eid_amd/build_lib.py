@@ -119,6 +119,22 @@ def build_mfma_ceiling() -> str:
     return MFMA_CEILING_BIN
 
 
+HBM_REFERENCE_SRC = os.path.join(PKG, "calibrate", "hbm_reference.hip")
+HBM_REFERENCE_BIN = os.path.join(BUILD, "hbm_reference")
+
+
+def build_hbm_reference() -> str:
+    """Builds the HBM streaming-reference probe (a measurement program beside the
+    library, run by `bench.py --hbm-reference`) and returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    cmd = [HIPCC, *COMMON, HBM_REFERENCE_SRC, "-o", HBM_REFERENCE_BIN]
+    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if out.returncode != 0:
+        print(out.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for the HBM reference probe")
+    return HBM_REFERENCE_BIN
+
+
 def ensure_built() -> str:
     """Builds the library when it is missing or was built from other sources than
     the tree holds now (compared by the embedded source hash); otherwise leaves
