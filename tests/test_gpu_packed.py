@@ -81,11 +81,12 @@ def test_packed_bytes_follow_the_index_formula(eng):
 @pytest.mark.parametrize("M,N,cols,D", [(1, 8, 3, 64), (77, 200, 3, 100), (300, 512, 6, 128),
                                         (1000, 264, 3, 192), (4097, 4096, 3, 512),
                                         (513, 300, 6, 1000), (256, 256, 3, 64),
-                                        (700, 520, 6, 2200), (255, 40, 3, 4097)])
+                                        (300, 264, 6, 2048), (700, 520, 6, 2200), (255, 40, 3, 4097)])
 def test_packed_projection_equals_unpacked(eng, M, N, cols, D):
     """Ragged M and N (row and column tile tails, a 264-wide weight whose last
     256-column block holds one 32-column tile) and K from 192 to 6,144 (128 x 256
-    tiles), and 13,248 and 12,352 (256 x 256 tiles, k_pad past 12,288)."""
+    tiles; 12,288, the largest k_pad they take), and 13,248 and 12,352 (256 x 256 tiles,
+    k_pad past 12,288)."""
     L = _layout(eng, cols, D)
     K = L.info.k_pad
     A, B = _operands(L, M, N, seed=M * 1000 + N)
