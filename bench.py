@@ -572,7 +572,8 @@ def main():
     if args.path != "fused":
         roofline_gate = {"bound": "hbm", "kernel": "gate_add", "achieved": gate_gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gate_gbs / HBM_PEAK_GBS,
-                         "traffic": None, "bytes_per_launch": per["gate_bytes"] * T,
+                         "traffic": measured_traffic(cfg, "gate_add_{tag}_traffic.txt", "gate.hip"),
+                         "bytes_per_launch": per["gate_bytes"] * T,
                          "avg_launch_ms": kern_ms["gate_add"]}
         # `roofline` is the dominant kernel's: the one with the most time per step (the
         # hash is a few microseconds at every size and never dominates)

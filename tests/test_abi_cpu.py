@@ -469,26 +469,29 @@ def test_bench_traffic_is_keyed_to_the_kernel_source(tmp_path):
     spec.loader.exec_module(bench)
     full = ei.get_config("full")
     proj = ("gemm_bf16_nt_packed_{tag}_counters.txt", "gemm_packed.hip")
+    gate = ("gate_add_{tag}_traffic.txt", "gate.hip")
     assert bench.measured_traffic(full) > bench.algorithmic_per_token(full)["gather_bytes"] * 65536
     assert bench.measured_traffic(full, *proj) > 0
+    assert bench.measured_traffic(full, *gate) > bench.algorithmic_per_token(full)["gate_bytes"] * 65536
     assert bench.measured_traffic(ei.get_config("tiny")) is None  # no counters for it
     # the same files under another root, with one comment added to each kernel source
     shutil.copytree(os.path.join(ROOT, "profiles"), tmp_path / "profiles")
     kdir = tmp_path / "hashed_gram_memory_tid2eid_amd" / "csrc" / "kernels"
     kdir.mkdir(parents=True)
-    for name in ("gather.hip", "gemm_packed.hip"):
+    for name in ("gather.hip", "gemm_packed.hip", "gate.hip"):
         src = open(os.path.join(ROOT, "hashed_gram_memory_tid2eid_amd", "csrc", "kernels", name)).read()
         (kdir / name).write_text(src)
     bench.ROOT = str(tmp_path)
-    assert bench.measured_traffic(full) is not None and bench.measured_traffic(full, *proj) is not None
+    measured = lambda: [bench.measured_traffic(full), bench.measured_traffic(full, *proj),
+                        bench.measured_traffic(full, *gate)]
+    assert None not in measured()
     # a comment edit leaves the kernel as it was measured; a code edit does not
-    for name in ("gather.hip", "gemm_packed.hip"):
+    for name in ("gather.hip", "gemm_packed.hip", "gate.hip"):
         (kdir / name).write_text((kdir / name).read_text() + "// edited\n/* edited */\n")
-    assert bench.measured_traffic(full) is not None and bench.measured_traffic(full, *proj) is not None
-    for name in ("gather.hip", "gemm_packed.hip"):
+    assert None not in measured()
+    for name in ("gather.hip", "gemm_packed.hip", "gate.hip"):
         (kdir / name).write_text((kdir / name).read_text() + "static int edited;\n")
-    assert bench.measured_traffic(full) is None
-    assert bench.measured_traffic(full, *proj) is None
+    assert measured() == [None, None, None]
 
 
 def test_readme_c_example_compiles_against_the_header(tmp_path):
