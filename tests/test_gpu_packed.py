@@ -232,13 +232,13 @@ def test_gated_residual_runs_the_planned_kernel(eng, shape):
 
 
 def test_packed_projection_random_shapes(eng):
-    """24 seeded random shapes (tokens 1..2,000, hidden a multiple of 8 up to 1,200;
+    """48 seeded random shapes (tokens 1..2,000, hidden a multiple of 8 up to 1,200;
     1 or 2 heads with rows of 1..1,100 elements, and every fourth case 2 heads with rows
     of 2,100..3,000, so k_pad past 12,288 and both tile heights): bit-identical to
     engram_project each time."""
     import numpy as np
     rng = np.random.default_rng(20261202)
-    for case in range(24):
+    for case in range(48):
         M = int(rng.integers(1, 2001))
         N = 8 * int(rng.integers(1, 151))
         if case % 4 == 0:  # k_pad past 12,288: the 256-row tiles

@@ -25,7 +25,7 @@ from engram_harness import (DEV, Site, assert_streams_close, assert_v_close, bf1
 
 pytestmark = pytest.mark.gpu
 
-CASES = 16
+CASES = 40
 
 
 @pytest.fixture(scope="module")
