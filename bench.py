@@ -96,6 +96,19 @@ def measured_traffic(cfg, profile="gather_dequant_{tag}_traffic.txt", source="ga
     return float(kv["traffic_bytes_per_launch"])
 
 
+def measured_mfma_ceiling():
+    """The bf16 matrix-core rate this part reached with no data movement
+    (profiles/mfma_ceiling_probe.txt, from `bench.py --mfma-ceiling`), TFLOP/s, or
+    None without that profile."""
+    import re
+    path = os.path.join(ROOT, "profiles", "mfma_ceiling_probe.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        m = re.search(r"^best: ([\d.]+) TFLOP/s", f.read(), re.M)
+    return float(m.group(1)) if m else None
+
+
 def kernel_code_hash(text: str) -> str:
     """First 16 hex digits of a SHA-256 over a kernel source with its comments removed
     and its whitespace collapsed: an edit of the code changes it, an edit of a comment
@@ -560,6 +573,11 @@ def main():
                                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                    "frac": proj_tflops / BF16_PEAK_TFLOPS, "traffic": proj_traffic,
                                    "flops_per_launch": proj_flops, "avg_launch_ms": kern_ms["project"]}
+            ceiling = measured_mfma_ceiling()
+            if ceiling:
+                # the same instruction's rate with its operands in registers on this part
+                roofline_projection["measured_ceiling"] = ceiling
+                roofline_projection["frac_of_measured_ceiling"] = proj_tflops / ceiling
         else:
             proj_gbs = gbs(proj_bytes, kern_ms["project"])
             kernels["project"].update({"bound": "hbm", "GB/s": proj_gbs})

@@ -470,6 +470,7 @@ def test_bench_traffic_is_keyed_to_the_kernel_source(tmp_path):
     full = ei.get_config("full")
     proj = ("gemm_bf16_nt_packed_{tag}_counters.txt", "gemm_packed.hip")
     gate = ("gate_add_{tag}_traffic.txt", "gate.hip")
+    assert 1000.0 < bench.measured_mfma_ceiling() < bench.BF16_PEAK_TFLOPS  # the probe's best rate
     assert bench.measured_traffic(full) > bench.algorithmic_per_token(full)["gather_bytes"] * 65536
     assert bench.measured_traffic(full, *proj) > 0
     assert bench.measured_traffic(full, *gate) > bench.algorithmic_per_token(full)["gate_bytes"] * 65536
