@@ -323,11 +323,13 @@ hipError_t launch_gemm_bf16_nt_packed(const GemmPackedArgs& g, hipStream_t strea
   a.vec_store = (g.ldc % 4 == 0 && ((uintptr_t)g.C & 15) == 0) ? 1 : 0;
   // short K: two 128-row workgroups per CU, in tile groups of 8 row blocks up to k_pad
   // 4,096 and of 4 above (measured at 3,072: 8 is 2-4% faster than 4, 16 is 3-5% slower;
-  // at 6,144: 4 is 1.3% faster than 8); long K: one 256-row workgroup per CU, groups of 2
+  // at 6,144: 4 is 1.3% faster than 8); long K: one 256-row workgroup per CU, groups of 4
+  // (at k_pad 19,584 as fast as groups of 2, 7.645 against 7.648 ms, with a third less
+  // traffic beyond L2: an XCD's 32 concurrent tiles then re-read W per 4 row blocks)
   const bool short_k = g.K <= kPackedShortK;
   const int bm = short_k ? 128 : 256;
   a.tiles_m = (g.M + bm - 1) / bm;
-  a.group_m = !short_k ? 2 : g.K <= 4096 ? 8 : 4;
+  a.group_m = short_k && g.K <= 4096 ? 8 : 4;
   const size_t lds_bytes = (size_t)kPackedAStages * bm * kGemmBK * 2;
   static std::atomic<uint64_t> lds_set256{0}, lds_set128{0};
   const hipError_t e =
