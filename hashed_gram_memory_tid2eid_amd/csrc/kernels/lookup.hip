@@ -31,34 +31,34 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_decode_kernel(LookupArg
   int slot = -1;
   uint32_t w0 = 0, w1 = 0, w2 = 0;
   if (wave == 0 && lane < cols) {
-    const uint32_t pad = (uint32_t)a.tid2eid[a.pad_token_id] & kIdMask;
+    // the per-token inputs first, all at once; then the loads that depend on them, at
+    // once too: addresses are clamped in bounds and the values selected afterwards, so
+    // no load waits on a branch (two dependent rounds instead of three or four)
+    const int32_t tok = a.tokens[t];
     const bool dead = a.dead != nullptr && a.dead[t] != 0;
-    w0 = pad;
-    if (!dead) {
-      const int32_t tok = a.tokens[t];
-      if (tok < 0 || tok >= a.vocab) {
-        if (lane == 0) latch_error(ENGRAM_E_TOKEN_RANGE);
-      } else {
-        w0 = (uint32_t)a.tid2eid[tok] & kIdMask;
-      }
+    const int32_t slot_in = a.slots != nullptr ? a.slots[t] : -1;
+    const bool tok_ok = tok >= 0 && tok < a.vocab;
+    const bool slot_ok = slot_in >= -1 && slot_in < a.num_slots && (slot_in < 0 || a.store != nullptr);
+    const uint32_t pad = (uint32_t)a.tid2eid[a.pad_token_id] & kIdMask;
+    const uint32_t e = (uint32_t)a.tid2eid[tok_ok ? tok : 0] & kIdMask;
+    int32_t s0 = 0, s1 = 0, s2 = 0;
+    if (a.store != nullptr) {  // uniform
+      const int32_t* st = a.store + 3 * (slot_ok && slot_in >= 0 ? slot_in : 0);
+      s0 = st[0];
+      s1 = st[1];
+      s2 = st[2];
     }
-    slot = a.slots != nullptr ? a.slots[t] : -1;
-    if (slot < -1 || slot >= a.num_slots || (slot >= 0 && a.store == nullptr)) {
-      if (lane == 0) latch_error(ENGRAM_E_SLOT_RANGE);
-      slot = -1;
-    }
+    if (!dead && !tok_ok && lane == 0) latch_error(ENGRAM_E_TOKEN_RANGE);
+    if (!slot_ok && lane == 0) latch_error(ENGRAM_E_SLOT_RANGE);
+    slot = slot_ok ? slot_in : -1;
+    w0 = dead || !tok_ok ? pad : e;
     // the window: a dead token's is all PAD; a token without a slot starts its
     // sequence, so its lookback is PAD; otherwise the slot holds the three earlier ids,
     // oldest first
-    w1 = pad;
-    w2 = pad;
-    uint32_t w3 = pad;
-    if (!dead && slot >= 0) {
-      const int32_t* st = a.store + 3 * slot;
-      w1 = (uint32_t)st[2];
-      w2 = (uint32_t)st[1];
-      w3 = (uint32_t)st[0];
-    }
+    const bool back = !dead && slot >= 0;
+    w1 = back ? (uint32_t)s2 : pad;
+    w2 = back ? (uint32_t)s1 : pad;
+    const uint32_t w3 = back ? (uint32_t)s0 : pad;
     const uint64_t k2 = (uint64_t)w0 + (uint64_t)w1 * a.vc1;
     const uint64_t k3 = k2 + (uint64_t)w2 * a.vc2;
     const uint64_t k4 = k3 + (uint64_t)w3 * a.vc3;
