@@ -26,22 +26,32 @@
 // same flops per cycle with a quarter of the accumulator per instruction, so the
 // matrix core reads and writes a third fewer register bytes per flop; measured 2-4%
 // faster at every K here, with C bit-identical to gemm_bf16_nt_kernel's (the matrix
-// core sums each output's products in the same k order under both shapes).  Each wave
-// raises its issue priority over its MFMA runs (s_setprio 1, back to 0 after), so a
-// SIMD keeps issuing the wave whose products are ready while the other issues loads;
-// about 2% at k_pad 19,584.
+// core sums each output's products in the same k order under both shapes).
 // A: direct loads into LDS of one 128-byte line per row per 64-k stage, in a ring
 // of A_STAGES stages, XOR-swizzled as in gemm.hip.
 // Inside a stage four sub-steps run: k32 step 0 on the first half of the wave tile's
-// rows, step 0 on the second half, then step 1 on each half; the A fragments of the
-// next sub-step are read from LDS while this one multiplies.
+// rows, step 0 on the second half, then step 1 on each half.
 // B: a ring of the two k32 steps in registers; step s of stage kt+1 is requested right
-// after the last sub-step of stage kt that multiplies step s, two sub-steps ahead.
+// after the last sub-step of stage kt that multiplies step s.
+//
+// Schedules.  The 128-row kernel runs every wave through the same sequence: the A
+// fragments of the next sub-step are read from LDS while this one multiplies, one
+// barrier per stage, and each wave raises its issue priority over its MFMA runs
+// (s_setprio 1), so a SIMD keeps issuing the wave whose products are ready while the
+// other issues loads (about 2% at k_pad 19,584 before the ping-pong below).
+// The 256-row kernel ping-pongs instead: waves 0-3 (one per SIMD) and waves 4-7 take
+// turns on the matrix cores.  A stage runs in four phases separated by barriers; in each
+// phase one group multiplies two sub-steps while the other reads the A fragments of its
+// next two sub-steps from LDS, and the second group runs the same loop one phase behind
+// the first.  With every wave on the same sequence both waves of a SIMD tended to wait
+// at the same moments; taking turns raised the matrix cores' busy share from 71% to 76%
+// of the cycles at k_pad 19,584 (the clock under load fell from ~1.80 to ~1.75 GHz with
+// it) and the kernel ran 1.3-2.1% faster, with C bit-identical (same products in the same
+// k order for every output).
 //
 // Every iteration issues the same loads (the last stages re-read clamped, in-bounds
-// addresses into slots nothing reads again), so the vector-memory counter wait
-// below is a fixed number: per iteration, in issue order, B step 0, the stage wait,
-// A, B step 1.
+// addresses into slots nothing reads again), so the explicit vector-memory counter
+// wait of each schedule is a fixed number.
 
 namespace engram {
 
@@ -80,7 +90,7 @@ void pack_weight_kernel(const __bf16* __restrict__ W, int64_t ldw, int32_t N, in
   out[c] = v;
 }
 
-template <int A_STAGES, int BM, int WM_WAVES, int WN_WAVES>
+template <int A_STAGES, int BM, int WM_WAVES, int WN_WAVES, bool PINGPONG>
 __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
   constexpr int BN = 256, NWAVES = WM_WAVES * WN_WAVES;
   constexpr int BK = kGemmBK;
@@ -181,76 +191,136 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{};
   auto mma = [&](const bf16x8* fa, const bf16x8* fb, int h) {
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!PINGPONG) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < HM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[h * HM + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[h * HM + i][j], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!PINGPONG) __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- prologue: B of stage 0, then A stages 0 .. A_STAGES-1; wait for A stage 0
-  issue_b(0, 0);
-  issue_b(0, 1);
+  if constexpr (PINGPONG) {
+    // Group 0 = waves 0 .. NWAVES/2-1, group 1 = the rest; one wave of each per SIMD.
+    // Loop body per stage kt, phases ending at a barrier:
+    //   Q0 multiply k32 step 0 (both row halves), then request B(kt+1, 0)
+    //   Q1 read the fragments of step 1; wait for this wave's parts of A(kt+1)
+    //   Q2 multiply step 1, then request B(kt+1, 1)
+    //   Q3 request A(kt+A_STAGES) into the slot of stage kt (every wave read its last
+    //      fragments of stage kt in its Q1, before a barrier both groups have passed),
+    //      then read the fragments of step 0 of stage kt+1
+    // Group 1 runs phase Q of the body while group 0 runs the next one, so by the start
+    // of group 0's Q3(kt) both groups have waited for their parts of A(kt+1).
+    static_assert(NWAVES % 2 == 0, "two groups of waves");
+    const bool group1 = wave >= NWAVES / 2;  // uniform per wave
+    issue_b(0, 0);
+    issue_b(0, 1);
 #pragma unroll
-  for (int s = 0; s < A_STAGES; ++s) issue_a(s);
-  wait_vmcnt<(A_STAGES - 1) * AI>();
-  __builtin_amdgcn_s_barrier();
-
-  // Loads issued after A stage kt+1 when iteration kt waits for it: fewest at kt = 0,
-  // where the stage came from the prologue and only A stages 2 .. A_STAGES-1 and B
-  // step 0 of stage 1 follow it.  That count serves every iteration: later ones have
-  // more loads after the stage (in steady state (A_STAGES-2) whole iterations plus two
-  // B steps), so the wait also covers A stage kt+2, requested two iterations earlier.
-  // One count keeps the loop a single body; with an exact count per iteration the
-  // compiler peels the first iterations and runs out of registers there.
-  constexpr int WAIT = (A_STAGES - 2) * AI + BL;
-  static_assert(WAIT <= (A_STAGES - 2) * PER_ITER + 2 * BL && WAIT <= 63, "vmcnt field holds 6 bits");
-
-  bf16x8 fa0[HM], fa1[HM];
-  load_a(0, 0, 0, fa0);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_lgkmcnt0();
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(kt, 0, 1, fa1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa0, bfr[0], 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_lgkmcnt0();
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(kt, 1, 0, fa0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, bfr[0], 1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(kt + 1, 0);
-    wait_lgkmcnt0();
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(kt, 1, 1, fa1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa0, bfr[1], 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // this wave has read all of A stage kt once the last sub-step's fragments have
-    // landed; the barrier makes that true for every wave and publishes A stage kt+1,
-    // then slot kt % A_STAGES is refilled with stage kt + A_STAGES
-    wait_lgkmcnt0();
-    wait_vmcnt<WAIT>();
+    for (int s = 0; s < A_STAGES; ++s) issue_a(s);
+    wait_vmcnt<(A_STAGES - 1) * AI>();
     __builtin_amdgcn_s_barrier();
-    issue_a(kt + A_STAGES);
+    // Loads a wave has issued after A(kt+1) when it waits in Q1(kt): fewest at kt = 0
+    // (A stages 2 .. A_STAGES-1 of the prologue and B(1, 0)); later stages have issued
+    // more, so the count also waits for later A stages, requested stages earlier.
+    constexpr int WAIT = (A_STAGES - 2) * AI + BL;
+    static_assert(WAIT <= 63, "vmcnt field holds 6 bits");
+    bf16x8 fa0[HM], fa1[HM];
+    load_a(0, 0, 0, fa0);
+    load_a(0, 0, 1, fa1);
+    wait_lgkmcnt0();
+    if (group1) __builtin_amdgcn_s_barrier();  // group 1's first phase: beside group 0's Q0(0)
     __builtin_amdgcn_sched_barrier(0);
-    load_a(kt + 1 < nk ? kt + 1 : kt, 0, 0, fa0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, bfr[1], 1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(kt + 1, 1);
+    for (int kt = 0; kt < nk; ++kt) {
+      mma(fa0, bfr[0], 0);  // Q0
+      mma(fa1, bfr[0], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(kt + 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      load_a(kt, 1, 0, fa0);  // Q1
+      load_a(kt, 1, 1, fa1);
+      wait_lgkmcnt0();
+      wait_vmcnt<WAIT>();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      mma(fa0, bfr[1], 0);  // Q2
+      mma(fa1, bfr[1], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(kt + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      issue_a(kt + A_STAGES);  // Q3
+      const int kn = kt + 1 < nk ? kt + 1 : kt;
+      load_a(kn, 0, 0, fa0);
+      load_a(kn, 0, 1, fa1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+    }
+    if (!group1) __builtin_amdgcn_s_barrier();  // beside group 1's last phase
+  } else {
+  // ---- prologue: B of stage 0, then A stages 0 .. A_STAGES-1; wait for A stage 0
+    issue_b(0, 0);
+    issue_b(0, 1);
+  #pragma unroll
+    for (int s = 0; s < A_STAGES; ++s) issue_a(s);
+    wait_vmcnt<(A_STAGES - 1) * AI>();
+    __builtin_amdgcn_s_barrier();
+  
+    // Loads issued after A stage kt+1 when iteration kt waits for it: fewest at kt = 0,
+    // where the stage came from the prologue and only A stages 2 .. A_STAGES-1 and B
+    // step 0 of stage 1 follow it.  That count serves every iteration: later ones have
+    // more loads after the stage (in steady state (A_STAGES-2) whole iterations plus two
+    // B steps), so the wait also covers A stage kt+2, requested two iterations earlier.
+    // One count keeps the loop a single body; with an exact count per iteration the
+    // compiler peels the first iterations and runs out of registers there.
+    constexpr int WAIT = (A_STAGES - 2) * AI + BL;
+    static_assert(WAIT <= (A_STAGES - 2) * PER_ITER + 2 * BL && WAIT <= 63, "vmcnt field holds 6 bits");
+  
+    bf16x8 fa0[HM], fa1[HM];
+    load_a(0, 0, 0, fa0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_lgkmcnt0();
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(kt, 0, 1, fa1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa0, bfr[0], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(kt, 1, 0, fa0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa1, bfr[0], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(kt + 1, 0);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(kt, 1, 1, fa1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa0, bfr[1], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // this wave has read all of A stage kt once the last sub-step's fragments have
+      // landed; the barrier makes that true for every wave and publishes A stage kt+1,
+      // then slot kt % A_STAGES is refilled with stage kt + A_STAGES
+      wait_lgkmcnt0();
+      wait_vmcnt<WAIT>();
+      __builtin_amdgcn_s_barrier();
+      issue_a(kt + A_STAGES);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(kt + 1 < nk ? kt + 1 : kt, 0, 0, fa0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fa1, bfr[1], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(kt + 1, 1);
+    }
   }
 
   // ---- epilogue (as gemm.hip): stage one 16-row slab per wave in LDS, write whole
-  //      row segments of C with 16-byte stores.  The clamped loads of the last
-  //      iterations may still be landing in the ring: drain them first.
+  //      row segments of C with 16-byte stores.  The clamped loads and fragment reads
+  //      of the last iterations may still be in flight: drain them first.
   constexpr int PITCH = WN + 4;
   static_assert(NWAVES * 16 * PITCH * 4 <= A_STAGES * STAGE, "epilogue staging must fit in the ring");
   wait_vmcnt<0>();
+  wait_lgkmcnt0();
   __builtin_amdgcn_s_barrier();
   float* slab = reinterpret_cast<float*>(smem) + wave * 16 * PITCH;
   const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N) && a.vec_store;
@@ -287,11 +357,11 @@ __device__ __forceinline__ void packed_gemm_tile(const GemmPackedKArgs& a) {
 
 // 256 x 256 tiles, one workgroup of 8 waves (1 x 8) per CU (calls with a long K)
 __global__ __launch_bounds__(512, 1) void gemm_bf16_nt_packed_kernel(GemmPackedKArgs a) {
-  packed_gemm_tile<kPackedAStages, 256, 1, 8>(a);
+  packed_gemm_tile<kPackedAStages, 256, 1, 8, true>(a);
 }
 // 128 x 256 tiles, two workgroups of 4 waves per CU (short K)
 __global__ __launch_bounds__(256, 2) void gemm_bf16_nt_packed128_kernel(GemmPackedKArgs a) {
-  packed_gemm_tile<kPackedAStages, 128, 1, 4>(a);
+  packed_gemm_tile<kPackedAStages, 128, 1, 4, false>(a);
 }
 
 hipError_t launch_pack_weight(const PackWeightArgs& g, hipStream_t stream) {
